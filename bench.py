@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA/HCA hot path on one MI355X, with roofline and a
+CPU-oracle baseline, printed as one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Workloads (synthetic, seeded, N(0,1); see compressed_sparse_attention_04_amd/inputs.py):
+  pair_prefill_128k  (default) one sequence of 131,072 tokens through a CSA
+                     layer (m=4, 4-head dim-64 MXFP4 indexer, top-512) and
+                     an HCA layer (m'=128), 128 query heads, one shared KV
+                     head, head_dim 128, 128-token window, bf16.  A step
+                     runs every stage of the path: gated compression of
+                     both layers' K and V, MXFP4 encoding of the indexer
+                     keys, indexer score + top-k, CSA attention, HCA
+                     attention.
+  csa_prefill_32k    the CSA layer alone at 32,768 tokens.
+  hca_decode_1m      32 sequences x 1,048,576 context tokens, m'=128: the
+                     decode step (last-token query over all 8,191
+                     candidates + window); caches precompressed, untimed.
+  csa_decode_1m      16 sequences x 1,048,576 tokens, m=4: indexer over
+                     262,112 candidates + top-512 + attention.
+
+The timed region is exactly K steps bracketed by synchronisations; stage
+durations come from HIP events recorded on the launch stream.  Decode
+steps rotate over several copies of the caches (> 512 MB in total) so the
+256 MB Infinity Cache cannot hold the working set between steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp4_TFLOPs": 10100.0}
+DEFAULT = "pair_prefill_128k"
+
+
+def n_cand(t, m, W):
+    """Vectorised candidate count (same rule as the library)."""
+    t = np.asarray(t, np.int64)
+    w0 = np.maximum(t - W + 1, 0)
+    return np.minimum((w0 + m - 1) // m, (t + 1) // m)
+
+
+def attend_keys(q_pos, m, W, k):
+    """Keys each query attends to: kept (k>0) or all (k=0) candidates + window."""
+    t = np.asarray(q_pos, np.int64)
+    nc = n_cand(t, m, W)
+    sel = np.minimum(nc, k) if k > 0 else nc
+    nwin = t - np.maximum(t - W + 1, 0) + 1
+    return sel + nwin, nc
+
+
+# --------------------------------------------------------------- workloads
+class Stage:
+    def __init__(self, name, fn, flops=0.0, bytes_=0.0, peak_key=None):
+        self.name, self.fn, self.flops, self.bytes, self.peak_key = name, fn, flops, bytes_, peak_key
+
+
+def setup_prefill(dev, layers):
+    """CSA (and optionally HCA) prefill layers over one sequence."""
+    import torch
+    from compressed_sparse_attention_04_amd import binding as csa
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    stages, tokens, notes = [], None, {}
+    for w in layers:
+        raw = I.draw_raw(w, device=dev)
+        q = I.draw_queries(w, device=dev)
+        o = torch.empty_like(q)
+        T, D, H, m, W = w.T, w.D, w.H, w.m, w.W
+        tokens = w.Tq
+        ck = torch.empty((1, w.Nc, D), dtype=q.dtype, device=dev)
+        cv = torch.empty_like(ck)
+        q_pos = np.arange(w.q_pos0, w.q_pos0 + w.Tq)
+        cbytes = 2.0 * (T * D * 2 + T * D * 2) + 2.0 * w.Nc * D * 2
+        stages.append(Stage(f"compress_m{m}",
+                            lambda raw=raw, m=m, ck=ck, cv=cv: (
+                                csa.hca_compress(raw["k"], raw["gk"], m, out=ck),
+                                csa.hca_compress(raw["v"], raw["gv"], m, out=cv)),
+                            bytes_=cbytes, peak_key="hbm_GBps"))
+        if w.kind == "csa":
+            k_idx = I.draw_indexer_keys(w, device=dev)
+            q_idx = I.draw_indexer_queries(w, device=dev)
+            kc = torch.empty((1, w.Nc, w.dI // 2), dtype=torch.uint8, device=dev)
+            ks = torch.empty((1, w.Nc, w.dI // 32), dtype=torch.uint8, device=dev)
+            topk = torch.empty((1, w.Tq, w.k), dtype=torch.int32, device=dev)
+            iws = torch.empty(max(1, csa.csa_index_topk_workspace(1, w.Tq, w.HI, w.dI, w.Nc, m, W,
+                                                                  w.k, w.q_pos0)),
+                              dtype=torch.uint8, device=dev)
+            nkeys, nc = attend_keys(q_pos, m, W, w.k)
+            stages.append(Stage("quantize_keys",
+                                lambda k_idx=k_idx, kc=kc, ks=ks: csa.csa_quantize_mxfp4(
+                                    k_idx, codes=kc, scales=ks),
+                                bytes_=w.Nc * (w.dI * 2 + w.dI // 2 + w.dI // 32),
+                                peak_key="hbm_GBps"))
+            stages.append(Stage("index_topk",
+                                lambda q_idx=q_idx, kc=kc, ks=ks, topk=topk, iws=iws, w=w:
+                                csa.csa_index_topk(q_idx, kc, ks, m=w.m, W=w.W, k=w.k,
+                                                   q_pos0=w.q_pos0, topk=topk, ws=iws),
+                                flops=2.0 * w.HI * w.dI * float(nc.sum()),
+                                peak_key="fp4_TFLOPs"))
+            stages.append(Stage("csa_attend",
+                                lambda q=q, ck=ck, cv=cv, topk=topk, raw=raw, o=o, w=w:
+                                csa.csa_attend(q, ck, cv, topk, raw["k"], raw["v"], m=w.m, W=w.W,
+                                               q_pos0=w.q_pos0, raw_pos0=0, out=o),
+                                flops=4.0 * H * D * float(nkeys.sum()),
+                                bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
+        else:
+            nkeys, nc = attend_keys(q_pos, m, W, 0)
+            stages.append(Stage("hca_attend",
+                                lambda q=q, ck=ck, cv=cv, raw=raw, o=o, w=w:
+                                csa.hca_attend(q, ck, cv, raw["k"], raw["v"], m=w.m, W=w.W,
+                                               q_pos0=w.q_pos0, raw_pos0=0, out=o),
+                                flops=4.0 * H * D * float(nkeys.sum()),
+                                bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
+    return stages, tokens, notes
+
+
+def _decode_caches(w, dev, with_keys):
+    """Precompress every sequence's 1M-token raw context chunk by chunk on the
+    GPU; keep the last W raw rows.  Untimed."""
+    import torch
+    from compressed_sparse_attention_04_amd import binding as csa
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    L = I.chunk_len(w)
+    per = L // w.m
+    ck = torch.empty((w.B, w.Nc, w.D), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    rk = torch.empty((w.B, w.W, w.D), dtype=torch.bfloat16, device=dev)
+    rv = torch.empty_like(rk)
+    nchunks = w.T // L
+    for b in range(w.B):
+        for c in range(nchunks):
+            x = {n: I.draw_chunk(w, n, b, c, device=dev)[None] for n in ("k", "v", "gk", "gv")}
+            csa.hca_compress(x["k"], x["gk"], w.m, out=ck[b:b + 1, c * per:(c + 1) * per])
+            csa.hca_compress(x["v"], x["gv"], w.m, out=cv[b:b + 1, c * per:(c + 1) * per])
+            if c == nchunks - 1:
+                rk[b].copy_(x["k"][0, -w.W:])
+                rv[b].copy_(x["v"][0, -w.W:])
+    out = {"ck": ck, "cv": cv, "rk": rk, "rv": rv}
+    if with_keys:
+        k_idx = I.draw_indexer_keys(w, device=dev)
+        kc, ks = csa.csa_quantize_mxfp4(k_idx)
+        del k_idx
+        out["kc"], out["ks"] = kc, ks
+    torch.cuda.synchronize()
+    return out
+
+
+def setup_decode(dev, w, min_bytes=600e6):
+    import torch
+    from compressed_sparse_attention_04_amd import binding as csa
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    sparse = w.kind == "csa"
+    base = _decode_caches(w, dev, sparse)
+    q = I.draw_queries(w, device=dev)
+    t = w.q_pos0
+    nkeys, nc = attend_keys([t], w.m, w.W, w.k if sparse else 0)
+    kv_bytes = float(nkeys[0]) * w.D * 2 * 2
+    qo_bytes = w.H * w.D * 2 * 2
+    key_bytes = float(nc[0]) * (w.dI // 2 + w.dI // 32) if sparse else 0.0
+    step_bytes = w.B * (kv_bytes + qo_bytes + key_bytes)
+    # rotate over enough copies that the step's working set is not cached
+    ncopy = max(2, int(np.ceil(min_bytes / step_bytes)) + 1)
+    copies = [base] + [{n: v.clone() for n, v in base.items()} for _ in range(ncopy - 1)]
+    o = torch.empty_like(q)
+    state = {"i": 0}
+    stages = []
+    if sparse:
+        topk = torch.empty((w.B, 1, w.k), dtype=torch.int32, device=dev)
+        q_idx = I.draw_indexer_queries(w, device=dev)
+        iws = torch.empty(max(1, csa.csa_index_topk_workspace(w.B, 1, w.HI, w.dI, w.Nc, w.m, w.W,
+                                                              w.k, t)), dtype=torch.uint8,
+                          device=dev)
+        aws = torch.empty(max(1, csa.csa_attend_workspace(1, w.B, 1, w.H, w.D, w.k, w.W)),
+                          dtype=torch.uint8, device=dev)
+
+        def index():
+            c = copies[state["i"] % ncopy]
+            csa.csa_index_topk(q_idx, c["kc"], c["ks"], m=w.m, W=w.W, k=w.k, q_pos0=t, topk=topk,
+                               ws=iws)
+
+        def attend():
+            c = copies[state["i"] % ncopy]
+            csa.csa_attend(q, c["ck"], c["cv"], topk, c["rk"], c["rv"], m=w.m, W=w.W, q_pos0=t,
+                           raw_pos0=t - w.W + 1, out=o, ws=aws)
+            state["i"] += 1
+
+        stages.append(Stage("index_topk", index, flops=2.0 * w.HI * w.dI * float(nc[0]) * w.B,
+                            bytes_=w.B * key_bytes, peak_key="hbm_GBps"))
+        stages.append(Stage("csa_attend", attend, flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
+                            bytes_=w.B * (kv_bytes + qo_bytes), peak_key="hbm_GBps"))
+    else:
+        aws = torch.empty(max(1, csa.hca_attend_workspace(1, w.B, 1, w.H, w.D, w.Nc, w.m, w.W, t)),
+                          dtype=torch.uint8, device=dev)
+
+        def attend():
+            c = copies[state["i"] % ncopy]
+            csa.hca_attend(q, c["ck"], c["cv"], c["rk"], c["rv"], m=w.m, W=w.W, q_pos0=t,
+                           raw_pos0=t - w.W + 1, out=o, ws=aws)
+            state["i"] += 1
+
+        stages.append(Stage("hca_attend", attend, flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
+                            bytes_=w.B * (kv_bytes + qo_bytes), peak_key="hbm_GBps"))
+    return stages, w.B, {"cache_copies": ncopy, "step_bytes": step_bytes}
+
+
+# --------------------------------------------------------------- CPU baseline
+def cpu_baseline(name, budget_s=20.0):
+    """Time the oracle, unchanged, on a bounded sample of the same workload."""
+    import torch
+
+    import oracle
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    oracle.build()
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    f64 = lambda t: t.to(torch.float64).numpy()
+    rng = np.random.default_rng(0)
+
+    if name in ("pair_prefill_128k", "csa_prefill_32k"):
+        layers = [I.PAIR_CSA_128K, I.PAIR_HCA_128K] if name == "pair_prefill_128k" \
+            else [I.CSA_PREFILL_32K]
+        per_token = 0.0
+        desc = []
+        for w in layers:
+            nrows = 32
+            rows = np.sort(rng.choice(w.Tq, size=nrows, replace=False))
+            q_pos = w.q_pos0 + rows
+            span = min(w.T, 8192)
+            raw = I.draw_raw(w, t0=0, t1=w.T)
+            t0 = time.perf_counter()
+            oracle.compress(f64(raw["k"][:, :span]), f64(raw["gk"][:, :span]), w.m)
+            oracle.compress(f64(raw["v"][:, :span]), f64(raw["gv"][:, :span]), w.m)
+            t_comp = (time.perf_counter() - t0) / span
+            # the sampled rows need the full compressed cache (not timed)
+            ck = oracle.compress(f64(raw["k"]), f64(raw["gk"]), w.m)
+            cv = oracle.compress(f64(raw["v"]), f64(raw["gv"]), w.m)
+            q = f64(I.draw_queries(w, rows=rows))
+            t0 = time.perf_counter()
+            if w.kind == "csa":
+                kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(w)))
+                tk, _ = oracle.index_topk(f64(I.draw_indexer_queries(w, rows=rows)), kc, ks, q_pos,
+                                          w.m, w.W, w.k)
+            else:
+                tk = None
+            oracle.attend(q, ck, cv, tk, f64(raw["k"]), f64(raw["v"]), 0, q_pos, w.m, w.W)
+            t_rows = (time.perf_counter() - t0) / nrows
+            per_token += t_comp + t_rows
+            desc.append(f"{w.name}: compression of {span} tokens + index/attend of {nrows} "
+                        f"random query rows")
+        return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": "; ".join(desc) + " (per-token times summed over the layers)"}
+
+    w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
+    nseq = 1
+    ws = w.replace(B=nseq)
+    t = w.q_pos0
+    ck = f64(I.draw_cache(ws, "ck", w.Nc))
+    cv = f64(I.draw_cache(ws, "cv", w.Nc))
+    rk = f64(I.draw_cache(ws, "rk", w.W))
+    rv = f64(I.draw_cache(ws, "rv", w.W))
+    q = f64(I.draw_queries(ws))
+    t0 = time.perf_counter()
+    if w.kind == "csa":
+        kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(ws)))
+        t0 = time.perf_counter()
+        tk, _ = oracle.index_topk(f64(I.draw_indexer_queries(ws)), kc, ks, [t], w.m, w.W, w.k)
+    else:
+        tk = None
+    oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
+    el = time.perf_counter() - t0
+    return {"value": nseq / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"decode step of {nseq} sequence (caches drawn at the workload's shapes)"}
+
+
+# --------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT,
+                    choices=["pair_prefill_128k", "csa_prefill_32k", "hca_decode_1m",
+                             "csa_decode_1m"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the work would shard); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    decode = args.workload.endswith("decode_1m")
+    steps = args.steps if args.steps is not None else (50 if decode else 10)
+    warmup = args.warmup if args.warmup is not None else (5 if decode else 2)
+
+    if args.workload == "pair_prefill_128k":
+        stages, tokens, notes = setup_prefill(dev, [I.PAIR_CSA_128K, I.PAIR_HCA_128K])
+        wl = {"workload": "csa_hca_layer_pair_prefill", "seq_len": 131072, "batch": 1,
+              "heads": 128, "kv_heads": 1, "head_dim": 128, "m_csa": 4, "m_hca": 128,
+              "top_k": 512, "indexer": "4x64 MXFP4", "window": 128}
+        metric, unit = "prefill tokens/s", "tokens/s"
+    elif args.workload == "csa_prefill_32k":
+        stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K])
+        wl = {"workload": "csa_prefill", "seq_len": 32768, "batch": 1, "heads": 128,
+              "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
+              "window": 128}
+        metric, unit = "prefill tokens/s", "tokens/s"
+    else:
+        w = I.HCA_DECODE_1M if args.workload == "hca_decode_1m" else I.CSA_DECODE_1M
+        stages, tokens, notes = setup_decode(dev, w)
+        wl = {"workload": args.workload.replace("_1m", "") + "_1m_ctx", "context": w.T,
+              "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
+              "top_k": w.k if w.kind == "csa" else None, "window": w.W}
+        metric, unit = "1M-ctx decode tokens/s/GPU", "tokens/s"
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for si, st in enumerate(stages):
+            st.fn()
+            if ev is not None:
+                ev[si].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        starts[s].record(stream)
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = np.zeros(len(stages))
+    for s in range(steps):
+        prev = starts[s]
+        for si in range(len(stages)):
+            stage_ms[si] += prev.elapsed_time(evs[s][si])
+            prev = evs[s][si]
+    stage_ms /= steps
+    ms_per_step = elapsed * 1e3 / steps
+    value = tokens / (ms_per_step / 1e3)
+
+    dom = int(np.argmax(stage_ms))
+    d = stages[dom]
+    sec = stage_ms[dom] / 1e3
+    if d.peak_key == "hbm_GBps":
+        roof = {"bound": "hbm", "achieved": d.bytes / sec / 1e9, "peak": PEAK["hbm_GBps"],
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": d.flops / sec / 1e12, "peak": PEAK[d.peak_key],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = d.name
+    roof["ms_per_launch"] = stage_ms[dom]
+
+    stage_info = {}
+    for st, ms in zip(stages, stage_ms):
+        e = {"ms": round(float(ms), 4)}
+        if st.flops:
+            e["TFLOP/s"] = round(st.flops / (ms / 1e3) / 1e12, 2)
+        if st.bytes:
+            e["GB/s"] = round(st.bytes / (ms / 1e3) / 1e9, 1)
+        stage_info[st.name] = e
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload)
+
+    rec = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+           "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1))", "config": wl, "roofline": roof,
+           "cpu_baseline": cpu, "stages": stage_info}
+    rec.update({k: v for k, v in notes.items()})
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+"""ctypes binding of libcsa.so (include/csa.h): the same entry points, taking
+torch device tensors.  Argument marshalling only -- every step runs in the
+library's HIP kernels; torch provides device memory and the stream.
+
+Importing this module does not load the library; the first call does, and
+raises :class:`CsaError` if ``libcsa.so`` has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+
+CSA_F32, CSA_BF16 = 0, 1
+STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EDEVICE"}
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "csa_abi_version": ([], ctypes.c_int),
+    "csa_last_error": ([], ctypes.c_char_p),
+    "hca_compress": ([ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p], ctypes.c_int),
+    "csa_quantize_mxfp4": ([ctypes.c_int, _i64, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "csa_index_topk_workspace": ([_i64] * 9 + [ctypes.POINTER(_sz)], ctypes.c_int),
+    "csa_index_topk": ([ctypes.c_int] + [_i64] * 9 + [_p] * 5 + [_sz, _p], ctypes.c_int),
+    "csa_attend_workspace": ([ctypes.c_int] + [_i64] * 6 + [ctypes.POINTER(_sz)], ctypes.c_int),
+    "csa_attend": ([ctypes.c_int] + [_i64] * 9 + [ctypes.c_float] + [_p] * 6 + [_i64, _i64]
+                   + [_p, _p, _sz, _p], ctypes.c_int),
+    "hca_attend_workspace": ([ctypes.c_int] + [_i64] * 8 + [ctypes.POINTER(_sz)], ctypes.c_int),
+    "hca_attend": ([ctypes.c_int] + [_i64] * 8 + [ctypes.c_float] + [_p] * 5 + [_i64, _i64]
+                   + [_p, _p, _sz, _p], ctypes.c_int),
+}
+
+
+class CsaError(RuntimeError):
+    """A libcsa call returned a status other than CSA_OK."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libcsa.so (once).  Fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CsaError("load", -1, f"{LIB_PATH} is missing; build it with "
+                           "`python -m compressed_sparse_attention_04_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise CsaError(name, st, lib().csa_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libcsa takes dense row-major tensors")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int | None:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    if t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws, ws.numel() * ws.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, nbytes
+
+
+def hca_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out=None, stream=None):
+    """Softmax-gated pooling: x [B,T,C], gate [B,T,1|C] -> [B, T//m, C]."""
+    B, T, C = x.shape
+    if out is None:
+        out = torch.empty((B, T // m, C), dtype=x.dtype, device=x.device)
+    _call("hca_compress", _dt(x), B, T, C, m, _ptr(x), _ptr(gate), gate.shape[-1], _ptr(out),
+          _stream(x, stream))
+    return out
+
+
+def csa_quantize_mxfp4(x: torch.Tensor, codes=None, scales=None, stream=None):
+    """MXFP4 encoding of rows of x [..., d]: (codes [..., d/2], scales [..., d/32])."""
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+    _call("csa_quantize_mxfp4", _dt(x), rows, d, _ptr(x), _ptr(codes), _ptr(scales),
+          _stream(x, stream))
+    return codes, scales
+
+
+def csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0) -> int:
+    n = _sz(0)
+    _call("csa_index_topk_workspace", B, Tq, HI, dI, Nc, m, W, k, q_pos0, ctypes.byref(n))
+    return n.value
+
+
+def csa_index_topk(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, *,
+                   m: int, W: int, k: int, q_pos0: int, topk=None, ws=None, stream=None):
+    """Indexer scores + top-k: q_idx [B,Tq,HI,dI], keys [B,Nc,dI/2]+[B,Nc,dI/32]
+    -> topk [B,Tq,k] int32 (ascending, -1 padded)."""
+    B, Tq, HI, dI = q_idx.shape
+    Nc = k_codes.shape[1]
+    nbytes = csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0)
+    ws, wsb = _workspace(nbytes, q_idx.device, ws)
+    if topk is None:
+        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+    _call("csa_index_topk", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
+          _ptr(k_codes), _ptr(k_scales), _ptr(topk), _ptr(ws), wsb, _stream(q_idx, stream))
+    return topk
+
+
+def csa_attend_workspace(dtype: int, B, Tq, H, D, k, W) -> int:
+    n = _sz(0)
+    _call("csa_attend_workspace", dtype, B, Tq, H, D, k, W, ctypes.byref(n))
+    return n.value
+
+
+def csa_attend(q, ck, cv, topk, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0: int,
+               scale: float = 1.0, out=None, ws=None, stream=None):
+    """Attention over the kept compressed entries + raw window -> [B,Tq,H,D]."""
+    B, Tq, H, D = q.shape
+    Nc = ck.shape[1]
+    k = topk.shape[2]
+    raw_len = rk.shape[1]
+    nbytes = csa_attend_workspace(_dt(q), B, Tq, H, D, k, W)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    if out is None:
+        out = torch.empty_like(q)
+    _call("csa_attend", _dt(q), B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
+          _ptr(cv), _ptr(topk), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws),
+          wsb, _stream(q, stream))
+    return out
+
+
+def hca_attend_workspace(dtype: int, B, Tq, H, D, Nc, m, W, q_pos0) -> int:
+    n = _sz(0)
+    _call("hca_attend_workspace", dtype, B, Tq, H, D, Nc, m, W, q_pos0, ctypes.byref(n))
+    return n.value
+
+
+def hca_attend(q, ck, cv, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0: int,
+               scale: float = 1.0, out=None, ws=None, stream=None):
+    """Dense attention over every compressed candidate + raw window."""
+    B, Tq, H, D = q.shape
+    Nc = ck.shape[1]
+    raw_len = rk.shape[1]
+    nbytes = hca_attend_workspace(_dt(q), B, Tq, H, D, Nc, m, W, q_pos0)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    if out is None:
+        out = torch.empty_like(q)
+    _call("hca_attend", _dt(q), B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck),
+          _ptr(cv), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws), wsb,
+          _stream(q, stream))
+    return out

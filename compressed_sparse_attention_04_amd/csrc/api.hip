@@ -1,0 +1,242 @@
+// api.hip -- the C ABI of libcsa.so (declared in include/csa.h): host-side
+// argument checks, workspace sizing and kernel launches.  Nothing here
+// allocates, frees or synchronises.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "csa.h"
+#include "common.h"
+#include "internal.h"
+
+namespace csa {
+int64_t index_merge_max();
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa_status fail(csa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+csa_status ok() {
+    g_err[0] = '\0';
+    return CSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+csa_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(CSA_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define CHECK(cond, st, ...) \
+    do { if (!(cond)) return fail(st, __VA_ARGS__); } while (0)
+
+csa_status check_dtype(csa_dtype dt, const char* fn) {
+    CHECK(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, "%s: unknown dtype %d", fn, (int)dt);
+    return CSA_OK;
+}
+
+// The window of every query must lie inside the raw rows, the compressed
+// tensors must hold every candidate, and the key list must be non-empty.
+csa_status check_positions(const char* fn, int64_t Tq, int64_t Nc, int64_t m, int64_t W,
+                           int64_t q_pos0, int64_t raw_pos0, int64_t raw_len) {
+    CHECK(m >= 1, CSA_EINVAL, "%s: m must be >= 1 (got %lld)", fn, (long long)m);
+    CHECK(W >= 1, CSA_EINVAL, "%s: window W must be >= 1 (got %lld)", fn, (long long)W);
+    CHECK(q_pos0 >= 0, CSA_EINVAL, "%s: q_pos0 must be >= 0", fn);
+    CHECK(Nc >= 0 && Nc < ((int64_t)1 << 31), CSA_EINVAL, "%s: Nc out of range", fn);
+    if (Tq == 0) return CSA_OK;
+    const int64_t tlast = q_pos0 + Tq - 1;
+    const int64_t need = csa::n_candidates(tlast, m, W);
+    CHECK(need <= Nc, CSA_EINVAL, "%s: query at %lld has %lld candidates but Nc = %lld", fn,
+          (long long)tlast, (long long)need, (long long)Nc);
+    if (raw_len >= 0) {
+        const int64_t w0 = q_pos0 - W + 1 < 0 ? 0 : q_pos0 - W + 1;
+        CHECK(raw_pos0 >= 0 && w0 >= raw_pos0 && tlast < raw_pos0 + raw_len, CSA_EINVAL,
+              "%s: raw rows [%lld, %lld) do not cover the windows [%lld, %lld]", fn,
+              (long long)raw_pos0, (long long)(raw_pos0 + raw_len), (long long)w0,
+              (long long)tlast);
+    }
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_last_error(void) { return g_err; }
+
+csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m,
+                        const void* x, const void* gate, int64_t gate_channels, void* out,
+                        hipStream_t stream) {
+    const char* fn = "hca_compress";
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    CHECK(B >= 1 && B < 65536 * 1024LL, CSA_EINVAL, "%s: B out of range", fn);
+    CHECK(T >= 0, CSA_EINVAL, "%s: T must be >= 0", fn);
+    CHECK(m >= 1, CSA_EINVAL, "%s: m must be >= 1", fn);
+    CHECK(C >= 8 && C % 8 == 0 && C <= 1024, CSA_EINVAL,
+          "%s: C must be a multiple of 8 in [8, 1024] (got %lld)", fn, (long long)C);
+    CHECK(gate_channels == 1 || gate_channels == C, CSA_EINVAL,
+          "%s: gate_channels must be 1 or C", fn);
+    CHECK(x && gate && out, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(x) && aligned16(out) && (gate_channels == 1 || aligned16(gate)), CSA_EINVAL,
+          "%s: x, out (and a per-channel gate) must be 16-byte aligned", fn);
+    const int64_t blocks = (m <= 16) ? (B * (T / m) * (C / 8) + 255) / 256 : B * (T / m);
+    CHECK(blocks < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "%s: problem too large", fn);
+    return launched(csa::launch_compress((int)dt, x, gate, out, B, T, (int)C, (int)m,
+                                         (int)gate_channels, stream), fn);
+}
+
+csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, const void* x,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    const char* fn = "csa_quantize_mxfp4";
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    CHECK(rows >= 0, CSA_EINVAL, "%s: rows must be >= 0", fn);
+    CHECK(d >= 32 && d % 32 == 0, CSA_EINVAL, "%s: d must be a positive multiple of 32", fn);
+    CHECK(x && codes && scales, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(x) && aligned16(codes), CSA_EINVAL, "%s: x and codes must be 16-byte aligned",
+          fn);
+    CHECK((rows * (d / 32) + 255) / 256 < ((int64_t)1 << 31), CSA_EUNSUPPORTED,
+          "%s: problem too large", fn);
+    return launched(csa::launch_quant_mxfp4((int)dt, x, codes, scales, rows, (int)d, stream), fn);
+}
+
+static csa_status index_args(const char* fn, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                             int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0) {
+    CHECK(B >= 1 && B < 65536, CSA_EINVAL, "%s: B must be in [1, 65535]", fn);
+    CHECK(Tq >= 0, CSA_EINVAL, "%s: Tq must be >= 0", fn);
+    CHECK(HI == 1 || HI == 2 || HI == 4, CSA_EUNSUPPORTED, "%s: HI must be 1, 2 or 4", fn);
+    CHECK(dI == 32 || dI == 64, CSA_EUNSUPPORTED, "%s: dI must be 32 or 64", fn);
+    CHECK(k >= 1 && k <= 2048, CSA_EINVAL, "%s: k must be in [1, 2048]", fn);
+    if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, 0, -1)) return s;
+    csa::IndexPlan p = csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0);
+    CHECK(p.n_qtiles < 65536, CSA_EUNSUPPORTED, "%s: too many query rows", fn);
+    CHECK(p.n_chunks < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "%s: too many candidates", fn);
+    CHECK(p.n_chunks == 1 || p.n_chunks * k <= csa::index_merge_max(), CSA_EUNSUPPORTED,
+          "%s: %lld candidate chunks x k = %lld exceeds the merge limit %lld", fn,
+          (long long)p.n_chunks, (long long)k, (long long)csa::index_merge_max());
+    return CSA_OK;
+}
+
+csa_status csa_index_topk_workspace(int64_t B, int64_t Tq, int64_t HI, int64_t dI, int64_t Nc,
+                                    int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                                    size_t* bytes) {
+    const char* fn = "csa_index_topk_workspace";
+    CHECK(bytes, CSA_EINVAL, "%s: null pointer", fn);
+    if (csa_status s = index_args(fn, B, Tq, HI, dI, Nc, m, W, k, q_pos0)) return s;
+    *bytes = csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0).ws_bytes;
+    return ok();
+}
+
+csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                          int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                          const void* q_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                          int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "csa_index_topk";
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    if (csa_status s = index_args(fn, B, Tq, HI, dI, Nc, m, W, k, q_pos0)) return s;
+    CHECK(q_idx && k_codes && k_scales && topk, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(q_idx) && aligned16(k_codes), CSA_EINVAL,
+          "%s: q_idx and k_codes must be 16-byte aligned", fn);
+    csa::IndexPlan p = csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0);
+    CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
+          "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    return launched(csa::launch_index_topk((int)dt, p, B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k,
+                                           q_pos0, q_idx, k_codes, k_scales, topk, ws, stream),
+                    fn);
+}
+
+static csa_status attend_shape(const char* fn, csa_dtype dt, int64_t B, int64_t Tq, int64_t H,
+                               int64_t D) {
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    CHECK(B >= 1 && B < 65536, CSA_EINVAL, "%s: B must be in [1, 65535]", fn);
+    CHECK(Tq >= 0 && Tq < ((int64_t)1 << 31), CSA_EINVAL, "%s: Tq out of range", fn);
+    CHECK(H >= 1 && D >= 1, CSA_EINVAL, "%s: H and D must be >= 1", fn);
+    if (dt == CSA_BF16) {
+        CHECK(H % 32 == 0 && (H / 32 == 1 || H / 32 == 2 || H / 32 == 4 || H / 32 == 8),
+              CSA_EUNSUPPORTED, "%s: bf16 needs H in {32, 64, 128, 256} (got %lld)", fn,
+              (long long)H);
+        CHECK(D == 64 || D == 128, CSA_EUNSUPPORTED, "%s: bf16 needs D in {64, 128}", fn);
+    } else {
+        CHECK(D <= 256, CSA_EUNSUPPORTED, "%s: fp32 needs D <= 256", fn);
+    }
+    return CSA_OK;
+}
+
+csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                                int64_t k, int64_t W, size_t* bytes) {
+    const char* fn = "csa_attend_workspace";
+    CHECK(bytes, CSA_EINVAL, "%s: null pointer", fn);
+    if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
+    CHECK(k >= 1 && k <= 2048 && W >= 1, CSA_EINVAL, "%s: need 1 <= k <= 2048 and W >= 1", fn);
+    *bytes = csa::plan_attend((int)dt, B, Tq, H, D, k + W).ws_bytes;
+    return ok();
+}
+
+csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                      int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                      const void* q, const void* ck, const void* cv, const int32_t* topk,
+                      const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
+                      void* o, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "csa_attend";
+    if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
+    CHECK(k >= 1 && k <= 2048, CSA_EINVAL, "%s: k must be in [1, 2048]", fn);
+    CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
+    if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
+    CHECK(q && ck && cv && topk && rk && rv && o, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
+              aligned16(o), CSA_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+    csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, k + W);
+    CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
+          "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck,
+                                       cv, topk, rk, rv, raw_pos0, raw_len, o, ws, stream),
+                    fn);
+}
+
+static int64_t hca_max_keys(int64_t Tq, int64_t m, int64_t W, int64_t q_pos0) {
+    return (Tq > 0 ? csa::n_candidates(q_pos0 + Tq - 1, m, W) : 0) + W;
+}
+
+csa_status hca_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                                int64_t Nc, int64_t m, int64_t W, int64_t q_pos0,
+                                size_t* bytes) {
+    const char* fn = "hca_attend_workspace";
+    CHECK(bytes, CSA_EINVAL, "%s: null pointer", fn);
+    if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
+    if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, 0, -1)) return s;
+    *bytes = csa::plan_attend((int)dt, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0)).ws_bytes;
+    return ok();
+}
+
+csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                      int64_t m, int64_t W, int64_t q_pos0, float scale, const void* q,
+                      const void* ck, const void* cv, const void* rk, const void* rv,
+                      int64_t raw_pos0, int64_t raw_len, void* o, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    const char* fn = "hca_attend";
+    if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
+    CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
+    if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
+    CHECK(q && ck && cv && rk && rv && o, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
+              aligned16(o), CSA_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+    csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0));
+    CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
+          "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, 0, q_pos0, scale, q, ck,
+                                       cv, nullptr, rk, rv, raw_pos0, raw_len, o, ws, stream),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+/*
+ * csa.h -- C ABI of libcsa.so: compressed sparse attention (CSA) and heavily
+ * compressed attention (HCA) for one layer on one MI355X (gfx950) GPU.
+ *
+ * The method (DeepSeek-V4 hybrid attention) as the pages describe it:
+ *   - jiwasawa.github.io "deepseek-v4" post, section on the hybrid attention
+ *     mechanism that breaks the context wall: CSA compresses the KV of m
+ *     adjacent tokens into one entry, a Lightning Indexer scores the
+ *     compressed entries per query token, a top-k selector keeps k of them,
+ *     and shared-KV multi-query attention runs over the kept entries; HCA
+ *     compresses with m' >> m and attends densely; a sliding-window branch
+ *     over the newest tokens runs alongside.
+ *   - hazakura.dev "DeepSeek V4とOpenCode", section "衝撃1：CSA + HCA":
+ *     m = 4, m' = 128, FP4 indexer, 128-token window.
+ *   - studioglobal.ai "DeepSeek V4 Flash" answer, section on the CSA/HCA
+ *     breakthrough: pooling is softmax-gated, k = 512 blocks per query,
+ *     the window branch is always present; section on FP4/FP8 mixed
+ *     precision: MXFP4 holds two values per byte.
+ *   - ai-papers.net "deepseek-v4-1m-context-window..." section on how the
+ *     hybrid attention works: the indexer runs at FP4 over the already
+ *     shortened sequence.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is device memory owned by the caller; the
+ *     library never allocates, frees, synchronises, or keeps a pointer after
+ *     the call returns.  Work is enqueued on `stream` (0 = null stream).
+ *   - All tensors are dense, row-major, with the innermost index last.
+ *   - Floating tensors are fp32 or bf16 as given by `dt` (one dtype per call);
+ *     arithmetic is fp32 inside the kernels.
+ *   - Positions: a sequence's tokens are at positions 0,1,2,...  Query row i
+ *     of every sequence is at position q_pos0 + i.  Raw row r of the raw
+ *     K/V tensors is at position raw_pos0 + r.  Compressed entry j covers
+ *     tokens m*j .. m*j+m-1.
+ *   - Window and candidates of a query at position t: the window is the raw
+ *     tokens w0..t with w0 = max(0, t-W+1); compressed entry j is a candidate
+ *     iff it is complete and visible (m*j+m-1 <= t) and starts before the
+ *     window (m*j < w0), so n_cand(t) = min(ceil(w0/m), floor((t+1)/m)).
+ *     A token is never reached both raw and through an entry lying wholly
+ *     inside the window.
+ *   - Errors: arguments are checked on the host before anything is
+ *     enqueued.  A failed check returns CSA_EINVAL (bad value, null or
+ *     misaligned pointer, too small workspace) or CSA_EUNSUPPORTED (a valid
+ *     shape this build has no kernel for), writes nothing, and sets a
+ *     thread-local message read by csa_last_error().  A launch error
+ *     returns CSA_EDEVICE.  Base pointers must be 16-byte aligned.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+typedef enum csa_status {
+    CSA_OK = 0,
+    CSA_EINVAL = 1,
+    CSA_EUNSUPPORTED = 2,
+    CSA_EDEVICE = 3
+} csa_status;
+
+/* Version of this ABI (CSA_ABI_VERSION of the build). */
+int csa_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *csa_last_error(void);
+
+/*
+ * hca_compress -- softmax-gated pooling of m adjacent rows into one entry
+ * (jiwasawa.github.io post, CSA token-level compression: m adjacent tokens'
+ * KV become one entry, the sequence shrinks to 1/m; studioglobal.ai answer,
+ * CSA bullet: the pooling is softmax-gated).  Serves both CSA (m = 4) and
+ * HCA (m' = 128).
+ *
+ *   out[b][j][c] = sum_{i<m} softmax_i( z[b][m*j+i][g(c)] ) * x[b][m*j+i][c]
+ *
+ * for j < T/m (a trailing partial block is not emitted), with the softmax
+ * over the block's m logits and g(c) = c if gate_channels == C, 0 if
+ * gate_channels == 1 (one logit per token).
+ *   x     [B, T, C]            dt
+ *   gate  [B, T, gate_channels] dt
+ *   out   [B, T/m, C]          dt (rounded to nearest even for bf16)
+ * Requires B >= 1, T >= 0, C % 8 == 0 and C <= 1024, m >= 1.
+ */
+csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m,
+                        const void *x, const void *gate, int64_t gate_channels,
+                        void *out, hipStream_t stream);
+
+/*
+ * csa_quantize_mxfp4 -- MXFP4 encoding of rows (studioglobal.ai answer,
+ * FP4/FP8 mixed precision: MXFP4, two values per byte; the indexer runs at
+ * FP4 per every page).  Per run of 32 values: scale exponent
+ * e = floor(log2 max|x|) - 2 clamped to [-127, 127] (-127 for an all-zero
+ * run), stored as the byte e + 127; each value x * 2^-e is rounded to the
+ * nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even code, larger
+ * magnitudes saturate to 6), code = magnitude index | 8 if x's sign bit is
+ * set.  Element 2i of a row is the low nibble of byte i.
+ *   x       [rows, d]      dt, finite values
+ *   codes   [rows, d/2]    uint8
+ *   scales  [rows, d/32]   uint8 (E8M0)
+ * Requires d % 32 == 0.
+ */
+csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, const void *x,
+                              uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/*
+ * csa_index_topk -- Lightning Indexer score and top-k selection per query
+ * token (jiwasawa.github.io post, CSA indexer bullet: every query token
+ * scores the compressed entries with a lightweight indexer and a top-k
+ * selector keeps k entries; studioglobal.ai answer: k = 512 at FP4).
+ *
+ * q_idx is encoded to MXFP4 inside the call (same rule as
+ * csa_quantize_mxfp4), then for every candidate j of the query at t
+ *   I(t, j) = sum_{h < HI} max(0, qhat[t][h] . khat[j])
+ * is formed in fp32 (exact for inputs whose partial sums need at most 24
+ * significant bits, e.g. N(0,1) data).  The kept entries are the first
+ * min(k, n_cand(t)) candidates under the order (score descending, index
+ * ascending); -0 counts as +0.
+ *   q_idx      [B, Tq, HI, dI]   dt
+ *   k_codes    [B, Nc, dI/2]     uint8 (csa_quantize_mxfp4 of the indexer keys)
+ *   k_scales   [B, Nc, dI/32]    uint8
+ *   topk       [B, Tq, k]        int32 out: kept indices in ascending order,
+ *                                then -1 in the remaining slots
+ *   ws         workspace of at least csa_index_topk_workspace(...) bytes
+ * Requires HI in {1, 2, 4}, dI in {32, 64}, 1 <= k <= 2048, W >= 0,
+ * q_pos0 >= 0 and n_cand(q_pos0 + Tq - 1) <= Nc.
+ */
+csa_status csa_index_topk_workspace(int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                                    int64_t Nc, int64_t m, int64_t W, int64_t k,
+                                    int64_t q_pos0, size_t *bytes);
+csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                          int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                          const void *q_idx, const uint8_t *k_codes,
+                          const uint8_t *k_scales, int32_t *topk, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_attend -- shared-KV multi-query attention over the kept compressed
+ * entries joined with the raw sliding window (jiwasawa.github.io post, CSA
+ * "Shared Key-Value MQA" bullet and the SWA branch; hazakura.dev note, CSA
+ * bullets: 128-token window).  For every sequence b, query row i at
+ * t = q_pos0 + i and head h, one softmax runs over the key set
+ *   S = { entries named in the first min(k, n_cand(t)) slots of topk[b][i]
+ *         that are candidates of t }  U  { raw tokens w0..t },
+ *   o[b][i][h] = sum_{s in S} softmax_s( scale * q[b][i][h] . key_s ) val_s
+ * with key/val = ck/cv rows for entries and rk/rv rows for raw tokens.
+ * Slots holding -1 or a non-candidate index contribute nothing.
+ *   q      [B, Tq, H, D]   dt         o   [B, Tq, H, D]  dt
+ *   ck, cv [B, Nc, D]      dt         topk [B, Tq, k]    int32
+ *   rk, rv [B, raw_len, D] dt, must cover positions w0..t of every query
+ *   ws     workspace of at least csa_attend_workspace(...) bytes
+ * bf16 requires H % 32 == 0 (H <= 256) and D in {64, 128}; fp32 requires
+ * D <= 256.
+ */
+csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                                int64_t k, int64_t W, size_t *bytes);
+csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                      int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                      float scale, const void *q, const void *ck, const void *cv,
+                      const int32_t *topk, const void *rk, const void *rv,
+                      int64_t raw_pos0, int64_t raw_len, void *o, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hca_attend -- dense attention over every compressed candidate joined with
+ * the raw window (jiwasawa.github.io post, HCA part: no sparse selection,
+ * dense attention over the heavily compressed sequence; hazakura.dev note,
+ * HCA bullets: m' = 128).  Same as csa_attend with S = { all candidates of
+ * t } U { raw tokens w0..t }.  Argument meaning, layouts and requirements
+ * as for csa_attend.
+ */
+csa_status hca_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                                int64_t Nc, int64_t m, int64_t W, int64_t q_pos0,
+                                size_t *bytes);
+csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                      int64_t Nc, int64_t m, int64_t W, int64_t q_pos0, float scale,
+                      const void *q, const void *ck, const void *cv, const void *rk,
+                      const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

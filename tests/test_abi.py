@@ -1,0 +1,113 @@
+"""C-ABI contract of libcsa.so on a host without a GPU: the library loads,
+exports every entry point include/csa.h declares, sizes workspaces, and
+rejects invalid arguments with CSA_EINVAL / CSA_EUNSUPPORTED and a message
+before anything reaches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_04_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+EINVAL, EUNSUP = 1, 2
+P = ctypes.c_void_p(0x1000)          # aligned non-null placeholder; never dereferenced
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:csa_status|int|const char \*)\s*(\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from compressed_sparse_attention_04_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert {"hca_compress", "csa_index_topk", "csa_attend", "hca_attend",
+            "csa_quantize_mxfp4"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding._SIGS), "binding and header disagree"
+
+
+def test_version(L):
+    assert L.csa_abi_version() == 1
+
+
+def err(L):
+    return L.csa_last_error().decode()
+
+
+def test_compress_rejects(L):
+    assert L.hca_compress(7, 1, 8, 8, 4, P, P, 1, P, None) == EINVAL
+    assert "dtype" in err(L)
+    assert L.hca_compress(1, 1, 8, 12, 4, P, P, 1, P, None) == EINVAL     # C % 8
+    assert L.hca_compress(1, 1, 8, 8, 0, P, P, 1, P, None) == EINVAL      # m
+    assert L.hca_compress(1, 1, 8, 8, 4, P, P, 3, P, None) == EINVAL      # gate channels
+    assert L.hca_compress(1, 1, 8, 8, 4, None, P, 1, P, None) == EINVAL   # null
+    assert "null" in err(L)
+    assert L.hca_compress(1, 1, 8, 8, 4, ctypes.c_void_p(0x1002), P, 1, P, None) == EINVAL
+    assert "aligned" in err(L)
+
+
+def test_quantize_rejects(L):
+    assert L.csa_quantize_mxfp4(1, 4, 48, P, P, P, None) == EINVAL
+    assert L.csa_quantize_mxfp4(1, 4, 64, P, None, P, None) == EINVAL
+
+
+def ws_index(L, *a):
+    n = ctypes.c_size_t(0)
+    st = L.csa_index_topk_workspace(*a, ctypes.byref(n))
+    return st, n.value
+
+
+def test_index_workspace_and_rejects(L):
+    # decode: 16 x 262144 compressed entries -> 64 chunks of 4096, union merge
+    st, n = ws_index(L, 16, 1, 4, 64, 262144, 4, 128, 512, (1 << 20) - 1)
+    assert st == 0 and n == 16 * 1 * 64 * 512 * 8
+    # one chunk needs no workspace
+    st, n = ws_index(L, 1, 16, 2, 32, 256, 4, 128, 16, 1008)
+    assert st == 0 and n == 0
+    assert ws_index(L, 1, 16, 3, 32, 256, 4, 128, 16, 1008)[0] == EUNSUP      # HI
+    assert ws_index(L, 1, 16, 2, 48, 256, 4, 128, 16, 1008)[0] == EUNSUP      # dI
+    assert ws_index(L, 1, 16, 2, 32, 256, 4, 128, 4096, 1008)[0] == EINVAL    # k
+    assert ws_index(L, 1, 16, 2, 32, 200, 4, 128, 16, 1008)[0] == EINVAL      # Nc short
+    assert "candidates" in err(L)
+    # a workspace that is too small is refused before launch
+    st = L.csa_index_topk(1, 16, 1, 4, 64, 262144, 4, 128, 512, (1 << 20) - 1,
+                          P, P, P, P, P, 1024, None)
+    assert st == EINVAL and "workspace" in err(L)
+
+
+def test_attend_workspace_and_rejects(L):
+    n = ctypes.c_size_t(0)
+    assert L.csa_attend_workspace(1, 1, 32768, 128, 128, 512, 128, ctypes.byref(n)) == 0
+    assert n.value == 0                                   # enough rows: no split
+    assert L.hca_attend_workspace(1, 32, 1, 128, 128, 8192, 128, 128, (1 << 20) - 1,
+                                  ctypes.byref(n)) == 0
+    assert n.value > 0                                    # decode splits the key list
+    assert L.csa_attend_workspace(1, 1, 1, 96, 128, 512, 128, ctypes.byref(n)) == EUNSUP
+    assert L.csa_attend_workspace(1, 1, 1, 128, 96, 512, 128, ctypes.byref(n)) == EUNSUP
+    # raw rows must cover the window of every query
+    st = L.csa_attend(1, 1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, P, P, P,
+                      1073, 127, P, None, 0, None)
+    assert st == EINVAL and "raw rows" in err(L)
+    st = L.hca_attend(1, 1, 1, 128, 128, 300, 4, 0, 1199, 1.0, P, P, P, P, P, 1072, 128, P,
+                      None, 0, None)
+    assert st == EINVAL and "window" in err(L)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(binding.CsaError):
+        binding.lib()
