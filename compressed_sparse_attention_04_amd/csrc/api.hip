@@ -122,7 +122,8 @@ static csa_status index_args(const char* fn, int64_t B, int64_t Tq, int64_t HI, 
     csa::IndexPlan p = csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0);
     CHECK(p.n_qtiles < 65536, CSA_EUNSUPPORTED, "%s: too many query rows", fn);
     CHECK(p.n_chunks < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "%s: too many candidates", fn);
-    CHECK(p.n_chunks == 1 || p.n_chunks * k <= csa::index_merge_max(), CSA_EUNSUPPORTED,
+    CHECK(p.path != csa::IDX_CHUNK || p.n_chunks == 1 || p.n_chunks * k <= csa::index_merge_max(),
+          CSA_EUNSUPPORTED,
           "%s: %lld candidate chunks x k = %lld exceeds the merge limit %lld", fn,
           (long long)p.n_chunks, (long long)k, (long long)csa::index_merge_max());
     return CSA_OK;

@@ -11,7 +11,8 @@
 // fetched once per query token for all heads.
 //
 // bf16 kernel, per block: one query token (all H = 32 * NW heads, one wave
-// per 32 heads) and one split of its key list.  Per tile of 32 keys:
+// per 32 heads) and one split of its key list, in tiles of 64 keys whose
+// gathers for tile n+1 are in flight while tile n is computed.  Per tile:
 //   S^T = K * Q^T      (V_MFMA_F32_32X32X16_BF16, K rows from LDS, Q^T held
 //                       in registers) -> every lane owns one head's column
 //   online softmax in fp32 (exp2 domain), rows = keys, so the running max
@@ -26,7 +27,8 @@
 
 namespace csa {
 
-constexpr int KT = 32;           // keys per tile
+constexpr int ATT_KT = 32;       // keys per tile of the bf16 kernel
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 struct KeyList {
     int64_t t, w0, nsel, nwin, len;
@@ -55,21 +57,195 @@ __device__ __forceinline__ int64_t list_row(const KeyList& L, int64_t s, const i
     return -((L.w0 + (s - L.nsel) - raw_pos0) + 2);
 }
 
-template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64)
+#define CSA_LDS __attribute__((address_space(3)))
+
+// Key rows of one tile are copied straight from global memory into LDS
+// (global_load_lds, 16 bytes per lane, lane-contiguous).  A row of D bf16 is
+// CH = D/8 chunks of 16 bytes; chunk c of tile row r sits in slot
+// c ^ (r % CH) so that the 32 rows read by one MFMA operand load hit
+// different LDS banks.
+template <int D>
+struct TileGeom {
+    static constexpr int KT = 32;                   // keys per tile
+    static constexpr int NST = 4;                   // LDS stages (3 tiles in flight)
+    static constexpr int CH = D / 8;                // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;              // bytes per row
+    static constexpr int RPI = 64 / CH;             // rows per wave-wide copy
+    static constexpr int NINS = KT / RPI;           // wave-wide copies per tile and tensor
+    static constexpr int BYTES = KT * ROWB;         // bytes per tile and tensor
+};
+
+template <int D>
+__device__ __forceinline__ int slot_of(int r, int c) { return c ^ (r & (TileGeom<D>::CH - 1)); }
+
+// Row of key-list entry s (compressed row in ck/cv, or raw row in rk/rv) and
+// whether it contributes.  Entries that contribute nothing point at the
+// window's first raw row, which always exists.
+__device__ __forceinline__ bool key_row(const KeyList& L, int64_t s, int64_t s_end, bool sparse,
+                                        const CSA_LDS int32_t* ssel, int64_t nc_t,
+                                        int64_t raw_pos0, bool* comp, int64_t* row) {
+    *comp = false;
+    *row = L.w0 - raw_pos0;
+    if (s >= s_end) return false;
+    if (s < L.nsel) {
+        const int64_t j = sparse ? (int64_t)ssel[s] : s;
+        if (j < 0 || j >= nc_t) return false;
+        *comp = true;
+        *row = j;
+        return true;
+    }
+    *row = L.w0 + (s - L.nsel) - raw_pos0;
+    return true;
+}
+
+// Issue this wave's copies of the K and V rows of the tile starting at key
+// s0; returns the wave's bits of the tile's contribution mask.
+template <int NW, int D>
+__device__ __forceinline__ uint32_t issue_tile(int64_t s0, int64_t s_end, const KeyList& L,
+                                               bool sparse, const CSA_LDS int32_t* ssel,
+                                               int64_t nc_t,
+                                               int64_t raw_pos0, const uint16_t* ckb,
+                                               const uint16_t* cvb, const uint16_t* rkb,
+                                               const uint16_t* rvb, CSA_LDS uint8_t* sk,
+                                               CSA_LDS uint8_t* sv) {
+    using G = TileGeom<D>;
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int ins = wave; ins < G::NINS; ins += NW) {
+        const int r = ins * G::RPI + lane / G::CH;
+        const int c = slot_of<D>(r, lane % G::CH);   // slot <-> chunk is an involution
+        bool comp;
+        int64_t row;
+        const bool ok = key_row(L, s0 + r, s_end, sparse, ssel, nc_t, raw_pos0, &comp, &row);
+        const uint16_t* kp = (comp ? ckb : rkb) + row * D + c * 8;
+        const uint16_t* vp = (comp ? cvb : rvb) + row * D + c * 8;
+        __builtin_amdgcn_global_load_lds(kp, (CSA_LDS void*)(sk + ins * G::RPI * G::ROWB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp, (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB), 16, 0, 0);
+        const uint64_t bal = __ballot(ok && (lane % G::CH) == 0);
+#pragma unroll
+        for (int x = 0; x < G::RPI; ++x)
+            mask |= (uint32_t)((bal >> (x * G::CH)) & 1ull) << (ins * G::RPI + x);
+    }
+    return mask;
+}
+
+// Running softmax state of one lane (one head, half of each key tile).
+template <int D>
+struct Online {
+    f32x16 acc[D / 32];
+    float m_run, l_run;
+};
+
+// One 32-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  K and V
+// are the tile's LDS copies; vmask marks the keys that contribute.
+template <int D>
+__device__ __forceinline__ void tile_compute(Online<D>& S, const bf16x8 (&qop)[D / 16],
+                                             const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
+                                             uint32_t vmask, float scale_log2) {
+    using G = TileGeom<D>;
+    const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
+    // S^T: rows = keys (8*(r/4) + 4*kb + r%4), column = head
+    f32x16 sacc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const CSA_LDS bf16x8*>(
+            K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], sacc, 0, 0, 0);
+    }
+    if (vmask != ~0u) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = 8 * (r / 4) + 4 * kb + (r % 4);
+            if (!((vmask >> key) & 1u)) sacc[r] = -INFINITY;
+        }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(S.m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((S.m_run - m_use) * scale_log2);
+    const float mb = -m_use * scale_log2;
+    S.m_run = m_new;
+    float psum = 0.f;
+    uint32_t pb[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, mb));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, mb));
+        psum += p0 + p1;
+        pb[r / 2] = pack_bf16x2(p0, p1);
+    }
+    S.l_run = S.l_run * alpha + psum;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S.acc[dt][r] *= alpha;
+    }
+    // O^T += V^T P^T.  k-step u covers keys 16u..16u+15; k-slot s of lane
+    // half kb is key 16u + 8*(s/4) + 4*kb + s%4 (the S^T register order).
+    // Each half of the V^T operand is one transposing LDS read: lane
+    // (16g + 4j + a) points at V[key 16u + 8h + 4kb + j][32dt + 16(g%2) + 4a].
+    const int g = lane >> 4, wj = (lane >> 2) & 3, wa = lane & 3;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        bf16x8 pop;
+        {
+            u32x4 w = {pb[4 * u], pb[4 * u + 1], pb[4 * u + 2], pb[4 * u + 3]};
+            pop = *reinterpret_cast<bf16x8*>(&w);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int d = 32 * dt + 16 * (g & 1) + 4 * wa;
+            const int key0 = 16 * u + 4 * (g >> 1) + wj;
+            const int key1 = key0 + 8;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
+                V + key0 * G::ROWB + slot_of<D>(key0, d / 8) * 16 + (d % 8) * 2));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
+                V + key1 * G::ROWB + slot_of<D>(key1, d / 8) * 16 + (d % 8) * 2));
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop, S.acc[dt], 0, 0, 0);
+        }
+    }
+}
+
+// vmcnt wait (other counters untouched) leaving n copies in flight
+#define CSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x3f70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// Block barrier without a memory fence: LDS writes are drained explicitly
+// and the copies each wave waited for are complete, so no outstanding copy
+// into another stage is waited for here.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int NW, int D>
+__global__ void __launch_bounds__(NW * 64, 2)
 k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
               const uint16_t* __restrict__ cv, const int32_t* __restrict__ topk,
               const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
               uint16_t* __restrict__ o, float* __restrict__ part, int64_t Tq, int64_t Nc,
               int64_t m, int64_t W, int k, int64_t q_pos0, float scale_log2, int64_t raw_pos0,
               int64_t raw_len, int splits) {
+    using G = TileGeom<D>;
     constexpr int NT = NW * 64;
     constexpr int H = NW * 32;
-    constexpr int KPAD = D + 8;            // K row stride (bf16)
-    constexpr int VPAD = KT + 8;           // V^T row stride (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t sK[KT * KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VPAD];
-    __shared__ int sValid[KT];
+    constexpr int KT = G::KT;
+    constexpr int PER = 2 * ((G::NINS + NW - 1) / NW);   // copies per wave per tile
+    // the stages live in distinct arrays, so the compiler can tell which
+    // stage an LDS read touches and never waits on another stage's copies
+    __shared__ __attribute__((aligned(16))) uint8_t sK0[G::BYTES], sV0[G::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sK1[G::BYTES], sV1[G::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sK2[G::BYTES], sV2[G::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sK3[G::BYTES], sV3[G::BYTES];
+    __shared__ uint32_t sM0[NW], sM1[NW], sM2[NW], sM3[NW];   // contribution masks
+    __shared__ int32_t sSel[2048];                  // this query's kept indices (CSA)
 
     const int64_t i = blockIdx.x;
     const int split = blockIdx.y;
@@ -80,13 +256,24 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     const bool sparse = topk != nullptr;
     const KeyList L = key_list(t, m, W, k, sparse);
     const int64_t nc_t = n_candidates(t, m, W);
-    const int32_t* sel = sparse ? topk + (b * Tq + i) * k : nullptr;
 
     // this split's range of the key list, in whole tiles
     const int64_t ntile = (L.len + KT - 1) / KT;
     const int64_t tps = (ntile + splits - 1) / splits;
     const int64_t s_begin = split * tps * KT;
     const int64_t s_end = min(L.len, s_begin + tps * KT);
+
+    const uint16_t* ckb = ck + b * Nc * D;
+    const uint16_t* cvb = cv + b * Nc * D;
+    const uint16_t* rkb = rk + b * raw_len * D;
+    const uint16_t* rvb = rv + b * raw_len * D;
+
+    if (sparse) {
+        const int32_t* sel = topk + (b * Tq + i) * k;
+        for (int x = tid; x < L.nsel; x += NT) sSel[x] = sel[x];
+        __syncthreads();
+    }
+    const CSA_LDS int32_t* ssel = (const CSA_LDS int32_t*)sSel;
 
     // Q^T operand: head hq, d = 16*kk + 8*kb + 0..7
     const int hq = wave * 32 + col;
@@ -97,165 +284,121 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         for (int kk = 0; kk < D / 16; ++kk)
             qop[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
     }
-    f32x16 acc[D / 32];
+    Online<D> S;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int r = 0; r < 16; ++r) S.acc[dt][r] = 0.f;
+    S.m_run = -INFINITY;
+    S.l_run = 0.f;
 
-    const uint16_t* ckb = ck + b * Nc * D;
-    const uint16_t* cvb = cv + b * Nc * D;
-    const uint16_t* rkb = rk + b * raw_len * D;
-    const uint16_t* rvb = rv + b * raw_len * D;
+    auto issue = [&](int64_t s0, uint8_t* sk, uint8_t* sv, uint32_t* sm) {
+        if (s0 < s_end) {
+            const uint32_t mk = issue_tile<NW, D>(s0, s_end, L, sparse, ssel, nc_t, raw_pos0, ckb, cvb,
+                                                  rkb, rvb, (CSA_LDS uint8_t*)sk,
+                                                  (CSA_LDS uint8_t*)sv);
+            if (lane == 0) sm[wave] = mk;
+        }
+    };
+    // one tile: wait for its copies, barrier (the stage written next is then
+    // free on every wave), issue the copies three tiles ahead, compute
+    auto step = [&](int64_t s0, uint8_t* ck_, uint8_t* cv_, uint32_t* cm_, uint8_t* nk_,
+                    uint8_t* nv_, uint32_t* nm_) {
+        const int64_t after = min((int64_t)(G::NST - 2), (s_end - s0 - 1) / KT);
+        if (after >= 2) CSA_WAIT_VM(2 * PER);
+        else if (after == 1) CSA_WAIT_VM(PER);
+        else CSA_WAIT_VM(0);
+        lds_barrier();
+        issue(s0 + (G::NST - 1) * KT, nk_, nv_, nm_);
+        uint32_t vm = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) vm |= cm_[w];
+        tile_compute<D>(S, qop, (const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_, vm,
+                        scale_log2);
+    };
 
-    for (int64_t s0 = s_begin; s0 < s_end; s0 += KT) {
-        __syncthreads();
-        // cooperative load: KT keys x D/8 16-byte pieces of K and of V
-        constexpr int PIECES = KT * (D / 8);
-#pragma unroll
-        for (int c = tid; c < PIECES; c += NT) {
-            const int kk = c / (D / 8), p = c % (D / 8);
-            const int64_t s = s0 + kk;
-            int64_t row = s < s_end ? list_row(L, s, sel, nc_t, raw_pos0) : -1;
-            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (row >= 0) {
-                kv = *reinterpret_cast<const u32x4*>(ckb + row * D + p * 8);
-                vv = *reinterpret_cast<const u32x4*>(cvb + row * D + p * 8);
-            } else if (row <= -2) {
-                const int64_t r = -row - 2;
-                kv = *reinterpret_cast<const u32x4*>(rkb + r * D + p * 8);
-                vv = *reinterpret_cast<const u32x4*>(rvb + r * D + p * 8);
-            }
-            *reinterpret_cast<u32x4*>(sK + kk * KPAD + p * 8) = kv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sVt[(p * 8 + 2 * e) * VPAD + kk] = (uint16_t)(vv[e] & 0xffffu);
-                sVt[(p * 8 + 2 * e + 1) * VPAD + kk] = (uint16_t)(vv[e] >> 16);
-            }
-            if (p == 0) sValid[kk] = row != -1;
-        }
-        __syncthreads();
-
-        // S^T = K Q^T : rows = keys (8*(r/4) + 4*kb + r%4), column = head
-        f32x16 st = {};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + col * KPAD + 16 * kk + 8 * kb);
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], st, 0, 0, 0);
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r / 4) + 4 * kb + (r % 4);
-            float v = sValid[key] ? st[r] * scale_log2 : -INFINITY;
-            st[r] = v;
-            tmax = fmaxf(tmax, v);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float psum = 0.f;
-        uint32_t pb[8];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            float p0 = __builtin_amdgcn_exp2f(st[r] - m_use);
-            float p1 = __builtin_amdgcn_exp2f(st[r + 1] - m_use);
-            psum += p0 + p1;
-            pb[r / 2] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-
-        // O^T += V^T P^T, two k-steps of 16 keys; k-slot s of lane half kb
-        // in step u is key 16u + 8*(s/4) + 4*kb + s%4 (the S^T register order)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            bf16x8 pop;
-            {
-                u32x4 w = {pb[4 * u], pb[4 * u + 1], pb[4 * u + 2], pb[4 * u + 3]};
-                pop = *reinterpret_cast<bf16x8*>(&w);
-            }
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const uint16_t* vr = sVt + (32 * dt + col) * VPAD + 16 * u + 4 * kb;
-                u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-                u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-                u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                bf16x8 a = *reinterpret_cast<bf16x8*>(&w);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop, acc[dt], 0, 0, 0);
-            }
-        }
+    issue(s_begin, sK0, sV0, sM0);
+    issue(s_begin + KT, sK1, sV1, sM1);
+    issue(s_begin + 2 * KT, sK2, sV2, sM2);
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += 4 * KT) {
+        step(s0, sK0, sV0, sM0, sK3, sV3, sM3);
+        if (s0 + KT >= s_end) break;
+        step(s0 + KT, sK1, sV1, sM1, sK0, sV0, sM0);
+        if (s0 + 2 * KT >= s_end) break;
+        step(s0 + 2 * KT, sK2, sV2, sM2, sK1, sV1, sM1);
+        if (s0 + 3 * KT >= s_end) break;
+        step(s0 + 3 * KT, sK3, sV3, sM3, sK2, sV2, sM2);
     }
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = S.l_run + __shfl_xor(S.l_run, 32, 64);
     if (splits == 1) {
         const float inv = 1.f / l_tot;
         uint16_t* op = o + ((b * Tq + i) * H + hq) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * dt + 8 * g + 4 * kb;
+            for (int gg = 0; gg < 4; ++gg) {
+                const int d = 32 * dt + 8 * gg + 4 * kb;
                 u32x2 w;
-                w[0] = f32_to_bf16_bits(acc[dt][4 * g] * inv) |
-                       (f32_to_bf16_bits(acc[dt][4 * g + 1] * inv) << 16);
-                w[1] = f32_to_bf16_bits(acc[dt][4 * g + 2] * inv) |
-                       (f32_to_bf16_bits(acc[dt][4 * g + 3] * inv) << 16);
+                w[0] = pack_bf16x2(S.acc[dt][4 * gg] * inv, S.acc[dt][4 * gg + 1] * inv);
+                w[1] = pack_bf16x2(S.acc[dt][4 * gg + 2] * inv, S.acc[dt][4 * gg + 3] * inv);
                 *reinterpret_cast<u32x2*>(op + d) = w;
             }
     } else {
-        // partial record per (query, split, head): D accumulators, max, sum
+        // partial record per (query, split, head): D accumulators, max, sum;
+        // the max is stored in the exp2 domain of the combine kernel
         float* pr = part + (((b * Tq + i) * splits + split) * H + hq) * (D + 2);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * dt + 8 * g + 4 * kb;
-                f32x4 w = {acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2],
-                           acc[dt][4 * g + 3]};
+            for (int gg = 0; gg < 4; ++gg) {
+                const int d = 32 * dt + 8 * gg + 4 * kb;
+                f32x4 w = {S.acc[dt][4 * gg], S.acc[dt][4 * gg + 1], S.acc[dt][4 * gg + 2],
+                           S.acc[dt][4 * gg + 3]};
                 *reinterpret_cast<f32x4*>(pr + d) = w;
             }
         if (kb == 0) {
-            pr[D] = m_run;
+            pr[D] = S.m_run == -INFINITY ? -INFINITY : S.m_run * scale_log2;
             pr[D + 1] = l_tot;
         }
     }
 }
 
-// Log-sum-exp merge of the split partials; one thread per (head, 8 dims).
+// Log-sum-exp merge of the split partials.  Grid (query, sequence, head
+// group of 8); one thread per (head, 4 dims).
 template <typename TO>
 __global__ void __launch_bounds__(256)
 k_attend_combine(const float* __restrict__ part, TO* __restrict__ o, int64_t Tq, int H, int D,
                  int splits) {
     const int64_t i = blockIdx.x, b = blockIdx.y;
-    const int groups = D / 8;
-    for (int w = threadIdx.x; w < H * groups; w += blockDim.x) {
-        const int h = w / groups, d0 = (w % groups) * 8;
-        const float* base = part + ((b * Tq + i) * splits * H + h) * (int64_t)(D + 2);
-        const int64_t sstride = (int64_t)H * (D + 2);
-        float M = -INFINITY;
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * sstride + D]);
-        float Lsum = 0.f, a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (M != -INFINITY) {
-            for (int s = 0; s < splits; ++s) {
-                const float* pr = base + s * sstride;
-                float ms = pr[D];
-                if (ms == -INFINITY) continue;
-                float wgt = __builtin_amdgcn_exp2f(ms - M);
-                Lsum += pr[D + 1] * wgt;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] += pr[d0 + e] * wgt;
-            }
-        }
-        const float inv = 1.f / Lsum;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] *= inv;
-        Elem<TO>::store8(o + ((b * Tq + i) * H + h) * (int64_t)D + d0, a);
+    const int per_head = D / 4;
+    const int h = blockIdx.z * 8 + threadIdx.x / per_head;
+    const int d0 = (threadIdx.x % per_head) * 4;
+    if (threadIdx.x >= 8 * per_head || h >= H) return;
+    const int64_t sstride = (int64_t)H * (D + 2);
+    const float* base = part + ((b * Tq + i) * splits * H + h) * (int64_t)(D + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * sstride + D]);
+    float Lsum = 0.f;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) {
+        const float* pr = base + s * sstride;
+        const float ms = pr[D];
+        if (ms == -INFINITY) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ms - M);
+        Lsum += pr[D + 1] * wgt;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(pr + d0);
+        a[0] += v[0] * wgt; a[1] += v[1] * wgt; a[2] += v[2] * wgt; a[3] += v[3] * wgt;
+    }
+    const float inv = 1.f / Lsum;
+    TO* op = o + ((b * Tq + i) * H + h) * (int64_t)D + d0;
+    if constexpr (sizeof(TO) == 2) {
+        u32x2 w;
+        w[0] = f32_to_bf16_bits(a[0] * inv) | (f32_to_bf16_bits(a[1] * inv) << 16);
+        w[1] = f32_to_bf16_bits(a[2] * inv) | (f32_to_bf16_bits(a[3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(op) = w;
+    } else {
+        f32x4 w = {a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv};
+        *reinterpret_cast<f32x4*>(op) = w;
     }
 }
 
@@ -325,9 +468,9 @@ AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int6
     p.splits = 1;
     if (dt == 1) {
         const int64_t rows = B * Tq;
-        const int64_t tiles = (max_keys + KT - 1) / KT;
-        if (rows < 1024 && tiles > 2) {
-            int64_t want = (1024 + rows - 1) / rows;          // ~4 blocks per CU
+        const int64_t tiles = (max_keys + ATT_KT - 1) / ATT_KT;
+        if (rows < 512 && tiles > 2) {
+            int64_t want = (512 + rows - 1) / rows;            // ~2 blocks per CU
             int64_t cap = (tiles + 1) / 2;                     // >= 2 tiles per split
             p.splits = (int)min(min(want, cap), (int64_t)64);
             if (p.splits < 1) p.splits = 1;
@@ -344,15 +487,17 @@ static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, 
                         const void* rv, int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
                         hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((k_attend_bf16<D, NW>), dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B),
-                       dim3(NW * 64), 0, st, (const uint16_t*)q, (const uint16_t*)ck,
-                       (const uint16_t*)cv, topk, (const uint16_t*)rk, (const uint16_t*)rv,
-                       (uint16_t*)o, (float*)ws, Tq, Nc, m, W, k, q_pos0, scale_log2, raw_pos0,
-                       raw_len, p.splits);
-    if (p.splits > 1)
-        hipLaunchKernelGGL(k_attend_combine<uint16_t>, dim3((unsigned)Tq, (unsigned)B),
-                           dim3(256), 0, st, (const float*)ws, (uint16_t*)o, Tq, NW * 32, D,
-                           p.splits);
+    hipLaunchKernelGGL((k_attend_bf16<NW, D>),
+                       dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
+                       (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq, Nc,
+                       m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
+    if (p.splits > 1) {
+        const int H = NW * 32;
+        hipLaunchKernelGGL(k_attend_combine<uint16_t>,
+                           dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
+                           st, (const float*)ws, (uint16_t*)o, Tq, H, D, p.splits);
+    }
 }
 
 hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int64_t H,

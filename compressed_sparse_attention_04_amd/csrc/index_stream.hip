@@ -1,0 +1,302 @@
+// index_stream.hip -- Lightning Indexer with streaming exact top-k, for
+// query tiles whose candidates fit one block (jiwasawa.github.io post, CSA
+// indexer bullet: per query token, score every compressed entry and keep the
+// top k; studioglobal.ai answer: FP4 indexer, k = 512).
+//
+//   I(t, j) = sum_{h < HI} max(0, qhat[t][h] . khat[j])
+//
+// One block owns 8 query rows and streams all their candidates in tiles of
+// 32 keys.  Each pass recomputes the FP4 scores on the scaled MFMA (cheaper
+// than keeping 8 x 32K fp32 scores anywhere) and, per query, either adds
+// the keys of the current range to a 1024-bin histogram (narrowing the
+// threshold range) or collects: keys above the range go to a candidate
+// bitmap, keys inside it to a small buffer (or, for a single-valued range,
+// to an equality bitmap).  Typical data needs two passes.  Each wave then
+// finishes two queries: exact threshold over the buffer, first-by-index
+// resolution of ties, and read-out of the bitmap in ascending order.
+#include "internal.h"
+#include "mxfp4.h"
+#include "wave_select.h"
+
+namespace csa {
+
+constexpr int ST_NT = 256;
+constexpr int ST_QT = 8;               // query rows per block
+constexpr int ST_CAP = 256;            // collected keys per query
+constexpr int ST_MAXW = 1024;          // bitmap words per query -> 32768 candidates
+
+enum : int { M_DONE = 0, M_HIST1 = 1, M_HIST = 2, M_COLLECT = 3 };
+
+struct StreamSmem {
+    uint32_t hist[ST_QT][SEL_NB];
+    u32x2 cb[ST_QT][ST_CAP];
+    uint32_t sel[ST_QT][ST_MAXW];
+    uint32_t eq[ST_QT][ST_MAXW];
+    uint32_t lo[ST_QT], hi[ST_QT];
+    int shift[ST_QT], mode[ST_QT], above[ST_QT], need[ST_QT], cnt[ST_QT], eqmode[ST_QT];
+    int any_active;
+};
+
+template <typename T, int HI>
+__global__ void __launch_bounds__(ST_NT)
+k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+               const uint8_t* __restrict__ ks, int32_t* __restrict__ topk, int64_t Tq, int dI,
+               int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    StreamSmem& S = *reinterpret_cast<StreamSmem*>(smem_raw);
+    constexpr int NU = 16 / HI;                     // query slots per lane in an MFMA tile
+
+    const int64_t q0 = (int64_t)blockIdx.x * ST_QT;
+    const int64_t b = blockIdx.y;
+    const int qv = (int)min((int64_t)ST_QT, Tq - q0);
+    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int row = lane & 31, kb = lane >> 5;
+    const int nc_max = (int)n_candidates(q_pos0 + q0 + qv - 1, m, W);
+    const int nw = (nc_max + 31) / 32;
+
+    // ---- per-query setup
+    if (tid < ST_QT) {
+        int nc = tid < qv ? (int)n_candidates(q_pos0 + q0 + tid, m, W) : 0;
+        int need = min(nc, k);
+        S.need[tid] = need;
+        S.above[tid] = 0;
+        S.cnt[tid] = 0;
+        S.eqmode[tid] = 0;
+        S.lo[tid] = 0u;
+        S.hi[tid] = KEY_END;
+        S.shift[tid] = 0;
+        // all candidates kept when there are at most k of them
+        S.mode[tid] = (need == 0 || nc <= k) ? M_DONE : M_HIST1;
+    }
+    for (int i = tid; i < ST_QT * ST_MAXW; i += ST_NT) {
+        const int q = i / ST_MAXW, w = i % ST_MAXW;
+        if (w < nw) {
+            int nc = q < qv ? (int)n_candidates(q_pos0 + q0 + q, m, W) : 0;
+            // queries with nc <= k keep every candidate
+            uint32_t full = 0u;
+            if (nc <= k) {
+                int lo_b = w * 32;
+                full = lo_b + 32 <= nc ? 0xFFFFFFFFu
+                                       : (lo_b >= nc ? 0u : ((1u << (nc - lo_b)) - 1u));
+            }
+            S.sel[q][w] = full;
+            S.eq[q][w] = 0u;
+        }
+    }
+
+    // ---- A operand: MXFP4 of query rows (row / HI, row % HI)
+    i32x8 aop = {0, 0, 0, 0, 0, 0, 0, 0};
+    int sa = 127;
+    {
+        const int qi = row / HI, h = row % HI;
+        if (qi < qv && kb * 32 < dI) {
+            const T* src = q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + kb * 32);
+            float v[32];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float t8[8];
+                Elem<T>::load8(src + p * 8, t8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[p * 8 + i] = t8[i];
+            }
+            uint32_t pk[4], sb;
+            mxfp4_encode32(v, pk, sb);
+            aop[0] = (int)pk[0]; aop[1] = (int)pk[1]; aop[2] = (int)pk[2]; aop[3] = (int)pk[3];
+            sa = (int)sb;
+        }
+    }
+    // the queries this lane's MFMA output rows belong to
+    const int kbq = kb * 4 / HI;
+    int qslot[NU];
+    int ncq[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int g = (u * HI) / 4, i = (u * HI) % 4;
+        const int qi = (8 * g + i) / HI + kbq;
+        qslot[u] = qi;
+        ncq[u] = (qi < qv) ? (int)n_candidates(q_pos0 + q0 + qi, m, W) : 0;
+    }
+    __syncthreads();
+
+    const int kbytes = dI / 2, kscales = dI / 32;
+    const int ntiles = (nc_max + 31) / 32;
+    const uint8_t* kcb = kc + b * Nc * kbytes;
+    const uint8_t* ksb = ks + b * Nc * kscales;
+
+#pragma unroll 1
+    for (int pass = 0; pass < 8; ++pass) {
+        // per-slot state of this pass (registers)
+        int md[NU], sh[NU];
+        uint32_t lo[NU], hi[NU];
+        bool eqm[NU];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int q = qslot[u] < ST_QT ? qslot[u] : 0;
+            md[u] = qslot[u] < qv ? S.mode[q] : M_DONE;
+            sh[u] = S.shift[q];
+            lo[u] = S.lo[q];
+            hi[u] = S.hi[q];
+            eqm[u] = S.eqmode[q] != 0;
+        }
+        if (tid == 0) {
+            int a = 0;
+            for (int q = 0; q < ST_QT; ++q) a |= S.mode[q] != M_DONE;
+            S.any_active = a;
+        }
+        for (int i = tid; i < ST_QT * SEL_NB; i += ST_NT) (&S.hist[0][0])[i] = 0u;
+        __syncthreads();
+        if (!S.any_active) break;
+        (void)any;
+
+        for (int tile = wave; tile < ntiles; tile += ST_NT / WAVE) {
+            const int j = tile * 32 + row;
+            i32x8 bop = {0, 0, 0, 0, 0, 0, 0, 0};
+            int sbk = 127;
+            if (j < nc_max && kb < kscales) {
+                u32x4 w = *reinterpret_cast<const u32x4*>(kcb + (int64_t)j * kbytes + kb * 16);
+                bop[0] = (int)w[0]; bop[1] = (int)w[1]; bop[2] = (int)w[2]; bop[3] = (int)w[3];
+                sbk = ksb[(int64_t)j * kscales + kb];
+            }
+            f32x16 acc = {};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc, 4, 4, 0, sa, 0,
+                                                                   sbk);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (md[u] == M_DONE || j >= ncq[u]) continue;
+                float s = 0.f;
+#pragma unroll
+                for (int hh = 0; hh < HI; ++hh) s += fmaxf(acc[u * HI + hh], 0.f);
+                const uint32_t key = s == 0.f ? 0u : __float_as_uint(s);
+                const int q = qslot[u];
+                if (md[u] == M_HIST1) {
+                    atomicAdd(&S.hist[q][lvl1_bin(key)], 1u);
+                } else if (md[u] == M_HIST) {
+                    if (key >= lo[u] && key < hi[u])
+                        atomicAdd(&S.hist[q][(key - lo[u]) >> sh[u]], 1u);
+                } else {                                  // collect
+                    if (key >= hi[u]) {
+                        atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
+                    } else if (key >= lo[u]) {
+                        if (eqm[u]) {
+                            atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
+                        } else {
+                            int pos = atomicAdd(&S.cnt[q], 1);
+                            if (pos < ST_CAP) {
+                                u32x2 e = {key, (uint32_t)j};
+                                S.cb[q][pos] = e;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- per-query decisions: wave w handles queries w and w + 4
+        for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
+            const int mode = S.mode[q];
+            if (mode == M_HIST1 || mode == M_HIST) {
+                const int rem = S.need[q] - S.above[q];
+                int gt, in;
+                const int d = wave_hist_find(&S.hist[q][0], rem, &gt, &in);
+                uint32_t nlo, nhi;
+                if (mode == M_HIST1) {
+                    lvl1_range(d, &nlo, &nhi);
+                } else {
+                    nlo = S.lo[q] + ((uint32_t)d << S.shift[q]);
+                    uint64_t top = (uint64_t)S.lo[q] + ((uint64_t)(d + 1) << S.shift[q]);
+                    nhi = top < (uint64_t)S.hi[q] ? (uint32_t)top : S.hi[q];
+                }
+                if (lane == 0) {
+                    S.above[q] += gt;
+                    S.lo[q] = nlo;
+                    S.hi[q] = nhi;
+                    const bool single = nhi - nlo == 1u;
+                    if (in <= ST_CAP || single) {
+                        S.mode[q] = M_COLLECT;
+                        S.eqmode[q] = single && in > ST_CAP;
+                        S.cnt[q] = 0;
+                    } else {
+                        S.mode[q] = M_HIST;
+                        S.shift[q] = range_shift(nlo, nhi);
+                    }
+                }
+            } else if (mode == M_COLLECT) {
+                const int need_in = S.need[q] - S.above[q];
+                int need_eq;
+                if (S.eqmode[q]) {
+                    need_eq = need_in;
+                } else {
+                    // exact threshold among the collected keys
+                    const int n = min(S.cnt[q], ST_CAP);
+                    constexpr int EPT = ST_CAP / WAVE;
+                    uint32_t key[EPT];
+                    bool valid[EPT];
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) {
+                        const int p = lane * EPT + e;
+                        valid[e] = p < n;
+                        key[e] = valid[e] ? S.cb[q][p][0] : 0u;
+                    }
+                    uint32_t thr;
+                    wave_radix_threshold<EPT>(key, valid, need_in, &S.hist[q][0], &thr, &need_eq);
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) {
+                        if (!valid[e]) continue;
+                        const uint32_t j = S.cb[q][lane * EPT + e][1];
+                        if (key[e] > thr) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
+                        else if (key[e] == thr) atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
+                wave_merge_first_bits(&S.sel[q][0], &S.eq[q][0], nw, need_eq);
+                if (lane == 0) S.mode[q] = M_DONE;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- read out: wave w writes queries w and w + 4
+    for (int q = wave; q < qv; q += ST_NT / WAVE) {
+        const int nc = (int)n_candidates(q_pos0 + q0 + q, m, W);
+        wave_emit_bitmap(&S.sel[q][0], (nc + 31) / 32, topk + (b * Tq + q0 + q) * k, k);
+    }
+}
+
+size_t stream_smem_bytes() { return sizeof(StreamSmem); }
+int stream_max_candidates() { return ST_MAXW * 32; }
+
+template <typename T, int HI>
+static hipError_t launch_stream_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m,
+                                  int64_t W, int k, int64_t q_pos0, const void* q_idx,
+                                  const uint8_t* kc, const uint8_t* ks, int32_t* topk,
+                                  hipStream_t st) {
+    auto kern = k_index_stream<T, HI>;
+    const size_t lds = sizeof(StreamSmem);
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    dim3 grid((unsigned)((Tq + ST_QT - 1) / ST_QT), (unsigned)B);
+    hipLaunchKernelGGL(kern, grid, dim3(ST_NT), lds, st, (const T*)q_idx, kc, ks, topk, Tq, dI,
+                       Nc, m, W, k, q_pos0);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_stream(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
+                               int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
+                               const uint8_t* kc, const uint8_t* ks, int32_t* topk,
+                               hipStream_t st) {
+    if (B == 0 || Tq == 0) return hipSuccess;
+#define CSA_ST_CASE(TT, HH) \
+    return launch_stream_t<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk, st)
+    if (dt == 0) {
+        if (HI == 1) CSA_ST_CASE(float, 1);
+        if (HI == 2) CSA_ST_CASE(float, 2);
+        CSA_ST_CASE(float, 4);
+    }
+    if (HI == 1) CSA_ST_CASE(uint16_t, 1);
+    if (HI == 2) CSA_ST_CASE(uint16_t, 2);
+    CSA_ST_CASE(uint16_t, 4);
+#undef CSA_ST_CASE
+}
+
+}  // namespace csa

@@ -197,6 +197,19 @@ k_topk_merge(const u32x2* __restrict__ part, int32_t* __restrict__ topk, int64_t
     for (int s = total + tid; s < k; s += NT) out[s] = -1;
 }
 
+int stream_max_candidates();
+int decode_max_candidates();
+int decode_max_rows();
+size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap);
+hipError_t launch_index_stream(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
+                               int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
+                               const uint8_t* kc, const uint8_t* ks, int32_t* topk,
+                               hipStream_t st);
+hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
+                               int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
+                               const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
+                               hipStream_t st);
+
 IndexPlan plan_index(int64_t B, int64_t Tq, int HI, int dI, int64_t Nc, int64_t m, int64_t W,
                      int k, int64_t q_pos0) {
     IndexPlan p{};
@@ -205,7 +218,16 @@ IndexPlan plan_index(int64_t B, int64_t Tq, int HI, int dI, int64_t Nc, int64_t 
     p.n_qtiles = (Tq + p.qt - 1) / p.qt;
     int64_t maxc = Tq > 0 ? n_candidates(q_pos0 + Tq - 1, m, W) : 0;
     p.n_chunks = maxc > 0 ? (maxc + p.ch - 1) / p.ch : 1;
-    p.ws_bytes = p.n_chunks > 1 ? (size_t)(B * Tq * p.n_chunks * k) * sizeof(u32x2) : 0;
+    if (Tq <= decode_max_rows() && maxc > 4096 && maxc <= decode_max_candidates()) {
+        p.path = IDX_DECODE;
+        p.ws_bytes = decode_ws_bytes(B, Tq, maxc);
+    } else if (maxc <= stream_max_candidates()) {
+        p.path = IDX_STREAM;
+        p.ws_bytes = 0;
+    } else {
+        p.path = IDX_CHUNK;
+        p.ws_bytes = p.n_chunks > 1 ? (size_t)(B * Tq * p.n_chunks * k) * sizeof(u32x2) : 0;
+    }
     (void)Nc; (void)dI;
     return p;
 }
@@ -240,6 +262,12 @@ hipError_t launch_index_topk(int dt, const IndexPlan& p, int64_t B, int64_t Tq, 
                              const void* q_idx, const uint8_t* kc, const uint8_t* ks,
                              int32_t* topk, void* ws, hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
+    if (p.path == IDX_STREAM)
+        return launch_index_stream(dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk,
+                                   st);
+    if (p.path == IDX_DECODE)
+        return launch_index_decode(dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk,
+                                   ws, st);
     hipError_t e;
 #define CSA_IDX_CASE(TT, HH)                                                                  \
     e = launch_chunk<TT, HH>(p, B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk, ws, st)

@@ -14,7 +14,14 @@ hipError_t launch_compress(int dt, const void* x, const void* gate, void* out, i
 hipError_t launch_quant_mxfp4(int dt, const void* x, uint8_t* codes, uint8_t* scales,
                               int64_t rows, int d, hipStream_t st);
 
+// Indexer paths: STREAM (one block per 8 query rows streams all their
+// candidates), DECODE (<= 8 rows over a long context: chunked scoring to
+// the workspace + one select block per row), CHUNK (chunk-local top-k lists
+// + merge; any size).
+enum IndexPath { IDX_STREAM = 0, IDX_DECODE = 1, IDX_CHUNK = 2 };
+
 struct IndexPlan {
+    int path;
     int qt;            // queries per tile (32 / HI)
     int ch;            // candidates per chunk
     int64_t n_qtiles;

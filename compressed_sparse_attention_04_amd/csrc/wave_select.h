@@ -1,0 +1,190 @@
+// wave_select.h -- pieces of the streaming exact top-k used by the indexer
+// kernels that never hold all of a query's scores at once.
+//
+// A query's candidates are ordered by key = fp32 bits of the (non-negative)
+// score, larger first, equal keys broken toward the lower candidate index.
+// The threshold is narrowed pass by pass over a key range [lo, hi):
+//   level 1: 1024 fixed bins -- bin 0 = [0, 2^-6), bins 1..1022 split
+//            [2^-6, ~2^10) into 1/64-octave ranges, bin 1023 = the rest;
+//   level n: 1024 equal sub-ranges of the previous range.
+// Keys >= hi are kept for sure (marked in a candidate bitmap); keys inside
+// the final range are resolved exactly, either from a small collected
+// buffer or, for a range holding one key value, by candidate order.  The
+// kept set is read out of the bitmap in ascending candidate order.
+#pragma once
+#include "common.h"
+
+namespace csa {
+
+constexpr int SEL_NB = 1024;                       // histogram bins per level
+constexpr uint32_t L1_BASE = 121u << 23;           // fp32 bits of 2^-6
+constexpr uint32_t KEY_END = 0xFFFFFFFFu;          // exclusive top of key space
+
+__device__ __forceinline__ int lvl1_bin(uint32_t key) {
+    if (key < L1_BASE) return 0;
+    uint32_t d = ((key - L1_BASE) >> 17) + 1u;
+    return d > 1023u ? 1023 : (int)d;
+}
+
+__device__ __forceinline__ void lvl1_range(int d, uint32_t* lo, uint32_t* hi) {
+    if (d == 0) {
+        *lo = 0u;
+        *hi = L1_BASE;
+    } else {
+        *lo = L1_BASE + ((uint32_t)(d - 1) << 17);
+        *hi = d == 1023 ? KEY_END : L1_BASE + ((uint32_t)d << 17);
+    }
+}
+
+// shift that splits [lo, hi) into at most SEL_NB sub-ranges
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+    uint32_t span = hi - lo - 1u;                  // >= 1 when refining
+    int bits = 32 - __clz(span);
+    return bits > 10 ? bits - 10 : 0;
+}
+
+// Wave-wide search of a SEL_NB-bin histogram (lane l owns bins 16l..16l+15):
+// the largest bin d with count(bins > d) < need <= count(bins >= d).
+// Returns d; *gt = count(bins > d), *in = count(bin d).  need >= 1 and the
+// histogram must hold at least need entries.
+__device__ __forceinline__ int wave_hist_find(const uint32_t* hist, int need, int* gt, int* in) {
+    const int lane = threadIdx.x % WAVE;
+    uint32_t c[16];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        c[i] = hist[lane * 16 + i];
+        s += (int)c[i];
+    }
+    int incl = wave_incl_scan(s);
+    int total = __shfl(incl, WAVE - 1, WAVE);
+    int suffix_excl = total - incl;                // count in lanes above this one
+    int found = -1, fgt = 0, fin = 0;
+    if (suffix_excl < need && suffix_excl + s >= need) {
+        int acc = suffix_excl;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            if (found < 0 && acc + (int)c[i] >= need) {
+                found = lane * 16 + i;
+                fgt = acc;
+                fin = (int)c[i];
+            }
+            acc += (int)c[i];
+        }
+    }
+    uint64_t who = __ballot(found >= 0);
+    int src = __ffsll((unsigned long long)who) - 1;
+    *gt = __shfl(fgt, src, WAVE);
+    *in = __shfl(fin, src, WAVE);
+    return __shfl(found, src, WAVE);
+}
+
+// Exact threshold among n <= 64*EPT collected keys (wave-wide, keys in
+// registers, 0xFFFFFFFF-free): the key T of the need-th largest and how many
+// keys equal to T are kept (need_eq).  hist: 256 words of scratch LDS.
+template <int EPT>
+__device__ __forceinline__ void wave_radix_threshold(const uint32_t (&key)[EPT],
+                                                     const bool (&valid)[EPT], int need,
+                                                     uint32_t* hist, uint32_t* T_out,
+                                                     int* need_eq_out) {
+    const int lane = threadIdx.x % WAVE;
+    uint32_t prefix = 0, mask = 0;
+    int rem = need;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hist[lane * 4 + i] = 0u;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (valid[e] && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+        __builtin_amdgcn_wave_barrier();
+        // lane l owns bins 4l..4l+3
+        uint32_t c[4];
+        int s = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = hist[lane * 4 + i];
+            s += (int)c[i];
+        }
+        int incl = wave_incl_scan(s);
+        int total = __shfl(incl, WAVE - 1, WAVE);
+        int above = total - incl;
+        int found = -1, fgt = 0;
+        if (above < rem && above + s >= rem) {
+            int acc = above;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                if (found < 0 && acc + (int)c[i] >= rem) {
+                    found = lane * 4 + i;
+                    fgt = acc;
+                }
+                acc += (int)c[i];
+            }
+        }
+        uint64_t who = __ballot(found >= 0);
+        int src = __ffsll((unsigned long long)who) - 1;
+        int d = __shfl(found, src, WAVE);
+        rem -= __shfl(fgt, src, WAVE);
+        prefix |= (uint32_t)d << shift;
+        mask |= 255u << shift;
+        __builtin_amdgcn_wave_barrier();
+    }
+    *T_out = prefix;
+    *need_eq_out = rem;
+}
+
+// Keep the first need_eq set bits of eq (in candidate order) by OR-ing them
+// into sel; nw words, wave-wide (lane l owns words l*per .. l*per+per-1).
+__device__ __forceinline__ void wave_merge_first_bits(uint32_t* sel, const uint32_t* eq, int nw,
+                                                      int need_eq) {
+    if (need_eq <= 0) return;
+    const int lane = threadIdx.x % WAVE;
+    const int per = (nw + WAVE - 1) / WAVE;
+    const int w0 = lane * per, w1 = min(nw, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(eq[w]);
+    int before = wave_incl_scan(cnt) - cnt;
+    for (int w = w0; w < w1 && before < need_eq; ++w) {
+        uint32_t bits = eq[w];
+        int c = __popc(bits);
+        if (before + c > need_eq) {              // keep only the lowest bits
+            int keep = need_eq - before;
+            uint32_t kept = 0;
+            for (int i = 0; i < keep; ++i) {
+                uint32_t low = bits & (0u - bits);
+                kept |= low;
+                bits ^= low;
+            }
+            bits = kept;
+            c = keep;
+        }
+        sel[w] |= bits;
+        before += c;
+    }
+}
+
+// Write the set bits of sel (nw words) as ascending candidate indices into
+// out[0..k), padding with -1.  Wave-wide.
+__device__ __forceinline__ void wave_emit_bitmap(const uint32_t* sel, int nw, int32_t* out,
+                                                 int k) {
+    const int lane = threadIdx.x % WAVE;
+    const int per = (nw + WAVE - 1) / WAVE;
+    const int w0 = lane * per, w1 = min(nw, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    int pos = wave_incl_scan(cnt) - cnt;
+    int total = __shfl(wave_incl_scan(cnt), WAVE - 1, WAVE);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t bits = sel[w];
+        while (bits) {
+            int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            if (pos < k) out[pos] = w * 32 + b;
+            pos++;
+        }
+    }
+    for (int s = total + lane; s < k; s += WAVE) out[s] = -1;
+}
+
+}  // namespace csa

@@ -114,17 +114,26 @@ def test_index_bf16_one_chunk(T, q_pos0, Tq, B):
 
 
 @pytest.mark.parametrize("T,q_pos0,Tq,B,k", [
-    (40000, 39990, 10, 2, 512),    # 9966+ candidates: 3 chunks + merge
-    (40000, 16500, 9, 1, 300),     # chunk boundary at 4096 candidates
-    (4 * 70000, 4 * 70000 - 1, 1, 3, 512),   # decode row, 18 chunks
+    # streaming path (candidates <= 32768 per block of 8 rows)
+    (40000, 39990, 10, 2, 512),
+    (40000, 16500, 9, 1, 300),
+    (4 * 32768, 4 * 32768 - 20, 20, 1, 512),   # largest streaming candidate count
+    # decode path (<= 8 rows, > 4096 candidates): chunked scores + select
+    (4 * 70000, 4 * 70000 - 1, 1, 3, 512),
+    (4 * 50000, 4 * 50000 - 8, 8, 2, 512),
+    (4 * 262144, 4 * 262144 - 1, 1, 2, 512),   # 1M-token context row
+    (4 * 5000, 4 * 5000 - 3, 3, 1, 2048),
+    # chunk + merge path (> 8 rows with > 32768 candidates)
+    (140000, 139990, 10, 1, 512),
 ])
-def test_index_bf16_multi_chunk(T, q_pos0, Tq, B, k):
-    say("index multi chunk", T, q_pos0, Tq, B, k)
+def test_index_bf16_paths(T, q_pos0, Tq, B, k):
+    say("index paths", T, q_pos0, Tq, B, k)
     w = I.Workload("t", "csa", seed=22, dtype="bf16", B=B, T=T, m=4, H=128, D=128, k=k)
     index_case(w, q_pos0, Tq)
 
 
-@pytest.mark.parametrize("T,q_pos0,Tq", [(3000, 2900, 8), (40000, 39990, 3)])
+@pytest.mark.parametrize("T,q_pos0,Tq", [(3000, 2900, 8), (40000, 39990, 3), (40000, 39990, 9),
+                                         (140000, 139990, 10)])
 def test_index_tie_storm_keeps_lowest(T, q_pos0, Tq):
     say("index tie storm", T, q_pos0, Tq)
     w = I.Workload("t", "csa", seed=23, dtype="bf16", B=1, T=T, m=4, H=128, D=128)
