@@ -71,12 +71,19 @@ def ws_index(L, *a):
 
 
 def test_index_workspace_and_rejects(L):
-    # decode: 16 x 262144 compressed entries -> 64 chunks of 4096, union merge
+    # decode rows over 262,112 candidates: per-row histograms (1024 words)
+    # plus every candidate's score (rows padded to 4 words)
     st, n = ws_index(L, 16, 1, 4, 64, 262144, 4, 128, 512, (1 << 20) - 1)
-    assert st == 0 and n == 16 * 1 * 64 * 512 * 8
-    # one chunk needs no workspace
+    assert st == 0 and n == 16 * 1 * (262112 + 1024) * 4
+    # the streaming path (<= 32768 candidates) needs no workspace
     st, n = ws_index(L, 1, 16, 2, 32, 256, 4, 128, 16, 1008)
     assert st == 0 and n == 0
+    st, n = ws_index(L, 1, 32768, 4, 64, 8192, 4, 128, 512, 0)
+    assert st == 0 and n == 0
+    # > 8 rows over > 32768 candidates: chunk lists of (key, index) pairs,
+    # 9 chunks of 4096 for 34,966 candidates
+    st, n = ws_index(L, 1, 10, 4, 64, 35000, 4, 128, 512, 139990)
+    assert st == 0 and n == 10 * 9 * 512 * 8
     assert ws_index(L, 1, 16, 3, 32, 256, 4, 128, 16, 1008)[0] == EUNSUP      # HI
     assert ws_index(L, 1, 16, 2, 48, 256, 4, 128, 16, 1008)[0] == EUNSUP      # dI
     assert ws_index(L, 1, 16, 2, 32, 256, 4, 128, 4096, 1008)[0] == EINVAL    # k
