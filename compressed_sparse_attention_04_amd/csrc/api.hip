@@ -174,6 +174,18 @@ static csa_status attend_shape(const char* fn, csa_dtype dt, int64_t B, int64_t 
     return CSA_OK;
 }
 
+// The bf16 attention kernel addresses rows with 32-bit byte offsets and
+// key-list positions with 32-bit ints.
+static csa_status attend_ranges(const char* fn, int64_t Nc, int64_t D, int64_t raw_len, int64_t k,
+                                int64_t W, int64_t q_pos0, int64_t Tq, int64_t m) {
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    CHECK(Nc * D * 2 <= lim && raw_len * D * 2 <= lim, CSA_EUNSUPPORTED,
+          "%s: caches larger than 2 GiB per sequence are not supported", fn);
+    const int64_t keys = (Tq > 0 ? csa::n_candidates(q_pos0 + Tq - 1, m, W) : 0) + k + W;
+    CHECK(keys <= lim, CSA_EUNSUPPORTED, "%s: key list too long", fn);
+    return CSA_OK;
+}
+
 csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
                                 int64_t k, int64_t W, size_t* bytes) {
     const char* fn = "csa_attend_workspace";
@@ -197,6 +209,7 @@ csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
     CHECK(q && ck && cv && topk && rk && rv && o, CSA_EINVAL, "%s: null pointer", fn);
     CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
               aligned16(o), CSA_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+    if (csa_status s = attend_ranges(fn, Nc, D, raw_len, k, W, q_pos0, Tq, m)) return s;
     csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, k + W);
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
@@ -232,6 +245,7 @@ csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
     CHECK(q && ck && cv && rk && rv && o, CSA_EINVAL, "%s: null pointer", fn);
     CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
               aligned16(o), CSA_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+    if (csa_status s = attend_ranges(fn, Nc, D, raw_len, 0, W, q_pos0, Tq, m)) return s;
     csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0));
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);

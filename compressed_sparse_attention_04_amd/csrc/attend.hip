@@ -75,74 +75,66 @@ struct TileGeom {
     static constexpr int BYTES = KT * ROWB;         // bytes per tile and tensor
 };
 
+// Swizzle of row r: an injective map of r mod CH whose values for four
+// consecutive rows (4-aligned) differ above bit 0.  Chunk c of row r sits in
+// slot c ^ f(r), so the 16 rows of one MFMA K read and the 4 rows x 2
+// chunks of one transposing V read land on distinct banks.
 template <int D>
-__device__ __forceinline__ int slot_of(int r, int c) { return c ^ (r & (TileGeom<D>::CH - 1)); }
-
-// Row of key-list entry s (compressed row in ck/cv, or raw row in rk/rv) and
-// whether it contributes.  Entries that contribute nothing point at the
-// window's first raw row, which always exists.
-__device__ __forceinline__ bool key_row(const KeyList& L, int64_t s, int64_t s_end, bool sparse,
-                                        const CSA_LDS int32_t* ssel, int64_t nc_t,
-                                        int64_t raw_pos0, bool* comp, int64_t* row) {
-    *comp = false;
-    *row = L.w0 - raw_pos0;
-    if (s >= s_end) return false;
-    if (s < L.nsel) {
-        const int64_t j = sparse ? (int64_t)ssel[s] : s;
-        if (j < 0 || j >= nc_t) return false;
-        *comp = true;
-        *row = j;
-        return true;
-    }
-    *row = L.w0 + (s - L.nsel) - raw_pos0;
-    return true;
+__device__ __forceinline__ int row_swz(int r) {
+    if constexpr (TileGeom<D>::CH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
 }
+template <int D>
+__device__ __forceinline__ int slot_of(int r, int c) { return c ^ row_swz<D>(r); }
 
-// Issue this wave's copies of the K and V rows of the tile starting at key
-// s0; returns the wave's bits of the tile's contribution mask.
+// Issue this wave's copies of the K and V rows of tile tau.  The key list
+// of a query is cut into ct tiles of compressed rows (row ssel[s] for CSA,
+// row s for HCA; s < nval) followed by the tiles of its raw window (nwin
+// rows from raw_first), so every tile reads from one source.  Rows past the
+// end of a part repeat a row that exists and are masked by the caller.
+// All offsets fit 32 bits (validated on the host).
 template <int NW, int D>
-__device__ __forceinline__ uint32_t issue_tile(int64_t s0, int64_t s_end, const KeyList& L,
-                                               bool sparse, const CSA_LDS int32_t* ssel,
-                                               int64_t nc_t,
-                                               int64_t raw_pos0, const uint16_t* ckb,
-                                               const uint16_t* cvb, const uint16_t* rkb,
-                                               const uint16_t* rvb, CSA_LDS uint8_t* sk,
-                                               CSA_LDS uint8_t* sv) {
+__device__ __forceinline__ void issue_tile(int tau, int ct, int nval, int nwin, int raw_first,
+                                           bool sparse, const CSA_LDS int32_t* ssel,
+                                           const char* ckb, const char* cvb, const char* rkb,
+                                           const char* rvb, CSA_LDS uint8_t* sk,
+                                           CSA_LDS uint8_t* sv) {
     using G = TileGeom<D>;
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    uint32_t mask = 0;
+    const bool comp = tau < ct;
+    const int base = comp ? ATT_KT * tau : ATT_KT * (tau - ct);
+    const char* kb = comp ? ckb : rkb;
+    const char* vb = comp ? cvb : rvb;
 #pragma unroll
     for (int ins = wave; ins < G::NINS; ins += NW) {
         const int r = ins * G::RPI + lane / G::CH;
-        const int c = slot_of<D>(r, lane % G::CH);   // slot <-> chunk is an involution
-        bool comp;
-        int64_t row;
-        const bool ok = key_row(L, s0 + r, s_end, sparse, ssel, nc_t, raw_pos0, &comp, &row);
-        const uint16_t* kp = (comp ? ckb : rkb) + row * D + c * 8;
-        const uint16_t* vp = (comp ? cvb : rvb) + row * D + c * 8;
-        __builtin_amdgcn_global_load_lds(kp, (CSA_LDS void*)(sk + ins * G::RPI * G::ROWB), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp, (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB), 16, 0, 0);
-        const uint64_t bal = __ballot(ok && (lane % G::CH) == 0);
-#pragma unroll
-        for (int x = 0; x < G::RPI; ++x)
-            mask |= (uint32_t)((bal >> (x * G::CH)) & 1ull) << (ins * G::RPI + x);
+        const int cb = slot_of<D>(r, lane % G::CH) * 16;   // slot <-> chunk: involution
+        int row;
+        if (comp) row = sparse ? ssel[base + r] : min(base + r, nval - 1);
+        else row = raw_first + min(base + r, nwin - 1);
+        const uint32_t off = (uint32_t)row * (uint32_t)G::ROWB + (uint32_t)cb;
+        __builtin_amdgcn_global_load_lds(kb + off, (CSA_LDS void*)(sk + ins * G::RPI * G::ROWB),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + off, (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB),
+                                         16, 0, 0);
     }
-    return mask;
 }
 
 // Running softmax state of one lane (one head, half of each key tile).
 template <int D>
 struct Online {
     f32x16 acc[D / 32];
-    float m_run, l_run;
+    float m_run;          // reference maximum (raw score units)
+    float mb;             // -m_run * scale_log2, or 0 while m_run is -inf
+    float l_run;          // running sum of the bf16-rounded probabilities
 };
 
 // One 32-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  K and V
-// are the tile's LDS copies; vmask marks the keys that contribute.
+// are the tile's LDS copies; the first nvalid keys of the tile contribute.
 template <int D>
 __device__ __forceinline__ void tile_compute(Online<D>& S, const bf16x8 (&qop)[D / 16],
                                              const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
-                                             uint32_t vmask, float scale_log2) {
+                                             int nvalid, float scale_log2) {
     using G = TileGeom<D>;
     const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
     // S^T: rows = keys (8*(r/4) + 4*kb + r%4), column = head
@@ -153,38 +145,48 @@ __device__ __forceinline__ void tile_compute(Online<D>& S, const bf16x8 (&qop)[D
             K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], sacc, 0, 0, 0);
     }
-    if (vmask != ~0u) {
+    if (nvalid < ATT_KT) {                         // wave-uniform
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r / 4) + 4 * kb + (r % 4);
-            if (!((vmask >> key) & 1u)) sacc[r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+            if (8 * (r / 4) + 4 * kb + (r % 4) >= nvalid) sacc[r] = -INFINITY;
     }
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(S.m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((S.m_run - m_use) * scale_log2);
-    const float mb = -m_use * scale_log2;
-    S.m_run = m_new;
-    float psum = 0.f;
-    uint32_t pb[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, mb));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, mb));
-        psum += p0 + p1;
-        pb[r / 2] = pack_bf16x2(p0, p1);
-    }
-    S.l_run = S.l_run * alpha + psum;
-    if (__ballot(alpha != 1.f)) {
+    // Lazy rescaling: the reference maximum moves only when a score exceeds
+    // it by more than a factor 2^8 in probability, so p stays <= 256; sum
+    // and accumulators share the reference, so the quotient is unchanged.
+    // (tmax - m_run) is NaN while both are -inf: no move.
+    const bool grow = (tmax - S.m_run) * scale_log2 > 8.f;
+    if (__ballot(grow)) {
+        float alpha = 1.f;
+        if (grow) {
+            alpha = __builtin_amdgcn_exp2f((S.m_run - tmax) * scale_log2);   // 0 from -inf
+            S.m_run = tmax;
+            S.mb = -tmax * scale_log2;
+        }
+        S.l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) S.acc[dt][r] *= alpha;
     }
+    uint32_t pb[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, S.mb));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, S.mb));
+        pb[r / 2] = pack_bf16x2(p0, p1);
+    }
+    // the sum takes the same bf16 values the PV product takes
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum = S.l_run;
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[x]), ones, psum,
+                                               false);
+    S.l_run = psum;
     // O^T += V^T P^T.  k-step u covers keys 16u..16u+15; k-slot s of lane
     // half kb is key 16u + 8*(s/4) + 4*kb + s%4 (the S^T register order).
     // Each half of the V^T operand is one transposing LDS read: lane
@@ -244,36 +246,62 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     __shared__ __attribute__((aligned(16))) uint8_t sK1[G::BYTES], sV1[G::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t sK2[G::BYTES], sV2[G::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t sK3[G::BYTES], sV3[G::BYTES];
-    __shared__ uint32_t sM0[NW], sM1[NW], sM2[NW], sM3[NW];   // contribution masks
     __shared__ int32_t sSel[2048];                  // this query's kept indices (CSA)
+    __shared__ int sCnt[NW];
 
-    const int64_t i = blockIdx.x;
+    const int i = (int)blockIdx.x;
     const int split = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int col = lane & 31, kb = lane >> 5;
     const int64_t t = q_pos0 + i;
     const bool sparse = topk != nullptr;
-    const KeyList L = key_list(t, m, W, k, sparse);
-    const int64_t nc_t = n_candidates(t, m, W);
+    const int nc_t = (int)n_candidates(t, m, W);
+    const int64_t w0 = t - W + 1 < 0 ? 0 : t - W + 1;
+    const int nwin = (int)(t - w0 + 1), raw_first = (int)(w0 - raw_pos0);
 
-    // this split's range of the key list, in whole tiles
-    const int64_t ntile = (L.len + KT - 1) / KT;
-    const int64_t tps = (ntile + splits - 1) / splits;
-    const int64_t s_begin = split * tps * KT;
-    const int64_t s_end = min(L.len, s_begin + tps * KT);
-
-    const uint16_t* ckb = ck + b * Nc * D;
-    const uint16_t* cvb = cv + b * Nc * D;
-    const uint16_t* rkb = rk + b * raw_len * D;
-    const uint16_t* rvb = rv + b * raw_len * D;
-
+    // compressed part of the key list: CSA keeps the valid selected indices
+    // (0 <= j < n_cand), in order, padded with row 0 to whole tiles
+    int nval = nc_t;
     if (sparse) {
+        const int nsel = min(k, nc_t);
         const int32_t* sel = topk + (b * Tq + i) * k;
-        for (int x = tid; x < L.nsel; x += NT) sSel[x] = sel[x];
+        nval = 0;
+        int jn = tid < nsel ? sel[tid] : -1;
+        for (int x0 = 0; x0 < nsel; x0 += NT) {
+            const int j = jn;
+            jn = x0 + NT + tid < nsel ? sel[x0 + NT + tid] : -1;
+            const bool ok = j >= 0 && j < nc_t;
+            const uint64_t bal = __ballot(ok);
+            if (lane == 0) sCnt[wave] = __popcll(bal);
+            __syncthreads();
+            int before = nval, total = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int c = sCnt[w];
+                before += w < wave ? c : 0;
+                total += c;
+            }
+            if (ok) sSel[before + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+            nval += total;
+            __syncthreads();
+        }
+        for (int x = nval + tid; x < ((nval + KT - 1) & ~(KT - 1)); x += NT) sSel[x] = 0;
         __syncthreads();
     }
     const CSA_LDS int32_t* ssel = (const CSA_LDS int32_t*)sSel;
+
+    // this split's range of tiles
+    const int ct = (nval + KT - 1) / KT;
+    const int ntile = ct + (nwin + KT - 1) / KT;
+    const int tps = (ntile + splits - 1) / splits;
+    const int tau0 = split * tps;
+    const int tau1 = min(ntile, tau0 + tps);
+
+    const char* ckb = reinterpret_cast<const char*>(ck + b * Nc * D);
+    const char* cvb = reinterpret_cast<const char*>(cv + b * Nc * D);
+    const char* rkb = reinterpret_cast<const char*>(rk + b * raw_len * D);
+    const char* rvb = reinterpret_cast<const char*>(rv + b * raw_len * D);
 
     // Q^T operand: head hq, d = 16*kk + 8*kb + 0..7
     const int hq = wave * 32 + col;
@@ -290,44 +318,39 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
 #pragma unroll
         for (int r = 0; r < 16; ++r) S.acc[dt][r] = 0.f;
     S.m_run = -INFINITY;
+    S.mb = 0.f;
     S.l_run = 0.f;
 
-    auto issue = [&](int64_t s0, uint8_t* sk, uint8_t* sv, uint32_t* sm) {
-        if (s0 < s_end) {
-            const uint32_t mk = issue_tile<NW, D>(s0, s_end, L, sparse, ssel, nc_t, raw_pos0, ckb, cvb,
-                                                  rkb, rvb, (CSA_LDS uint8_t*)sk,
-                                                  (CSA_LDS uint8_t*)sv);
-            if (lane == 0) sm[wave] = mk;
-        }
+    auto issue = [&](int tau, uint8_t* sk, uint8_t* sv) {
+        if (tau < tau1)
+            issue_tile<NW, D>(tau, ct, nval, nwin, raw_first, sparse, ssel, ckb, cvb, rkb, rvb,
+                              (CSA_LDS uint8_t*)sk, (CSA_LDS uint8_t*)sv);
     };
     // one tile: wait for its copies, barrier (the stage written next is then
     // free on every wave), issue the copies three tiles ahead, compute
-    auto step = [&](int64_t s0, uint8_t* ck_, uint8_t* cv_, uint32_t* cm_, uint8_t* nk_,
-                    uint8_t* nv_, uint32_t* nm_) {
-        const int64_t after = min((int64_t)(G::NST - 2), (s_end - s0 - 1) / KT);
+    auto step = [&](int tau, uint8_t* ck_, uint8_t* cv_, uint8_t* nk_, uint8_t* nv_) {
+        const int after = min(G::NST - 2, tau1 - tau - 1);
         if (after >= 2) CSA_WAIT_VM(2 * PER);
         else if (after == 1) CSA_WAIT_VM(PER);
         else CSA_WAIT_VM(0);
         lds_barrier();
-        issue(s0 + (G::NST - 1) * KT, nk_, nv_, nm_);
-        uint32_t vm = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) vm |= cm_[w];
-        tile_compute<D>(S, qop, (const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_, vm,
-                        scale_log2);
+        issue(tau + G::NST - 1, nk_, nv_);
+        const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
+        tile_compute<D>(S, qop, (const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_,
+                        nvalid, scale_log2);
     };
 
-    issue(s_begin, sK0, sV0, sM0);
-    issue(s_begin + KT, sK1, sV1, sM1);
-    issue(s_begin + 2 * KT, sK2, sV2, sM2);
-    for (int64_t s0 = s_begin; s0 < s_end; s0 += 4 * KT) {
-        step(s0, sK0, sV0, sM0, sK3, sV3, sM3);
-        if (s0 + KT >= s_end) break;
-        step(s0 + KT, sK1, sV1, sM1, sK0, sV0, sM0);
-        if (s0 + 2 * KT >= s_end) break;
-        step(s0 + 2 * KT, sK2, sV2, sM2, sK1, sV1, sM1);
-        if (s0 + 3 * KT >= s_end) break;
-        step(s0 + 3 * KT, sK3, sV3, sM3, sK2, sV2, sM2);
+    issue(tau0, sK0, sV0);
+    issue(tau0 + 1, sK1, sV1);
+    issue(tau0 + 2, sK2, sV2);
+    for (int tau = tau0; tau < tau1; tau += 4) {
+        step(tau, sK0, sV0, sK3, sV3);
+        if (tau + 1 >= tau1) break;
+        step(tau + 1, sK1, sV1, sK0, sV0);
+        if (tau + 2 >= tau1) break;
+        step(tau + 2, sK2, sV2, sK1, sV1);
+        if (tau + 3 >= tau1) break;
+        step(tau + 3, sK3, sV3, sK2, sV2);
     }
     const float l_tot = S.l_run + __shfl_xor(S.l_run, 32, 64);
     if (splits == 1) {

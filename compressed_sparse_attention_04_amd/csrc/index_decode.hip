@@ -8,10 +8,14 @@
 //   k_dscore : scores of <= 8 query rows against one chunk (scaled FP4
 //              MFMA), written as fp32 to the workspace, plus the level-1
 //              threshold histogram of each row (LDS, then global atomics);
-//   k_dselect: one block per query row narrows the threshold from the
-//              histogram, collects from the stored scores and emits the
-//              kept indices in ascending order (same exact rule as the
-//              streaming kernel: score desc, index asc).
+//   k_dcollect: blocks over (chunk of 4096 stored scores, row) find the
+//              threshold range from the row's histogram, write the chunk's
+//              bitmap words of the surely kept keys (above the range) and
+//              append the keys inside the range to the row's small buffer;
+//   k_dfinal : one block per row resolves the range exactly from the buffer
+//              (or, when the range holds too many keys, narrows it further
+//              by scanning the stored scores) and emits the kept indices in
+//              ascending order (score desc, index asc, as everywhere).
 #include "internal.h"
 #include "mxfp4.h"
 #include "wave_select.h"
@@ -20,7 +24,7 @@ namespace csa {
 
 constexpr int DS_NT = 256;
 constexpr int DS_QT = 8;
-constexpr int DS_CH = 2048;            // candidates per scoring block
+constexpr int DS_CH = 4096;            // candidates per scoring block
 constexpr int DL_NT = 1024;
 constexpr int DL_CAP = 1024;           // collected keys per row
 constexpr int DL_MAXW = 8192;          // bitmap words -> 262144 candidates
@@ -33,13 +37,54 @@ __global__ void k_zero_u32(uint32_t* p, int64_t n) {
     if (i < n) p[i] = 0u;
 }
 
+// Workspace of the decode path (rows = B * Tq; u32 words, counts padded to
+// multiples of 4): hist [rows][1024] | cnt [rows] | thr [rows][4] | bitmap [rows][DL_MAXW] | buffer [rows][DL_CAP] (key,
+// index) | scores [rows][stride]
+struct DecodeWs {
+    uint32_t* hist;
+    uint32_t* cnt;
+    u32x4* thr;        // [rows] level-1 range: lo, hi, count above, count inside
+    uint32_t* bmp;
+    u32x2* cb;
+    uint32_t* scores;
+};
+
+__host__ __device__ __forceinline__ int64_t pad4(int64_t n) { return (n + 3) & ~(int64_t)3; }
+
+__host__ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int64_t B, int64_t rows) {
+    DecodeWs w;
+    uint32_t* p = reinterpret_cast<uint32_t*>(ws);
+    w.hist = p;
+    p += rows * SEL_NB;
+    w.cnt = p;
+    p += pad4(rows);
+    w.thr = reinterpret_cast<u32x4*>(p);
+    p += rows * 4;
+    w.bmp = p;
+    p += rows * DL_MAXW;
+    w.cb = reinterpret_cast<u32x2*>(p);
+    p += rows * DL_CAP * 2;
+    w.scores = p;
+    return w;
+}
+
+// Threshold range of a row at level 1 from its histogram (one wave).
+__device__ __forceinline__ void lvl1_threshold(const uint32_t* hist, int need, uint32_t* lo,
+                                               uint32_t* hi, int* above, int* in) {
+    int gt, cnt_in;
+    const int d = wave_hist_find(hist, need, &gt, &cnt_in);
+    lvl1_range(d, lo, hi);
+    *above = gt;
+    *in = cnt_in;
+}
+
 template <typename T, int HI>
 __global__ void __launch_bounds__(DS_NT)
 k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
-         const uint8_t* __restrict__ ks, uint32_t* __restrict__ scores,
-         uint32_t* __restrict__ ghist, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W,
-         int64_t q_pos0, int64_t ncap) {
-    __shared__ uint32_t hist[DS_QT][SEL_NB];
+         const uint8_t* __restrict__ ks, DecodeWs ws, int64_t Tq, int dI, int64_t Nc, int64_t m,
+         int64_t W, int k, int64_t q_pos0, int64_t ncap) {
+    extern __shared__ uint32_t hist_raw[];           // [Tq][SEL_NB]
+    uint32_t (*hist)[SEL_NB] = reinterpret_cast<uint32_t (*)[SEL_NB]>(hist_raw);
     constexpr int NU = 16 / HI;
     const int64_t c0 = (int64_t)blockIdx.x * DS_CH;
     const int64_t b = blockIdx.y;
@@ -47,9 +92,9 @@ k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int row = lane & 31, kb = lane >> 5;
     const int64_t nc_max = n_candidates(q_pos0 + qv - 1, m, W);
-    const int nkeys = (int)min((int64_t)DS_CH, nc_max - c0);
-    if (nkeys <= 0) return;
-    for (int i = tid; i < DS_QT * SEL_NB; i += DS_NT) (&hist[0][0])[i] = 0u;
+    const int nkeys = (int)min((int64_t)DS_CH, nc_max - c0);   // >= 1: grid covers nc_max
+    uint32_t* scores = ws.scores;
+    for (int i = tid; i < qv * SEL_NB; i += DS_NT) hist_raw[i] = 0u;
 
     i32x8 aop = {0, 0, 0, 0, 0, 0, 0, 0};
     int sa = 127;
@@ -85,7 +130,7 @@ k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     const int kbytes = dI / 2, kscales = dI / 32;
     const uint8_t* kcb = kc + b * Nc * kbytes;
     const uint8_t* ksb = ks + b * Nc * kscales;
-    constexpr int UNR = 4;                           // tiles in flight per wave
+    constexpr int UNR = 8;                           // key tiles in flight per wave
     const int ntiles = (nkeys + 31) / 32;
     for (int t0 = wave * UNR; t0 < ntiles; t0 += (DS_NT / WAVE) * UNR) {
         i32x8 bop[UNR];
@@ -126,8 +171,8 @@ k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     }
     __syncthreads();
     for (int i = tid; i < qv * SEL_NB; i += DS_NT) {
-        const uint32_t c = (&hist[0][0])[i];
-        if (c) atomicAdd(&ghist[(b * Tq) * SEL_NB + i], c);
+        const uint32_t c = hist_raw[i];
+        if (c) atomicAdd(&ws.hist[(b * Tq) * SEL_NB + i], c);
     }
 }
 
@@ -157,56 +202,126 @@ __device__ __forceinline__ void scan_scores(const uint32_t* __restrict__ sc, int
     for (int j = 4 * nv + (int)threadIdx.x; j < nc; j += DL_NT) fn(sc[j], j);
 }
 
+constexpr int DC_NT = 256;
+constexpr int DC_CH = 4096;            // stored scores per collecting block
+
+__global__ void __launch_bounds__(DC_NT)
+k_dcollect(DecodeWs ws, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
+           int64_t stride) {
+    __shared__ uint32_t words[DC_CH / 32];
+    const int64_t c0 = (int64_t)blockIdx.x * DC_CH;
+    const int64_t q = blockIdx.y, b = blockIdx.z;
+    const int64_t rowi = b * Tq + q;
+    const int nc = (int)n_candidates(q_pos0 + q, m, W);
+    if (nc <= k || c0 >= nc) return;                 // the final kernel needs nothing here
+    const int tid = threadIdx.x;
+    const int n = (int)min((int64_t)DC_CH, (int64_t)nc - c0);
+    const uint32_t* sc = ws.scores + rowi * stride + c0;
+    const int nv = n / 4;
+    // this block's scores are in flight while wave 0 finds the range
+    constexpr int VPT = DC_CH / 4 / DC_NT;
+    u32x4 vals[VPT];
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+        const int v = tid + x * DC_NT;
+        vals[x] = v < nv ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sc) + v)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+    __shared__ u32x4 s_thr;
+    if (tid < WAVE) {
+        uint32_t lo, hi;
+        int above, in;
+        lvl1_threshold(ws.hist + rowi * SEL_NB, k, &lo, &hi, &above, &in);
+        const u32x4 t = {lo, hi, (uint32_t)above, (uint32_t)in};
+        if (tid == 0) {
+            s_thr = t;
+            if (blockIdx.x == 0) ws.thr[rowi] = t;   // for the final kernel
+        }
+    }
+    for (int w = tid; w < DC_CH / 32; w += DC_NT) words[w] = 0u;
+    __syncthreads();
+    const uint32_t lo = s_thr[0], hi = s_thr[1];
+    const bool collect = s_thr[3] <= (uint32_t)DL_CAP;
+    uint32_t* cnt = ws.cnt + rowi;
+    u32x2* cb = ws.cb + rowi * DL_CAP;
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+        const int v = tid + x * DC_NT;
+        if (v >= nv) break;
+        const u32x4 w = vals[x];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * v + e;
+            const uint32_t key = w[e];
+            if (key >= hi) {
+                atomicOr(&words[j >> 5], 1u << (j & 31));
+            } else if (key >= lo && collect) {
+                const uint32_t pos = atomicAdd(cnt, 1u);
+                if (pos < (uint32_t)DL_CAP) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
+            }
+        }
+    }
+    for (int j = 4 * nv + tid; j < n; j += DC_NT) {
+        const uint32_t key = sc[j];
+        if (key >= hi) {
+            atomicOr(&words[j >> 5], 1u << (j & 31));
+        } else if (key >= lo && collect) {
+            const uint32_t pos = atomicAdd(cnt, 1u);
+            if (pos < (uint32_t)DL_CAP) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
+        }
+    }
+    __syncthreads();
+    for (int w = tid; w < (n + 31) / 32; w += DC_NT) ws.bmp[rowi * DL_MAXW + c0 / 32 + w] = words[w];
+}
+
 struct DselSmem {
     uint32_t sel[DL_MAXW];
     uint32_t eq[DL_MAXW];
     uint32_t hist[SEL_NB];
     u32x2 cb[DL_CAP];
     uint32_t lo, hi;
-    int shift, above, in, mode, cnt, eqmode;
+    int shift, above, in, mode, cnt, eqmode, need_eq;
+    int scratch[DL_NT / WAVE + 1];
 };
 
 __global__ void __launch_bounds__(DL_NT)
-k_dselect(const uint32_t* __restrict__ scores, const uint32_t* __restrict__ ghist,
-          int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
-          int64_t ncap) {
+k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t W, int k,
+         int64_t q_pos0, int64_t stride) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     DselSmem& S = *reinterpret_cast<DselSmem*>(smem_raw);
     const int64_t q = blockIdx.x, b = blockIdx.y;
+    const int64_t rowi = b * Tq + q;
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int nc = (int)n_candidates(q_pos0 + q, m, W);
     const int nw = (nc + 31) / 32;
     const int need = min(nc, k);
-    const uint32_t* sc = scores + (b * Tq + q) * ncap;
-    int32_t* out = topk + (b * Tq + q) * k;
+    const uint32_t* sc = ws.scores + rowi * stride;
+    int32_t* out = topk + rowi * k;
 
+    if (nc <= k) {                                  // every candidate is kept
+        for (int s2 = tid; s2 < k; s2 += DL_NT) out[s2] = s2 < nc ? s2 : -1;
+        return;
+    }
+    // the collecting blocks wrote the bits of the keys above the range
     for (int w = tid; w < nw; w += DL_NT) {
-        uint32_t full = 0u;
-        if (nc <= k) {
-            const int lo_b = w * 32;
-            full = lo_b + 32 <= nc ? 0xFFFFFFFFu : ((1u << (nc - lo_b)) - 1u);
-        }
-        S.sel[w] = full;
+        S.sel[w] = ws.bmp[rowi * DL_MAXW + w];
         S.eq[w] = 0u;
     }
-    if (nc > k) {
-        // level 1 from the scoring blocks' histogram
-        if (wave == 0) {
-            int gt, in;
-            for (int i = lane; i < SEL_NB; i += WAVE) S.hist[i] = ghist[(b * Tq + q) * SEL_NB + i];
-            __builtin_amdgcn_wave_barrier();
-            const int d = wave_hist_find(S.hist, need, &gt, &in);
-            if (lane == 0) {
-                uint32_t lo, hi;
-                lvl1_range(d, &lo, &hi);
-                S.lo = lo;
-                S.hi = hi;
-                S.above = gt;
-                S.in = in;
-            }
-        }
+    if (tid == 0) {
+        const u32x4 thr = ws.thr[rowi];
+        S.lo = thr[0];
+        S.hi = thr[1];
+        S.above = (int)thr[2];
+        S.in = (int)thr[3];
+        S.cnt = S.in <= DL_CAP ? (int)min(ws.cnt[rowi], (uint32_t)DL_CAP) : -1;
+    }
+    __syncthreads();
+    if (S.cnt >= 0) {
+        // the collecting blocks gathered the range's keys
+        for (int p = tid; p < S.cnt; p += DL_NT) S.cb[p] = ws.cb[rowi * DL_CAP + p];
         __syncthreads();
-        // refine while the threshold range holds too many keys
+    } else {
+        // too many keys in the level-1 range: narrow it over the stored scores
 #pragma unroll 1
         for (int it = 0; it < 6; ++it) {
             const uint32_t lo = S.lo, hi = S.hi;
@@ -232,9 +347,9 @@ k_dselect(const uint32_t* __restrict__ scores, const uint32_t* __restrict__ ghis
             }
             __syncthreads();
         }
-        // collect
+        // collect the narrowed range (keys above it are kept for sure)
         const uint32_t lo = S.lo, hi = S.hi;
-        const bool eqmode = S.in > DL_CAP;             // single-valued range with many ties
+        const bool eqmode = S.in > DL_CAP;         // single-valued range with many ties
         if (tid == 0) S.cnt = 0;
         __syncthreads();
         scan_scores(sc, nc, [&](uint32_t key, int j) {
@@ -245,44 +360,44 @@ k_dselect(const uint32_t* __restrict__ scores, const uint32_t* __restrict__ ghis
                     atomicOr(&S.eq[j >> 5], 1u << (j & 31));
                 } else {
                     const int pos = atomicAdd(&S.cnt, 1);
-                    if (pos < DL_CAP) {
-                        u32x2 e = {key, (uint32_t)j};
-                        S.cb[pos] = e;
-                    }
+                    if (pos < DL_CAP) S.cb[pos] = u32x2{key, (uint32_t)j};
                 }
             }
         });
         __syncthreads();
-        if (wave == 0) {
-            const int need_in = need - S.above;
-            int need_eq = need_in;
-            if (!eqmode) {
-                const int n = min(S.cnt, DL_CAP);
-                constexpr int EPT = DL_CAP / WAVE;
-                uint32_t key[EPT];
-                bool valid[EPT];
+        if (eqmode && tid == 0) S.cnt = -1;
+        __syncthreads();
+    }
+    if (wave == 0) {
+        const int need_in = need - S.above;
+        int need_eq = need_in;
+        if (S.cnt >= 0) {
+            const int n = min(S.cnt, DL_CAP);
+            constexpr int EPT = DL_CAP / WAVE;
+            uint32_t key[EPT];
+            bool valid[EPT];
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const int p = lane * EPT + e;
-                    valid[e] = p < n;
-                    key[e] = valid[e] ? S.cb[p][0] : 0u;
-                }
-                uint32_t T;
-                wave_radix_threshold<EPT>(key, valid, need_in, S.hist, &T, &need_eq);
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    if (!valid[e]) continue;
-                    const uint32_t j = S.cb[lane * EPT + e][1];
-                    if (key[e] > T) atomicOr(&S.sel[j >> 5], 1u << (j & 31));
-                    else if (key[e] == T) atomicOr(&S.eq[j >> 5], 1u << (j & 31));
-                }
-                __builtin_amdgcn_wave_barrier();
+            for (int e = 0; e < EPT; ++e) {
+                const int p = lane * EPT + e;
+                valid[e] = p < n;
+                key[e] = valid[e] ? S.cb[p][0] : 0u;
             }
-            wave_merge_first_bits(S.sel, S.eq, nw, need_eq);
+            uint32_t thr;
+            wave_radix_threshold<EPT>(key, valid, need_in, S.hist, &thr, &need_eq);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                if (!valid[e]) continue;
+                const uint32_t j = S.cb[lane * EPT + e][1];
+                if (key[e] > thr) atomicOr(&S.sel[j >> 5], 1u << (j & 31));
+                else if (key[e] == thr) atomicOr(&S.eq[j >> 5], 1u << (j & 31));
+            }
+            __builtin_amdgcn_wave_barrier();
         }
+        if (lane == 0) S.need_eq = need_eq;
     }
     __syncthreads();
-    if (wave == 0) wave_emit_bitmap(S.sel, nw, out, k);
+    block_merge_first_bits<DL_NT>(S.sel, S.eq, nw, S.need_eq, S.scratch);
+    block_emit_bitmap<DL_NT>(S.sel, nw, out, k, S.scratch);
 }
 
 size_t dselect_smem_bytes() { return sizeof(DselSmem); }
@@ -290,16 +405,19 @@ int decode_max_candidates() { return DL_MAXW * 32; }
 int decode_max_rows() { return DS_QT; }
 
 size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap) {
-    return (size_t)(B * Tq) * (size_t)(score_stride(ncap) + SEL_NB) * sizeof(uint32_t);
+    const int64_t rows = B * Tq;
+    const int64_t words = rows * SEL_NB + pad4(rows) + rows * 4 + rows * DL_MAXW +
+                          rows * DL_CAP * 2 + rows * score_stride(ncap);
+    return (size_t)words * sizeof(uint32_t);
 }
 
 template <typename T, int HI>
-static void launch_dscore(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W,
+static void launch_dscore(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W, int k,
                           int64_t q_pos0, const void* q_idx, const uint8_t* kc, const uint8_t* ks,
-                          uint32_t* scores, uint32_t* ghist, int64_t ncap, hipStream_t st) {
-    dim3 grid((unsigned)((ncap + DS_CH - 1) / DS_CH), (unsigned)B);
-    hipLaunchKernelGGL((k_dscore<T, HI>), grid, dim3(DS_NT), 0, st, (const T*)q_idx, kc, ks,
-                       scores, ghist, Tq, dI, Nc, m, W, q_pos0, ncap);
+                          const DecodeWs& w, int64_t ncand, int64_t stride, hipStream_t st) {
+    dim3 grid((unsigned)((ncand + DS_CH - 1) / DS_CH), (unsigned)B);
+    hipLaunchKernelGGL((k_dscore<T, HI>), grid, dim3(DS_NT), Tq * SEL_NB * sizeof(uint32_t), st,
+                       (const T*)q_idx, kc, ks, w, Tq, dI, Nc, m, W, k, q_pos0, stride);
 }
 
 hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
@@ -307,14 +425,17 @@ hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, in
                                const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
                                hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
-    const int64_t ncap = score_stride(n_candidates(q_pos0 + Tq - 1, m, W));
-    uint32_t* ghist = reinterpret_cast<uint32_t*>(ws);
-    uint32_t* scores = ghist + B * Tq * SEL_NB;
-    const int64_t nh = B * Tq * SEL_NB;
-    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st, ghist, nh);
-    if (ncap > 0) {
+    const int64_t ncand = n_candidates(q_pos0 + Tq - 1, m, W);
+    const int64_t stride = score_stride(ncand);
+    const int64_t rows = B * Tq;
+    DecodeWs w = decode_ws(ws, B, rows);
+    if (ncand > 0) {
+        // histograms and buffer counters start at zero
+        const int64_t nz = rows * SEL_NB + pad4(rows);
+        hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st,
+                           w.hist, nz);
 #define CSA_DS_CASE(TT, HH) \
-    launch_dscore<TT, HH>(B, Tq, dI, Nc, m, W, q_pos0, q_idx, kc, ks, scores, ghist, ncap, st)
+    launch_dscore<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, w, ncand, stride, st)
         if (dt == 0) {
             if (HI == 1) CSA_DS_CASE(float, 1);
             else if (HI == 2) CSA_DS_CASE(float, 2);
@@ -325,11 +446,14 @@ hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, in
             else CSA_DS_CASE(uint16_t, 4);
         }
 #undef CSA_DS_CASE
+        hipLaunchKernelGGL(k_dcollect, dim3((unsigned)((ncand + DC_CH - 1) / DC_CH), (unsigned)Tq,
+                                             (unsigned)B),
+                           dim3(DC_NT), 0, st, w, Tq, m, W, k, q_pos0, stride);
     }
     const size_t lds = sizeof(DselSmem);
-    hipFuncSetAttribute((const void*)k_dselect, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k_dselect, dim3((unsigned)Tq, (unsigned)B), dim3(DL_NT), lds, st, scores,
-                       ghist, topk, Tq, m, W, k, q_pos0, ncap);
+    hipFuncSetAttribute((const void*)k_dfinal, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(k_dfinal, dim3((unsigned)Tq, (unsigned)B), dim3(DL_NT), lds, st, w, topk, Tq,
+                       m, W, k, q_pos0, stride);
     return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@
 
 namespace csa {
 
-constexpr int ST_NT = 256;
+constexpr int ST_NT = 512;            // 8 waves: one per query row at the decisions
 constexpr int ST_QT = 8;               // query rows per block
 constexpr int ST_CAP = 256;            // collected keys per query
 constexpr int ST_MAXW = 1024;          // bitmap words per query -> 32768 candidates
@@ -149,18 +149,29 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         if (!S.any_active) break;
         (void)any;
 
-        for (int tile = wave; tile < ntiles; tile += ST_NT / WAVE) {
-            const int j = tile * 32 + row;
-            i32x8 bop = {0, 0, 0, 0, 0, 0, 0, 0};
-            int sbk = 127;
+        constexpr int NWV = ST_NT / WAVE;
+        constexpr int UNR = 8;                       // key tiles in flight per wave
+        for (int t0 = wave * UNR; t0 < ntiles; t0 += NWV * UNR) {
+          u32x4 kw[UNR];
+          int ksv[UNR];
+#pragma unroll
+          for (int x = 0; x < UNR; ++x) {
+            const int j = (t0 + x) * 32 + row;
+            kw[x] = u32x4{0u, 0u, 0u, 0u};
+            ksv[x] = 127;
             if (j < nc_max && kb < kscales) {
-                u32x4 w = *reinterpret_cast<const u32x4*>(kcb + (int64_t)j * kbytes + kb * 16);
-                bop[0] = (int)w[0]; bop[1] = (int)w[1]; bop[2] = (int)w[2]; bop[3] = (int)w[3];
-                sbk = ksb[(int64_t)j * kscales + kb];
+                kw[x] = *reinterpret_cast<const u32x4*>(kcb + (int64_t)j * kbytes + kb * 16);
+                ksv[x] = ksb[(int64_t)j * kscales + kb];
             }
+          }
+#pragma unroll
+          for (int x = 0; x < UNR; ++x) {
+            const int j = (t0 + x) * 32 + row;
+            if ((t0 + x) * 32 >= nc_max) break;
+            i32x8 bop = {(int)kw[x][0], (int)kw[x][1], (int)kw[x][2], (int)kw[x][3], 0, 0, 0, 0};
             f32x16 acc = {};
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc, 4, 4, 0, sa, 0,
-                                                                   sbk);
+                                                                   ksv[x]);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (md[u] == M_DONE || j >= ncq[u]) continue;
@@ -190,10 +201,11 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
                     }
                 }
             }
+          }
         }
         __syncthreads();
 
-        // ---- per-query decisions: wave w handles queries w and w + 4
+        // ---- per-query decisions: wave w handles query w
         for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
             const int mode = S.mode[q];
             if (mode == M_HIST1 || mode == M_HIST) {
@@ -257,7 +269,7 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         __syncthreads();
     }
 
-    // ---- read out: wave w writes queries w and w + 4
+    // ---- read out: wave w writes query w
     for (int q = wave; q < qv; q += ST_NT / WAVE) {
         const int nc = (int)n_candidates(q_pos0 + q0 + q, m, W);
         wave_emit_bitmap(&S.sel[q][0], (nc + 31) / 32, topk + (b * Tq + q0 + q) * k, k);

@@ -187,4 +187,74 @@ __device__ __forceinline__ void wave_emit_bitmap(const uint32_t* sel, int nw, in
     for (int s = total + lane; s < k; s += WAVE) out[s] = -1;
 }
 
+// Block-wide versions of the two bitmap steps above, for long rows: every
+// thread owns a contiguous run of words; scratch holds NT/64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan_i(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+    const int inc = wave_incl_scan(v);
+    __syncthreads();
+    if (lane == WAVE - 1) scratch[w] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / WAVE; ++i) {
+        const int x = scratch[i];
+        base += i < w ? x : 0;
+        tot += x;
+    }
+    *total = tot;
+    return base + inc - v;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_merge_first_bits(uint32_t* sel, const uint32_t* eq, int nw,
+                                                       int need_eq, int* scratch) {
+    const int per = (nw + NT - 1) / NT;
+    const int w0 = threadIdx.x * per, w1 = min(nw, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(eq[w]);
+    int tot;
+    int before = block_excl_scan_i<NT>(cnt, scratch, &tot);
+    for (int w = w0; w < w1 && before < need_eq; ++w) {
+        uint32_t bits = eq[w];
+        int c = __popc(bits);
+        if (before + c > need_eq) {
+            const int keep = need_eq - before;
+            uint32_t kept = 0;
+            for (int i = 0; i < keep; ++i) {
+                const uint32_t low = bits & (0u - bits);
+                kept |= low;
+                bits ^= low;
+            }
+            bits = kept;
+            c = keep;
+        }
+        sel[w] |= bits;
+        before += c;
+    }
+    __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void block_emit_bitmap(const uint32_t* sel, int nw, int32_t* out, int k,
+                                                  int* scratch) {
+    const int per = (nw + NT - 1) / NT;
+    const int w0 = threadIdx.x * per, w1 = min(nw, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    int total;
+    int pos = block_excl_scan_i<NT>(cnt, scratch, &total);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t bits = sel[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            if (pos < k) out[pos] = w * 32 + b;
+            pos++;
+        }
+    }
+    for (int s = total + (int)threadIdx.x; s < k; s += NT) out[s] = -1;
+}
+
 }  // namespace csa
