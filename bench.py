@@ -41,6 +41,47 @@ sys.path.insert(0, ROOT)
 PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp4_TFLOPs": 10100.0}
 DEFAULT = "pair_prefill_128k"
 
+# Kernel sources behind each stage: the HBM traffic recorded in
+# profiles/traffic.json for a stage is reported only while the digest of
+# these sources (comments and blank space removed) still matches.
+_IDX = ["indexer.hip", "index_stream.hip", "index_decode.hip", "wave_select.h", "select.h",
+        "mxfp4.h", "common.h", "internal.h"]
+STAGE_SOURCES = {
+    "index_topk": _IDX,
+    "csa_attend": ["attend.hip", "common.h", "internal.h"],
+    "hca_attend": ["attend.hip", "common.h", "internal.h"],
+    "compress_m4": ["compress.hip", "common.h", "internal.h"],
+    "compress_m128": ["compress.hip", "common.h", "internal.h"],
+    "quantize_keys": ["mxfp4.hip", "mxfp4.h", "common.h", "internal.h"],
+}
+
+
+def source_digest(files):
+    """sha1 over the kernel sources with comments and blank space removed."""
+    import hashlib
+    import re
+    h = hashlib.sha1()
+    for f in files:
+        text = open(os.path.join(ROOT, "compressed_sparse_attention_04_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(f.encode())
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, stage):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE passes kept
+    in profiles/traffic.json, or None if absent or the kernel changed since."""
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        e = rec["entries"][f"{workload}/{stage}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("bytes") is None or e.get("digest") != source_digest(STAGE_SOURCES[stage]):
+        return None
+    return e["bytes"]
+
 
 def n_cand(t, m, W):
     """Vectorised candidate count (same rule as the library)."""
@@ -295,12 +336,25 @@ def main():
                     choices=["pair_prefill_128k", "csa_prefill_32k", "hca_decode_1m",
                              "csa_decode_1m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard); run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the path has no multi-GPU mode (sequences or "
+              "query ranges would shard across GPUs); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -374,7 +428,7 @@ def main():
         roof = {"bound": "mfma", "achieved": d.flops / sec / 1e12, "peak": PEAK[d.peak_key],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(args.workload, d.name)
     roof["kernel"] = d.name
     roof["ms_per_launch"] = stage_ms[dom]
 

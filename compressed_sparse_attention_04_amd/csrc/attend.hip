@@ -5,21 +5,20 @@
 // studioglobal.ai answer: the 128-token window branch is always present).
 //
 // For the query at position t the key list is
-//   [ selected (CSA) or all (HCA) compressed candidates | raw tokens w0..t ]
+//   [ kept (CSA) or all (HCA) compressed candidates | raw tokens w0..t ]
 // and one softmax runs over it.  All H query heads share the one K/V head,
-// so the H heads are the M dimension of the bf16 MFMAs and every K/V row is
+// so the H heads are a dimension of the bf16 MFMAs and every K/V row is
 // fetched once per query token for all heads.
 //
 // bf16 kernel, per block: one query token (all H = 32 * NW heads, one wave
-// per 32 heads) and one split of its key list, in tiles of 64 keys whose
-// gathers for tile n+1 are in flight while tile n is computed.  Per tile:
-//   S^T = K * Q^T      (V_MFMA_F32_32X32X16_BF16, K rows from LDS, Q^T held
-//                       in registers) -> every lane owns one head's column
-//   online softmax in fp32 (exp2 domain), rows = keys, so the running max
-//   and sum are per lane plus one cross-half exchange
-//   O^T += V^T * P^T   (P^T straight from the S^T registers as bf16; V^T
-//                       read from an LDS tile stored transposed, with its
-//                       key order permuted to match P^T's register order)
+// per 32 heads) and one split of its key list, in tiles of 32 keys that
+// never mix the two sources.  K and V rows are copied straight into LDS
+// (global_load_lds) three tiles ahead of use.  Per tile and wave:
+//   S^T = K Q^T          (8 x V_MFMA_F32_32X32X16_BF16, K rows from LDS,
+//                         Q^T in registers) -> each lane owns one head
+//   online softmax in fp32 (exp2 domain) with lazy rescaling
+//   O^T += V^T P^T       (P^T straight from the S^T registers as bf16; V^T
+//                         by transposing LDS reads, ds_read_b64_tr_b16)
 // With more than one split the unnormalised (acc, max, sum) go to the
 // workspace and k_attend_combine merges them (log-sum-exp).
 #include "common.h"
