@@ -50,6 +50,10 @@ template <> struct Elem<float> {
         *reinterpret_cast<f32x4*>(p) = a;
         *reinterpret_cast<f32x4*>(p + 4) = b;
     }
+    __device__ static __forceinline__ void load4(const float* p, float (&v)[4]) {
+        f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    }
     __device__ static __forceinline__ float load1(const float* p) { return *p; }
 };
 template <> struct Elem<uint16_t> {
@@ -67,6 +71,13 @@ template <> struct Elem<uint16_t> {
         for (int i = 0; i < 4; ++i)
             a[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
         *reinterpret_cast<u32x4*>(p) = a;
+    }
+    __device__ static __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+        u32x2 a = *reinterpret_cast<const u32x2*>(p);
+        v[0] = __uint_as_float(a[0] << 16);
+        v[1] = __uint_as_float(a[0] & 0xffff0000u);
+        v[2] = __uint_as_float(a[1] << 16);
+        v[3] = __uint_as_float(a[1] & 0xffff0000u);
     }
     __device__ static __forceinline__ float load1(const uint16_t* p) {
         return bf16_bits_to_f32(*p);

@@ -5,37 +5,137 @@
 //
 //   I(t, j) = sum_{h < HI} max(0, qhat[t][h] . khat[j])
 //
-// One block owns 8 query rows and streams all their candidates in tiles of
-// 32 keys.  Each pass recomputes the FP4 scores on the scaled MFMA (cheaper
-// than keeping 8 x 32K fp32 scores anywhere) and, per query, either adds
-// the keys of the current range to a 1024-bin histogram (narrowing the
-// threshold range) or collects: keys above the range go to a candidate
-// bitmap, keys inside it to a small buffer (or, for a single-valued range,
-// to an equality bitmap).  Typical data needs two passes.  Each wave then
-// finishes two queries: exact threshold over the buffer, first-by-index
-// resolution of ties, and read-out of the bitmap in ascending order.
+// One block owns 8 query rows and streams their candidates in tiles of 32
+// keys; every pass recomputes the FP4 scores on the scaled MFMA (cheaper
+// than keeping 8 x 32K fp32 scores anywhere).  Key order: fp32 bits of the
+// score, larger first, ties to the lower candidate index.
+//
+// Rows with enough candidates take the sampled path:
+//   1. a level-1 histogram (1/64-octave bins) of every 8th key tile;
+//   2. from the sample's rank statistics, a key range [lo, hi) that holds
+//      the k-th key with a margin of 3 sigma + 4 sample ranks each side;
+//   3. one pass over all keys: keys >= hi go to the kept bitmap, keys in
+//      [lo, hi) to the wave's own segment of a buffer (ballot compaction,
+//      no shared counter);
+//   4. if the counts prove that the k-th key lies in the buffer (kept < k
+//      <= kept + buffered, no overflow), an exact radix threshold over the
+//      buffer finishes the row.
+// Other rows, and any row whose check fails, run the exact multi-pass
+// search: histogram passes narrow the range of the k-th key until it holds
+// at most 256 keys (or one key value), then a collecting pass.  Either way
+// ties at the threshold are resolved by candidate order and the kept set is
+// read out of the bitmap in ascending order.
 #include "internal.h"
 #include "mxfp4.h"
 #include "wave_select.h"
 
 namespace csa {
 
-constexpr int ST_NT = 512;            // 8 waves: one per query row at the decisions
+constexpr int ST_NT = 512;             // 8 waves: one per query row at the decisions
 constexpr int ST_QT = 8;               // query rows per block
-constexpr int ST_CAP = 256;            // collected keys per query
-constexpr int ST_MAXW = 1024;          // bitmap words per query -> 32768 candidates
+constexpr int ST_CAP = 256;            // collected keys per row (multi-pass search)
+constexpr int ST_SEG = 96;             // buffered keys per row and wave (sampled path)
+constexpr int ST_BUF = ST_SEG * (ST_NT / WAVE);
+constexpr int ST_MAXW = 1024;          // bitmap words per row -> 32768 candidates
+constexpr int ST_SAMPLE = 8;           // one key tile in ST_SAMPLE is sampled
+constexpr int ST_SAMPLE_MIN = 2048;    // candidates a row needs for the sampled path
+// key tiles per wave and batch: 8, or 4 when HI < 4 (more query slots per
+// lane leave fewer registers)
+template <int HI> constexpr int st_unr() { return HI == 4 ? 8 : 4; }
 
-enum : int { M_DONE = 0, M_HIST1 = 1, M_HIST = 2, M_COLLECT = 3 };
+enum : int { M_DONE = 0, M_HIST1 = 1, M_HIST = 2, M_COLLECT = 3, M_SAMPLED = 4 };
 
 struct StreamSmem {
-    uint32_t hist[ST_QT][SEL_NB];
-    u32x2 cb[ST_QT][ST_CAP];
-    uint32_t sel[ST_QT][ST_MAXW];
-    uint32_t eq[ST_QT][ST_MAXW];
+    uint32_t sel[ST_QT][ST_MAXW];      // kept candidates
+    uint32_t hist[ST_QT][SEL_NB];      // histograms; radix scratch
+    uint32_t eq[ST_QT][ST_MAXW];       // candidates equal to the threshold key
+    u32x2 buf[ST_QT][ST_BUF];          // (key, index): one segment per wave (sampled
+                                       // path); the first ST_CAP: multi-pass buffer
+    int segcnt[ST_QT][ST_NT / WAVE];
+    u32x4 aq[64];                      // MFMA A operand of lane kb*32 + row
+    uint32_t as[64];                   // and its scale byte
     uint32_t lo[ST_QT], hi[ST_QT];
     int shift[ST_QT], mode[ST_QT], above[ST_QT], need[ST_QT], cnt[ST_QT], eqmode[ST_QT];
-    int any_active;
+    int nc[ST_QT];
+    int any_active, any_sampled;
 };
+
+// One wave's batches of UNR key tiles: virtual tiles v = 0..nv-1 map to
+// key tiles v * stride; the wave takes batches wave, wave + NWV, ...  The
+// next batch's key loads are in flight while the current one is processed.
+struct TileSrc {
+    const uint8_t* kcb;
+    const uint8_t* ksb;
+    int kbytes, kscales, nc_max, row, kb;
+};
+
+// Loads are unconditional (rows clamped to the last candidate; lanes past
+// dI read a valid offset and get the neutral scale 2^0 against a zero A
+// operand), so the compiler can count them: the current batch is waited
+// for while the next one stays in flight.
+template <int UNR>
+__device__ __forceinline__ void load_batch(const TileSrc& ts, int v0, int stride,
+                                           u32x4 (&kw)[UNR], int (&ksv)[UNR]) {
+    const int koff = min(ts.kb * 16, ts.kbytes - 16);
+    const int soff = min(ts.kb, ts.kscales - 1);
+#pragma unroll
+    for (int x = 0; x < UNR; ++x) {
+        const int j = min((v0 + x) * stride * 32 + ts.row, ts.nc_max - 1);
+        kw[x] = *reinterpret_cast<const u32x4*>(ts.kcb + (int64_t)j * ts.kbytes + koff);
+        const int sc = ts.ksb[(int64_t)j * ts.kscales + soff];
+        ksv[x] = ts.kb < ts.kscales ? sc : 127;
+    }
+}
+
+// f(acc, j0): MFMA scores of the tile whose first key is j0 (this lane's
+// key is j0 + row for its S rows; see the callers)
+template <int UNR, typename F>
+__device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stride,
+                                             const i32x8& aop, int sa, F&& f) {
+    constexpr int NWV = ST_NT / WAVE;
+    const int wave = threadIdx.x / WAVE;
+    u32x4 kwA[UNR], kwB[UNR];
+    int ksA[UNR], ksB[UNR];
+    auto run = [&](const u32x4 (&kw)[UNR], const int (&ksv)[UNR], int v0) {
+#pragma unroll
+        for (int x = 0; x < UNR; ++x) {
+            if (v0 + x >= nv) break;
+            const i32x8 bop = {(int)kw[x][0], (int)kw[x][1], (int)kw[x][2], (int)kw[x][3],
+                               0, 0, 0, 0};
+            f32x16 acc = {};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc, 4, 4, 0, sa, 0,
+                                                                   ksv[x]);
+            f(acc, (v0 + x) * stride * 32);
+            // one tile's scores live at a time (no hoisting of later MFMAs)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int v0 = wave * UNR;
+    if (v0 >= nv) return;
+    load_batch<UNR>(ts, v0, stride, kwA, ksA);
+    while (true) {
+        load_batch<UNR>(ts, v0 + NWV * UNR, stride, kwB, ksB);
+        run(kwA, ksA, v0);
+        v0 += NWV * UNR;
+        if (v0 >= nv) break;
+        load_batch<UNR>(ts, v0 + NWV * UNR, stride, kwA, ksA);
+        run(kwB, ksB, v0);
+        v0 += NWV * UNR;
+        if (v0 >= nv) break;
+    }
+}
+
+// ReLU head sum of slot u of an MFMA tile as an order key.  ReLU is the
+// signed-integer max of the bit pattern with 0 (negative floats, -0
+// included, have negative patterns), so the sum of non-negative terms is
+// never -0.  The MFMA outputs are finite (products of FP4 values).
+template <int HI>
+__device__ __forceinline__ uint32_t score_key(const f32x16& acc, int u) {
+    float s = __int_as_float(max(__float_as_int(acc[u * HI]), 0));
+#pragma unroll
+    for (int hh = 1; hh < HI; ++hh) s += __int_as_float(max(__float_as_int(acc[u * HI + hh]), 0));
+    return __float_as_uint(s);
+}
 
 template <typename T, int HI>
 __global__ void __launch_bounds__(ST_NT)
@@ -56,8 +156,10 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
 
     // ---- per-query setup
     if (tid < ST_QT) {
-        int nc = tid < qv ? (int)n_candidates(q_pos0 + q0 + tid, m, W) : 0;
-        int need = min(nc, k);
+        const int nc = tid < qv ? (int)n_candidates(q_pos0 + q0 + tid, m, W) : 0;
+        for (int w = 0; w < ST_NT / WAVE; ++w) S.segcnt[tid][w] = 0;
+        const int need = min(nc, k);
+        S.nc[tid] = nc;
         S.need[tid] = need;
         S.above[tid] = 0;
         S.cnt[tid] = 0;
@@ -66,16 +168,42 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         S.hi[tid] = KEY_END;
         S.shift[tid] = 0;
         // all candidates kept when there are at most k of them
-        S.mode[tid] = (need == 0 || nc <= k) ? M_DONE : M_HIST1;
+        S.mode[tid] = (need == 0 || nc <= k) ? M_DONE
+                      : nc >= ST_SAMPLE_MIN ? M_SAMPLED : M_HIST1;
     }
-    for (int i = tid; i < ST_QT * ST_MAXW; i += ST_NT) {
-        const int q = i / ST_MAXW, w = i % ST_MAXW;
-        if (w < nw) {
-            int nc = q < qv ? (int)n_candidates(q_pos0 + q0 + q, m, W) : 0;
+    // ---- MXFP4 of the query rows, once per block: 8 threads per 32-value
+    // block (lane kb*32 + row of the MFMA A operand: query row / HI, head
+    // row % HI, dims kb*32..), 4 values each, staged in LDS
+    static_assert(ST_NT == 64 * 8, "one 32-value block per 8 threads");
+    {
+        const int bl = tid >> 3, part = tid & 7;
+        const int brow = bl & 31, bkb = bl >> 5;
+        const int qi = brow / HI, h = brow % HI;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (qi < qv && bkb * 32 < dI)
+            Elem<T>::load4(q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + bkb * 32 + part * 4), v);
+        uint32_t amax = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7fffffffu);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, WAVE));
+        const int e = mxfp4_exponent(amax);
+        const float p2e = pow2_neg(e);
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c |= mxfp4_code(v[i], p2e) << (4 * i);
+        const uint32_t c2 = (uint32_t)__shfl_xor((int)c, 1, WAVE);
+        if (!(part & 1)) S.aq[bl][part >> 1] = c | (c2 << 16);
+        if (part == 0) S.as[bl] = (uint32_t)(e + 127);
+    }
+    __syncthreads();
+    for (int q = 0; q < ST_QT; ++q) {
+        const int nc = S.nc[q];
+        for (int w = tid; w < nw; w += ST_NT) {
             // queries with nc <= k keep every candidate
             uint32_t full = 0u;
             if (nc <= k) {
-                int lo_b = w * 32;
+                const int lo_b = w * 32;
                 full = lo_b + 32 <= nc ? 0xFFFFFFFFu
                                        : (lo_b >= nc ? 0u : ((1u << (nc - lo_b)) - 1u));
             }
@@ -83,28 +211,9 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
             S.eq[q][w] = 0u;
         }
     }
-
-    // ---- A operand: MXFP4 of query rows (row / HI, row % HI)
-    i32x8 aop = {0, 0, 0, 0, 0, 0, 0, 0};
-    int sa = 127;
-    {
-        const int qi = row / HI, h = row % HI;
-        if (qi < qv && kb * 32 < dI) {
-            const T* src = q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + kb * 32);
-            float v[32];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float t8[8];
-                Elem<T>::load8(src + p * 8, t8);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[p * 8 + i] = t8[i];
-            }
-            uint32_t pk[4], sb;
-            mxfp4_encode32(v, pk, sb);
-            aop[0] = (int)pk[0]; aop[1] = (int)pk[1]; aop[2] = (int)pk[2]; aop[3] = (int)pk[3];
-            sa = (int)sb;
-        }
-    }
+    const u32x4 aw = S.aq[kb * 32 + row];
+    const i32x8 aop = {(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3], 0, 0, 0, 0};
+    const int sa = (int)S.as[kb * 32 + row];
     // the queries this lane's MFMA output rows belong to
     const int kbq = kb * 4 / HI;
     int qslot[NU];
@@ -114,22 +223,163 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         const int g = (u * HI) / 4, i = (u * HI) % 4;
         const int qi = (8 * g + i) / HI + kbq;
         qslot[u] = qi;
-        ncq[u] = (qi < qv) ? (int)n_candidates(q_pos0 + q0 + qi, m, W) : 0;
+        ncq[u] = (qi < qv) ? S.nc[qi] : 0;
     }
     __syncthreads();
 
-    const int kbytes = dI / 2, kscales = dI / 32;
     const int ntiles = (nc_max + 31) / 32;
-    const uint8_t* kcb = kc + b * Nc * kbytes;
-    const uint8_t* ksb = ks + b * Nc * kscales;
+    const TileSrc ts{kc + b * Nc * (dI / 2), ks + b * Nc * (dI / 32), dI / 2, dI / 32, nc_max,
+                     row, kb};
 
+    // ================= sampled path
+    if (tid == 0) {
+        int a = 0;
+        for (int q = 0; q < ST_QT; ++q) a |= S.mode[q] == M_SAMPLED;
+        S.any_sampled = a;
+    }
+    for (int i = tid; i < ST_QT * SEL_NB; i += ST_NT) (&S.hist[0][0])[i] = 0u;
+    __syncthreads();
+    if (S.any_sampled) {
+        bool act[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) act[u] = qslot[u] < qv && S.mode[qslot[u]] == M_SAMPLED;
+        // 1. level-1 histogram of the sampled tiles
+        stream_tiles<st_unr<HI>()>(ts, (ntiles + ST_SAMPLE - 1) / ST_SAMPLE, ST_SAMPLE, aop, sa,
+                     [&](const f32x16& acc, int j0) {
+            const int j = j0 + row;
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                if (act[u] && j < ncq[u])
+                    atomicAdd(&S.hist[qslot[u]][lvl1_bin(score_key<HI>(acc, u))], 1u);
+        });
+        __syncthreads();
+        // 2. key range of the k-th key, per sampled row (wave q)
+        for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
+            if (S.mode[q] != M_SAMPLED) continue;
+            const int nc = S.nc[q], need = S.need[q];
+            const int ns = (nc / (32 * ST_SAMPLE)) * 32 + min(32, nc % (32 * ST_SAMPLE));
+            const float f = (float)ns / (float)nc;
+            const float rt = (float)need * f;
+            const float margin = 3.f * sqrtf(rt * (1.f - f)) + 4.f;
+            const int need_hi = (int)floorf(rt - margin);
+            const int need_lo = (int)ceilf(rt + margin);
+            uint32_t khi = KEY_END, klo = 0u;
+            int gt, in;
+            if (need_hi >= 1) {
+                const int d = wave_hist_find(&S.hist[q][0], need_hi, &gt, &in);
+                uint32_t l0, h0;
+                lvl1_range(d, &l0, &h0);
+                khi = h0;
+            }
+            if (need_lo <= ns) {
+                const int d = wave_hist_find(&S.hist[q][0], need_lo, &gt, &in);
+                uint32_t l0, h0;
+                lvl1_range(d, &l0, &h0);
+                klo = l0;
+            }
+            if (lane == 0) {
+                S.lo[q] = klo;
+                S.hi[q] = khi;
+                S.cnt[q] = 0;
+            }
+        }
+        __syncthreads();
+        // 3. one pass over every key
+        uint32_t lo[NU], hi[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int q = qslot[u] < ST_QT ? qslot[u] : 0;
+            lo[u] = S.lo[q];
+            hi[u] = S.hi[q];
+        }
+        int wc0[NU], wc1[NU];           // this wave's segment counts, half-waves 0 / 1
+#pragma unroll
+        for (int u = 0; u < NU; ++u) wc0[u] = wc1[u] = 0;
+        stream_tiles<st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+            const int j = j0 + row;
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const bool ok = act[u] && j < ncq[u];
+                const uint32_t key = score_key<HI>(acc, u);
+                const bool above = ok && key >= hi[u];
+                const bool in = ok && !above && key >= lo[u];
+                const int q = qslot[u] < ST_QT ? qslot[u] : 0;
+                if (above) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
+                const uint64_t bin = __ballot(in);
+                if (bin != 0ull) {
+                    const uint32_t h0 = (uint32_t)bin, h1 = (uint32_t)(bin >> 32);
+                    if (in) {
+                        const uint32_t mine = kb ? h1 : h0;
+                        const int pos = (kb ? wc1[u] : wc0[u]) +
+                                        __popc(mine & ((1u << row) - 1u));
+                        if (pos < ST_SEG)
+                            S.buf[q][wave * ST_SEG + pos] = u32x2{key, (uint32_t)j};
+                    }
+                    wc0[u] += __popc(h0);
+                    wc1[u] += __popc(h1);
+                }
+            }
+        });
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+            if (row == 0 && act[u]) S.segcnt[qslot[u]][wave] = kb ? wc1[u] : wc0[u];
+        __syncthreads();
+        // 4. check the counts and finish the row, or hand it to the search
+        for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
+            if (S.mode[q] != M_SAMPLED) continue;
+            const int qnw = (S.nc[q] + 31) / 32;
+            int c = 0;
+            for (int w = lane; w < qnw; w += WAVE) c += __popc(S.sel[q][w]);
+            const int kept = wave_sum(c);
+            int nin = 0, over = 0;
+            for (int w = 0; w < ST_NT / WAVE; ++w) {
+                nin += S.segcnt[q][w];
+                over |= S.segcnt[q][w] > ST_SEG;
+            }
+            const int need = S.need[q];
+            if (kept < need && kept + nin >= need && !over) {
+                constexpr int EPT = ST_BUF / WAVE;
+                uint32_t key[EPT];
+                bool valid[EPT];
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    const int p = lane * EPT + e;
+                    valid[e] = p % ST_SEG < S.segcnt[q][p / ST_SEG];
+                    key[e] = valid[e] ? S.buf[q][p][0] : 0u;
+                }
+                uint32_t thr;
+                int need_eq;
+                wave_radix_threshold<EPT>(key, valid, need - kept, &S.hist[q][0], &thr, &need_eq);
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    if (!valid[e]) continue;
+                    const uint32_t j = S.buf[q][lane * EPT + e][1];
+                    if (key[e] > thr) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
+                    else if (key[e] == thr) atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
+                }
+                __builtin_amdgcn_wave_barrier();
+                wave_merge_first_bits(&S.sel[q][0], &S.eq[q][0], qnw, need_eq);
+                if (lane == 0) S.mode[q] = M_DONE;
+            } else {
+                for (int w = lane; w < qnw; w += WAVE) S.sel[q][w] = 0u;
+                if (lane == 0) {
+                    S.mode[q] = M_HIST1;
+                    S.lo[q] = 0u;
+                    S.hi[q] = KEY_END;
+                    S.cnt[q] = 0;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ================= exact multi-pass search for the remaining rows
 #pragma unroll 1
     for (int pass = 0; pass < 8; ++pass) {
         // per-slot state of this pass (registers)
         int md[NU], sh[NU];
         uint32_t lo[NU], hi[NU];
         bool eqm[NU];
-        bool any = false;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int q = qslot[u] < ST_QT ? qslot[u] : 0;
@@ -147,38 +397,13 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         for (int i = tid; i < ST_QT * SEL_NB; i += ST_NT) (&S.hist[0][0])[i] = 0u;
         __syncthreads();
         if (!S.any_active) break;
-        (void)any;
 
-        constexpr int NWV = ST_NT / WAVE;
-        constexpr int UNR = 8;                       // key tiles in flight per wave
-        for (int t0 = wave * UNR; t0 < ntiles; t0 += NWV * UNR) {
-          u32x4 kw[UNR];
-          int ksv[UNR];
-#pragma unroll
-          for (int x = 0; x < UNR; ++x) {
-            const int j = (t0 + x) * 32 + row;
-            kw[x] = u32x4{0u, 0u, 0u, 0u};
-            ksv[x] = 127;
-            if (j < nc_max && kb < kscales) {
-                kw[x] = *reinterpret_cast<const u32x4*>(kcb + (int64_t)j * kbytes + kb * 16);
-                ksv[x] = ksb[(int64_t)j * kscales + kb];
-            }
-          }
-#pragma unroll
-          for (int x = 0; x < UNR; ++x) {
-            const int j = (t0 + x) * 32 + row;
-            if ((t0 + x) * 32 >= nc_max) break;
-            i32x8 bop = {(int)kw[x][0], (int)kw[x][1], (int)kw[x][2], (int)kw[x][3], 0, 0, 0, 0};
-            f32x16 acc = {};
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc, 4, 4, 0, sa, 0,
-                                                                   ksv[x]);
+        stream_tiles<st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+            const int j = j0 + row;
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (md[u] == M_DONE || j >= ncq[u]) continue;
-                float s = 0.f;
-#pragma unroll
-                for (int hh = 0; hh < HI; ++hh) s += fmaxf(acc[u * HI + hh], 0.f);
-                const uint32_t key = s == 0.f ? 0u : __float_as_uint(s);
+                const uint32_t key = score_key<HI>(acc, u);
                 const int q = qslot[u];
                 if (md[u] == M_HIST1) {
                     atomicAdd(&S.hist[q][lvl1_bin(key)], 1u);
@@ -193,16 +418,12 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
                             atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
                         } else {
                             int pos = atomicAdd(&S.cnt[q], 1);
-                            if (pos < ST_CAP) {
-                                u32x2 e = {key, (uint32_t)j};
-                                S.cb[q][pos] = e;
-                            }
+                            if (pos < ST_CAP) S.buf[q][pos] = u32x2{key, (uint32_t)j};
                         }
                     }
                 }
             }
-          }
-        }
+        });
         __syncthreads();
 
         // ---- per-query decisions: wave w handles query w
@@ -249,14 +470,14 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
                     for (int e = 0; e < EPT; ++e) {
                         const int p = lane * EPT + e;
                         valid[e] = p < n;
-                        key[e] = valid[e] ? S.cb[q][p][0] : 0u;
+                        key[e] = valid[e] ? S.buf[q][p][0] : 0u;
                     }
                     uint32_t thr;
                     wave_radix_threshold<EPT>(key, valid, need_in, &S.hist[q][0], &thr, &need_eq);
 #pragma unroll
                     for (int e = 0; e < EPT; ++e) {
                         if (!valid[e]) continue;
-                        const uint32_t j = S.cb[q][lane * EPT + e][1];
+                        const uint32_t j = S.buf[q][lane * EPT + e][1];
                         if (key[e] > thr) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
                         else if (key[e] == thr) atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
                     }
@@ -271,7 +492,7 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
 
     // ---- read out: wave w writes query w
     for (int q = wave; q < qv; q += ST_NT / WAVE) {
-        const int nc = (int)n_candidates(q_pos0 + q0 + q, m, W);
+        const int nc = S.nc[q];
         wave_emit_bitmap(&S.sel[q][0], (nc + 31) / 32, topk + (b * Tq + q0 + q) * k, k);
     }
 }

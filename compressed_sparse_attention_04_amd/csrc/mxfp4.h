@@ -6,37 +6,30 @@
 // Scale exponent e = floor(log2 max|x|) - 2, clamped to [-127, 127]
 // (-127 for an all-zero run).  Element code: nearest of the e2m1 magnitudes
 // {0, .5, 1, 1.5, 2, 3, 4, 6} to |x| * 2^-e, ties to the even code,
-// saturating at 6; bit 3 = sign bit of x.  The comparison runs in fp64 on a
-// value rebuilt from the fp32 bit fields, so it is exact for every finite
-// input including fp32 subnormals.
+// saturating at 6; bit 3 = sign bit of x.  |x| * 2^-e is formed in fp32:
+// 2^-e is a normal fp32 for every e the rule produces (-127 <= e <= 125),
+// so the product is exact whenever it is >= 2^-126, and a smaller product
+// (possible only for elements far below the block maximum) has code 0
+// however it rounds.  The thresholds are exact fp32 constants.
 #pragma once
 #include "common.h"
 
 namespace csa {
 
-__device__ __forceinline__ double pow2_f64(int k) {
-    return __longlong_as_double((long long)(k + 1023) << 52);
+// e2m1 code of y = |x| * 2^-e (0 <= y < 8); a tie goes to the even code
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+    return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+           (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+           (uint32_t)(y > 5.0f);
 }
 
-// |x| * 2^-e for a non-negative fp32 bit pattern a, exactly, in fp64
-__device__ __forceinline__ double scaled_mag(uint32_t a, int e) {
-    uint32_t ef = a >> 23, mant = a & 0x7fffffu;
-    if (ef == 0) return (double)mant * pow2_f64(-149 - e);
-    return (double)(mant | 0x800000u) * pow2_f64((int)ef - 150 - e);
-}
+// 2^-e as fp32 (normal for -127 <= e <= 126)
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
-__device__ __forceinline__ uint32_t e2m1_code(double y) {
-    // boundaries between neighbouring magnitudes; equality goes to the even code
-    uint32_t c;
-    if (y <= 0.25) c = 0;
-    else if (y < 0.75) c = 1;
-    else if (y <= 1.25) c = 2;
-    else if (y < 1.75) c = 3;
-    else if (y <= 2.5) c = 4;
-    else if (y < 3.5) c = 5;
-    else if (y <= 5.0) c = 6;
-    else c = 7;
-    return c;
+// sign | code of one value under scale exponent e
+__device__ __forceinline__ uint32_t mxfp4_code(float x, float p2e) {
+    const uint32_t bits = __float_as_uint(x);
+    return e2m1_code(__uint_as_float(bits & 0x7fffffffu) * p2e) | ((bits >> 28) & 8u);
 }
 
 __device__ __forceinline__ int mxfp4_exponent(uint32_t amax_bits) {
@@ -61,12 +54,9 @@ __device__ __forceinline__ void mxfp4_encode32(const float (&v)[32], uint32_t (&
     scale_byte = (uint32_t)(e + 127);
 #pragma unroll
     for (int w = 0; w < 4; ++w) packed[w] = 0;
+    const float p2e = pow2_neg(e);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        uint32_t bits = __float_as_uint(v[i]);
-        uint32_t code = e2m1_code(scaled_mag(bits & 0x7fffffffu, e)) | ((bits >> 28) & 8u);
-        packed[i / 8] |= code << (4 * (i % 8));
-    }
+    for (int i = 0; i < 32; ++i) packed[i / 8] |= mxfp4_code(v[i], p2e) << (4 * (i % 8));
 }
 
 }  // namespace csa

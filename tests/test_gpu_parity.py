@@ -143,6 +143,30 @@ def test_index_tie_storm_keeps_lowest(T, q_pos0, Tq):
         assert g[0, i].tolist() == list(range(512))
 
 
+@pytest.mark.parametrize("T,q_pos0,Tq,shrink", [(40000, 39990, 10, True), (40000, 39990, 10, False),
+                                                (20000, 19000, 16, True)])
+def test_index_unrepresentative_sample(T, q_pos0, Tq, shrink):
+    """Keys of every 8th tile of 32 (j % 256 < 32) scaled by 1/64 (or 64):
+    a range estimated from those tiles alone misses the k-th key, so the
+    exact search must take over and still give the oracle's set."""
+    say("index skewed sample", T, q_pos0, Tq, shrink)
+    w = I.Workload("t", "csa", seed=25, dtype="bf16", B=1, T=T, m=4, H=128, D=128)
+    w = w.replace(Tq=Tq, q_pos0=q_pos0)
+    k_idx = I.draw_indexer_keys(w)
+    j = torch.arange(k_idx.shape[1])
+    f = 1.0 / 64 if shrink else 64.0
+    k_idx[:, (j % 256) < 32] = (k_idx[:, (j % 256) < 32].float() * f).to(k_idx.dtype)
+    q_idx = I.draw_indexer_queries(w)
+    kc, ks = oracle.quant_mxfp4(f64(k_idx))
+    q_pos = np.arange(q_pos0, q_pos0 + Tq)
+    ref, exact = oracle.index_topk(f64(q_idx), kc, ks, q_pos, w.m, w.W, w.k)
+    assert exact
+    gkc, gks = csa.csa_quantize_mxfp4(k_idx.to(DEV))
+    got = csa.csa_index_topk(q_idx.to(DEV), gkc, gks, m=w.m, W=w.W, k=w.k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
 def test_index_one_head_small_k():
     say("index HI=1")
     w = I.Workload("t", "csa", seed=24, dtype="f32", B=2, T=6000, m=4, H=8, D=64, HI=1, dI=64,
