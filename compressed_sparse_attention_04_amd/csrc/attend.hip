@@ -119,85 +119,46 @@ __device__ __forceinline__ void issue_tile(int tau, int ct, int nval, int nwin, 
     }
 }
 
-// Running softmax state of one lane (one head, half of each key tile).
-template <int D>
+// Running softmax state of one lane: HG groups of 32 heads, one head per
+// group (column col), half of each key tile.
+template <int D, int HG>
 struct Online {
-    f32x16 acc[D / 32];
-    float m_run;          // reference maximum (raw score units)
-    float mb;             // -m_run * scale_log2, or 0 while m_run is -inf
-    float l_run;          // running sum of the bf16-rounded probabilities
+    f32x16 acc[HG][D / 32];
+    float m_run[HG], mb[HG], l_run[HG];
 };
 
-// One 32-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  K and V
-// are the tile's LDS copies; the first nvalid keys of the tile contribute.
-template <int D>
-__device__ __forceinline__ void tile_compute(Online<D>& S, const bf16x8 (&qop)[D / 16],
+// One 32-key tile for HG head groups: S^T = K Q^T, online softmax,
+// O^T += V^T P^T.  K and V are the tile's LDS copies; every operand read
+// from them feeds all HG groups.  The first nvalid keys contribute.
+template <int D, int HG>
+__device__ __forceinline__ void tile_compute(Online<D, HG>& S, const bf16x8 (&qop)[HG][D / 16],
                                              const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
                                              int nvalid, float scale_log2) {
     using G = TileGeom<D>;
     const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
     // S^T: rows = keys (8*(r/4) + 4*kb + r%4), column = head
-    f32x16 sacc = {};
+    // every K operand read is issued before the chain, so the LDS latency is
+    // paid once per tile, not once per MFMA pair
+    bf16x8 kop[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        kop[kk] = *reinterpret_cast<const CSA_LDS bf16x8*>(
+            K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sacc[HG];
+#pragma unroll
+    for (int h = 0; h < HG; ++h) sacc[h] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const CSA_LDS bf16x8*>(
-            K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], sacc, 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < HG; ++h)
+            sacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[h][kk], sacc[h], 0, 0, 0);
     }
-    if (nvalid < ATT_KT) {                         // wave-uniform
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (8 * (r / 4) + 4 * kb + (r % 4) >= nvalid) sacc[r] = -INFINITY;
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // Lazy rescaling: the reference maximum moves only when a score exceeds
-    // it by more than a factor 2^8 in probability, so p stays <= 256; sum
-    // and accumulators share the reference, so the quotient is unchanged.
-    // (tmax - m_run) is NaN while both are -inf: no move.
-    const bool grow = (tmax - S.m_run) * scale_log2 > 8.f;
-    if (__ballot(grow)) {
-        float alpha = 1.f;
-        if (grow) {
-            alpha = __builtin_amdgcn_exp2f((S.m_run - tmax) * scale_log2);   // 0 from -inf
-            S.m_run = tmax;
-            S.mb = -tmax * scale_log2;
-        }
-        S.l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S.acc[dt][r] *= alpha;
-    }
-    uint32_t pb[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, S.mb));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, S.mb));
-        pb[r / 2] = pack_bf16x2(p0, p1);
-    }
-    // the sum takes the same bf16 values the PV product takes
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float psum = S.l_run;
-#pragma unroll
-    for (int x = 0; x < 8; ++x)
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[x]), ones, psum,
-                                               false);
-    S.l_run = psum;
-    // O^T += V^T P^T.  k-step u covers keys 16u..16u+15; k-slot s of lane
-    // half kb is key 16u + 8*(s/4) + 4*kb + s%4 (the S^T register order).
-    // Each half of the V^T operand is one transposing LDS read: lane
-    // (16g + 4j + a) points at V[key 16u + 8h + 4kb + j][32dt + 16(g%2) + 4a].
+    // the V^T operands (independent of P) are read while the softmax runs
     const int g = lane >> 4, wj = (lane >> 2) & 3, wa = lane & 3;
+    bf16x8 vop[2][D / 32];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        bf16x8 pop;
-        {
-            u32x4 w = {pb[4 * u], pb[4 * u + 1], pb[4 * u + 2], pb[4 * u + 3]};
-            pop = *reinterpret_cast<bf16x8*>(&w);
-        }
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             const int d = 32 * dt + 16 * (g & 1) + 4 * wa;
@@ -207,9 +168,82 @@ __device__ __forceinline__ void tile_compute(Online<D>& S, const bf16x8 (&qop)[D
                 V + key0 * G::ROWB + slot_of<D>(key0, d / 8) * 16 + (d % 8) * 2));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
                 V + key1 * G::ROWB + slot_of<D>(key1, d / 8) * 16 + (d % 8) * 2));
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop, S.acc[dt], 0, 0, 0);
+            vop[u][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+    if (nvalid < ATT_KT) {                         // wave-uniform
+#pragma unroll
+        for (int h = 0; h < HG; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r / 4) + 4 * kb + (r % 4) >= nvalid) sacc[h][r] = -INFINITY;
+    }
+    // Lazy rescaling: the reference maximum moves only when a score exceeds
+    // it by more than a factor 2^8 in probability, so p stays <= 256; sum
+    // and accumulators share the reference, so the quotient is unchanged.
+    // (tmax - m_run) is NaN while both are -inf: no move.
+    float tmax[HG];
+    bool grow[HG], any = false;
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[h][r]);
+        tmax[h] = fmaxf(t, __shfl_xor(t, 32, 64));
+        grow[h] = (tmax[h] - S.m_run[h]) * scale_log2 > 8.f;
+        any |= grow[h];
+    }
+    if (__ballot(any)) {
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+            float alpha = 1.f;
+            if (grow[h]) {
+                alpha = __builtin_amdgcn_exp2f((S.m_run[h] - tmax[h]) * scale_log2);   // 0 from -inf
+                S.m_run[h] = tmax[h];
+                S.mb[h] = -tmax[h] * scale_log2;
+            }
+            S.l_run[h] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S.acc[h][dt][r] *= alpha;
+        }
+    }
+    uint32_t pb[HG][8];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[h][r], scale_log2, S.mb[h]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[h][r + 1], scale_log2, S.mb[h]));
+            pb[h][r / 2] = pack_bf16x2(p0, p1);
+        }
+        // the sum takes the same bf16 values the PV product takes
+        float psum = S.l_run[h];
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[h][x]), ones,
+                                                   psum, false);
+        S.l_run[h] = psum;
+    }
+    // O^T += V^T P^T.  k-step u covers keys 16u..16u+15; k-slot s of lane
+    // half kb is key 16u + 8*(s/4) + 4*kb + s%4 (the S^T register order).
+    // Each half of the V^T operand is one transposing LDS read: lane
+    // (16g + 4j + a) points at V[key 16u + 8h + 4kb + j][32dt + 16(g%2) + 4a].
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        bf16x8 pop[HG];
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+            u32x4 w = {pb[h][4 * u], pb[h][4 * u + 1], pb[h][4 * u + 2], pb[h][4 * u + 3]};
+            pop[h] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int h = 0; h < HG; ++h)
+                S.acc[h][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[h],
+                                                                       S.acc[h][dt], 0, 0, 0);
     }
 }
 
@@ -226,8 +260,8 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int NW, int D>
-__global__ void __launch_bounds__(NW * 64, 2)
+template <int NW, int D, int HG>
+__global__ void __launch_bounds__(NW * 64, HG == 1 ? 2 : 1)
 k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
               const uint16_t* __restrict__ cv, const int32_t* __restrict__ topk,
               const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
@@ -236,7 +270,7 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
               int64_t raw_len, int splits) {
     using G = TileGeom<D>;
     constexpr int NT = NW * 64;
-    constexpr int H = NW * 32;
+    constexpr int H = NW * 32 * HG;
     constexpr int KT = G::KT;
     constexpr int PER = 2 * ((G::NINS + NW - 1) / NW);   // copies per wave per tile
     // the stages live in distinct arrays, so the compiler can tell which
@@ -302,23 +336,24 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     const char* rkb = reinterpret_cast<const char*>(rk + b * raw_len * D);
     const char* rvb = reinterpret_cast<const char*>(rv + b * raw_len * D);
 
-    // Q^T operand: head hq, d = 16*kk + 8*kb + 0..7
-    const int hq = wave * 32 + col;
-    bf16x8 qop[D / 16];
-    {
+    // Q^T operand of group h: head (wave * HG + h) * 32 + col, d = 16*kk + 8*kb + 0..7
+    bf16x8 qop[HG][D / 16];
+    Online<D, HG> S;
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+        const int hq = (wave * HG + h) * 32 + col;
         const uint16_t* qp = q + ((b * Tq + i) * H + hq) * D + 8 * kb;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-            qop[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+            qop[h][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S.acc[h][dt][r] = 0.f;
+        S.m_run[h] = -INFINITY;
+        S.mb[h] = 0.f;
+        S.l_run[h] = 0.f;
     }
-    Online<D> S;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S.acc[dt][r] = 0.f;
-    S.m_run = -INFINITY;
-    S.mb = 0.f;
-    S.l_run = 0.f;
 
     auto issue = [&](int tau, uint8_t* sk, uint8_t* sv) {
         if (tau < tau1)
@@ -335,7 +370,7 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         lds_barrier();
         issue(tau + G::NST - 1, nk_, nv_);
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
-        tile_compute<D>(S, qop, (const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_,
+        tile_compute<D, HG>(S, qop, (const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_,
                         nvalid, scale_log2);
     };
 
@@ -351,36 +386,41 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         if (tau + 3 >= tau1) break;
         step(tau + 3, sK3, sV3, sK2, sV2);
     }
-    const float l_tot = S.l_run + __shfl_xor(S.l_run, 32, 64);
-    if (splits == 1) {
-        const float inv = 1.f / l_tot;
-        uint16_t* op = o + ((b * Tq + i) * H + hq) * D;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+    for (int h = 0; h < HG; ++h) {
+        const int hq = (wave * HG + h) * 32 + col;
+        const float l_tot = S.l_run[h] + __shfl_xor(S.l_run[h], 32, 64);
+        if (splits == 1) {
+            const float inv = 1.f / l_tot;
+            uint16_t* op = o + ((b * Tq + i) * H + hq) * D;
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int d = 32 * dt + 8 * gg + 4 * kb;
-                u32x2 w;
-                w[0] = pack_bf16x2(S.acc[dt][4 * gg] * inv, S.acc[dt][4 * gg + 1] * inv);
-                w[1] = pack_bf16x2(S.acc[dt][4 * gg + 2] * inv, S.acc[dt][4 * gg + 3] * inv);
-                *reinterpret_cast<u32x2*>(op + d) = w;
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int d = 32 * dt + 8 * gg + 4 * kb;
+                    u32x2 w;
+                    w[0] = pack_bf16x2(S.acc[h][dt][4 * gg] * inv, S.acc[h][dt][4 * gg + 1] * inv);
+                    w[1] = pack_bf16x2(S.acc[h][dt][4 * gg + 2] * inv,
+                                       S.acc[h][dt][4 * gg + 3] * inv);
+                    *reinterpret_cast<u32x2*>(op + d) = w;
+                }
+        } else {
+            // partial record per (query, split, head): D accumulators, max, sum;
+            // the max is stored in the exp2 domain of the combine kernel
+            float* pr = part + (((b * Tq + i) * splits + split) * H + hq) * (D + 2);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int d = 32 * dt + 8 * gg + 4 * kb;
+                    f32x4 w = {S.acc[h][dt][4 * gg], S.acc[h][dt][4 * gg + 1],
+                               S.acc[h][dt][4 * gg + 2], S.acc[h][dt][4 * gg + 3]};
+                    *reinterpret_cast<f32x4*>(pr + d) = w;
+                }
+            if (kb == 0) {
+                pr[D] = S.m_run[h] == -INFINITY ? -INFINITY : S.m_run[h] * scale_log2;
+                pr[D + 1] = l_tot;
             }
-    } else {
-        // partial record per (query, split, head): D accumulators, max, sum;
-        // the max is stored in the exp2 domain of the combine kernel
-        float* pr = part + (((b * Tq + i) * splits + split) * H + hq) * (D + 2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int d = 32 * dt + 8 * gg + 4 * kb;
-                f32x4 w = {S.acc[dt][4 * gg], S.acc[dt][4 * gg + 1], S.acc[dt][4 * gg + 2],
-                           S.acc[dt][4 * gg + 3]};
-                *reinterpret_cast<f32x4*>(pr + d) = w;
-            }
-        if (kb == 0) {
-            pr[D] = S.m_run == -INFINITY ? -INFINITY : S.m_run * scale_log2;
-            pr[D + 1] = l_tot;
         }
     }
 }
@@ -502,20 +542,21 @@ AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int6
     return p;
 }
 
-template <int D, int NW>
+// NW waves per block, HG groups of 32 heads per wave (H = 32 * NW * HG)
+template <int D, int NW, int HG>
 static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, int64_t m,
                         int64_t W, int k, int64_t q_pos0, float scale, const void* q,
                         const void* ck, const void* cv, const int32_t* topk, const void* rk,
                         const void* rv, int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
                         hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((k_attend_bf16<NW, D>),
+    hipLaunchKernelGGL((k_attend_bf16<NW, D, HG>),
                        dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64), 0, st,
                        (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
                        (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq, Nc,
                        m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {
-        const int H = NW * 32;
+        const int H = NW * 32 * HG;
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,
                            dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
                            st, (const float*)ws, (uint16_t*)o, Tq, H, D, p.splits);
@@ -536,23 +577,26 @@ hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int
         return hipGetLastError();
     }
     const int nw = (int)(H / 32);
-#define CSA_ATT_CASE(DD, NN)                                                                  \
-    launch_bf16<DD, NN>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, topk, rk, rv,   \
-                        raw_pos0, raw_len, o, ws, st)
+#define CSA_ATT_CASE(DD, NN, GG)                                                              \
+    launch_bf16<DD, NN, GG>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, topk, rk, rv, \
+                            raw_pos0, raw_len, o, ws, st)
+    // one group of 32 heads per wave: at two groups (every K/V operand read
+    // feeding both) the registers allow one wave per SIMD, which measured
+    // slower than two waves of one group
     if (D == 128) {
         switch (nw) {
-            case 1: CSA_ATT_CASE(128, 1); break;
-            case 2: CSA_ATT_CASE(128, 2); break;
-            case 4: CSA_ATT_CASE(128, 4); break;
-            case 8: CSA_ATT_CASE(128, 8); break;
+            case 1: CSA_ATT_CASE(128, 1, 1); break;
+            case 2: CSA_ATT_CASE(128, 2, 1); break;
+            case 4: CSA_ATT_CASE(128, 4, 1); break;
+            case 8: CSA_ATT_CASE(128, 8, 1); break;
             default: return hipErrorInvalidValue;
         }
     } else {
         switch (nw) {
-            case 1: CSA_ATT_CASE(64, 1); break;
-            case 2: CSA_ATT_CASE(64, 2); break;
-            case 4: CSA_ATT_CASE(64, 4); break;
-            case 8: CSA_ATT_CASE(64, 8); break;
+            case 1: CSA_ATT_CASE(64, 1, 1); break;
+            case 2: CSA_ATT_CASE(64, 2, 1); break;
+            case 4: CSA_ATT_CASE(64, 4, 1); break;
+            case 8: CSA_ATT_CASE(64, 8, 1); break;
             default: return hipErrorInvalidValue;
         }
     }
