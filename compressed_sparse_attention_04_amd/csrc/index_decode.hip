@@ -19,6 +19,7 @@
 #include "internal.h"
 #include "mxfp4.h"
 #include "wave_select.h"
+#include "fp4_tiles.h"
 
 namespace csa {
 
@@ -128,47 +129,21 @@ k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     __syncthreads();
 
     const int kbytes = dI / 2, kscales = dI / 32;
-    const uint8_t* kcb = kc + b * Nc * kbytes;
-    const uint8_t* ksb = ks + b * Nc * kscales;
-    constexpr int UNR = 8;                           // key tiles in flight per wave
-    const int ntiles = (nkeys + 31) / 32;
-    for (int t0 = wave * UNR; t0 < ntiles; t0 += (DS_NT / WAVE) * UNR) {
-        i32x8 bop[UNR];
-        int sbk[UNR];
+    const TileSrc ts{kc + (b * Nc + c0) * kbytes, ks + (b * Nc + c0) * kscales, kbytes, kscales,
+                     nkeys, row, kb};
+    stream_tiles<DS_NT, 8, true>(ts, (nkeys + 31) / 32, 1, aop, sa,
+                                 [&](const f32x16& acc, int jt) {
+        const int jj = jt + row;
+        const int64_t j = c0 + jj;
 #pragma unroll
-        for (int x = 0; x < UNR; ++x) {
-            const int jj = (t0 + x) * 32 + row;
-            bop[x] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            sbk[x] = 127;
-            if (jj < nkeys && kb < kscales) {
-                const int64_t j = c0 + jj;
-                u32x4 w = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(kcb + j * kbytes + kb * 16));
-                bop[x][0] = (int)w[0]; bop[x][1] = (int)w[1];
-                bop[x][2] = (int)w[2]; bop[x][3] = (int)w[3];
-                sbk[x] = ksb[j * kscales + kb];
-            }
+        for (int u = 0; u < NU; ++u) {
+            const int q = qslot[u];
+            if (q >= qv || jj >= nkeys) continue;
+            const uint32_t key = score_key<HI>(acc, u);
+            scores[((b * Tq + q) * ncap) + j] = key;
+            if (j < ncq[u]) atomicAdd(&hist[q][lvl1_bin(key)], 1u);
         }
-#pragma unroll
-        for (int x = 0; x < UNR; ++x) {
-            const int jj = (t0 + x) * 32 + row;
-            const int64_t j = c0 + jj;
-            f32x16 acc = {};
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[x], acc, 4, 4, 0, sa, 0,
-                                                                   sbk[x]);
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int q = qslot[u];
-                if (q >= qv || jj >= nkeys) continue;
-                float s = 0.f;
-#pragma unroll
-                for (int hh = 0; hh < HI; ++hh) s += fmaxf(acc[u * HI + hh], 0.f);
-                const uint32_t key = s == 0.f ? 0u : __float_as_uint(s);
-                scores[((b * Tq + q) * ncap) + j] = key;
-                if (j < ncq[u]) atomicAdd(&hist[q][lvl1_bin(key)], 1u);
-            }
-        }
-    }
+    });
     __syncthreads();
     for (int i = tid; i < qv * SEL_NB; i += DS_NT) {
         const uint32_t c = hist_raw[i];

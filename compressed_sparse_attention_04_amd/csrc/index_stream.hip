@@ -28,6 +28,7 @@
 #include "internal.h"
 #include "mxfp4.h"
 #include "wave_select.h"
+#include "fp4_tiles.h"
 
 namespace csa {
 
@@ -59,83 +60,6 @@ struct StreamSmem {
     int nc[ST_QT];
     int any_active, any_sampled;
 };
-
-// One wave's batches of UNR key tiles: virtual tiles v = 0..nv-1 map to
-// key tiles v * stride; the wave takes batches wave, wave + NWV, ...  The
-// next batch's key loads are in flight while the current one is processed.
-struct TileSrc {
-    const uint8_t* kcb;
-    const uint8_t* ksb;
-    int kbytes, kscales, nc_max, row, kb;
-};
-
-// Loads are unconditional (rows clamped to the last candidate; lanes past
-// dI read a valid offset and get the neutral scale 2^0 against a zero A
-// operand), so the compiler can count them: the current batch is waited
-// for while the next one stays in flight.
-template <int UNR>
-__device__ __forceinline__ void load_batch(const TileSrc& ts, int v0, int stride,
-                                           u32x4 (&kw)[UNR], int (&ksv)[UNR]) {
-    const int koff = min(ts.kb * 16, ts.kbytes - 16);
-    const int soff = min(ts.kb, ts.kscales - 1);
-#pragma unroll
-    for (int x = 0; x < UNR; ++x) {
-        const int j = min((v0 + x) * stride * 32 + ts.row, ts.nc_max - 1);
-        kw[x] = *reinterpret_cast<const u32x4*>(ts.kcb + (int64_t)j * ts.kbytes + koff);
-        const int sc = ts.ksb[(int64_t)j * ts.kscales + soff];
-        ksv[x] = ts.kb < ts.kscales ? sc : 127;
-    }
-}
-
-// f(acc, j0): MFMA scores of the tile whose first key is j0 (this lane's
-// key is j0 + row for its S rows; see the callers)
-template <int UNR, typename F>
-__device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stride,
-                                             const i32x8& aop, int sa, F&& f) {
-    constexpr int NWV = ST_NT / WAVE;
-    const int wave = threadIdx.x / WAVE;
-    u32x4 kwA[UNR], kwB[UNR];
-    int ksA[UNR], ksB[UNR];
-    auto run = [&](const u32x4 (&kw)[UNR], const int (&ksv)[UNR], int v0) {
-#pragma unroll
-        for (int x = 0; x < UNR; ++x) {
-            if (v0 + x >= nv) break;
-            const i32x8 bop = {(int)kw[x][0], (int)kw[x][1], (int)kw[x][2], (int)kw[x][3],
-                               0, 0, 0, 0};
-            f32x16 acc = {};
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc, 4, 4, 0, sa, 0,
-                                                                   ksv[x]);
-            f(acc, (v0 + x) * stride * 32);
-            // one tile's scores live at a time (no hoisting of later MFMAs)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    int v0 = wave * UNR;
-    if (v0 >= nv) return;
-    load_batch<UNR>(ts, v0, stride, kwA, ksA);
-    while (true) {
-        load_batch<UNR>(ts, v0 + NWV * UNR, stride, kwB, ksB);
-        run(kwA, ksA, v0);
-        v0 += NWV * UNR;
-        if (v0 >= nv) break;
-        load_batch<UNR>(ts, v0 + NWV * UNR, stride, kwA, ksA);
-        run(kwB, ksB, v0);
-        v0 += NWV * UNR;
-        if (v0 >= nv) break;
-    }
-}
-
-// ReLU head sum of slot u of an MFMA tile as an order key.  ReLU is the
-// signed-integer max of the bit pattern with 0 (negative floats, -0
-// included, have negative patterns), so the sum of non-negative terms is
-// never -0.  The MFMA outputs are finite (products of FP4 values).
-template <int HI>
-__device__ __forceinline__ uint32_t score_key(const f32x16& acc, int u) {
-    float s = __int_as_float(max(__float_as_int(acc[u * HI]), 0));
-#pragma unroll
-    for (int hh = 1; hh < HI; ++hh) s += __int_as_float(max(__float_as_int(acc[u * HI + hh]), 0));
-    return __float_as_uint(s);
-}
 
 template <typename T, int HI>
 __global__ void __launch_bounds__(ST_NT)
@@ -244,7 +168,7 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
 #pragma unroll
         for (int u = 0; u < NU; ++u) act[u] = qslot[u] < qv && S.mode[qslot[u]] == M_SAMPLED;
         // 1. level-1 histogram of the sampled tiles
-        stream_tiles<st_unr<HI>()>(ts, (ntiles + ST_SAMPLE - 1) / ST_SAMPLE, ST_SAMPLE, aop, sa,
+        stream_tiles<ST_NT, st_unr<HI>()>(ts, (ntiles + ST_SAMPLE - 1) / ST_SAMPLE, ST_SAMPLE, aop, sa,
                      [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
 #pragma unroll
@@ -295,7 +219,7 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         int wc0[NU], wc1[NU];           // this wave's segment counts, half-waves 0 / 1
 #pragma unroll
         for (int u = 0; u < NU; ++u) wc0[u] = wc1[u] = 0;
-        stream_tiles<st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+        stream_tiles<ST_NT, st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
@@ -398,7 +322,7 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         __syncthreads();
         if (!S.any_active) break;
 
-        stream_tiles<st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+        stream_tiles<ST_NT, st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
