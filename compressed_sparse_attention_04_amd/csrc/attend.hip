@@ -119,133 +119,158 @@ __device__ __forceinline__ void issue_tile(int tau, int ct, int nval, int nwin, 
     }
 }
 
-// Running softmax state of one lane: HG groups of 32 heads, one head per
-// group (column col), half of each key tile.
-template <int D, int HG>
-struct Online {
-    f32x16 acc[HG][D / 32];
-    float m_run[HG], mb[HG], l_run[HG];
-};
+// Per-wave attention engine.  An engine owns HPW heads of the block's
+// query token: their Q^T operand, running softmax state and accumulators,
+// the work of one 32-key tile (K and V in LDS; the first nvalid keys
+// contribute), and the final store.  Scores stay in the exp2 domain
+// (scale_log2 = softmax scale * log2 e).
+//
+// Lazy rescaling: the reference maximum of a head moves only
+// when one of its scores exceeds it by more than a factor 2^8 in
+// probability, so p stays <= 256; sum and accumulators share the
+// reference, so the quotient is unchanged.  (tmax - m_run) is NaN while
+// both are -inf: no move.  The row sum adds the same bf16-rounded p that
+// the PV product takes.
 
-// One 32-key tile for HG head groups: S^T = K Q^T, online softmax,
-// O^T += V^T P^T.  K and V are the tile's LDS copies; every operand read
-// from them feeds all HG groups.  The first nvalid keys contribute.
-template <int D, int HG>
-__device__ __forceinline__ void tile_compute(Online<D, HG>& S, const bf16x8 (&qop)[HG][D / 16],
-                                             const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
-                                             int nvalid, float scale_log2) {
-    using G = TileGeom<D>;
-    const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
-    // S^T: rows = keys (8*(r/4) + 4*kb + r%4), column = head
-    // every K operand read is issued before the chain, so the LDS latency is
-    // paid once per tile, not once per MFMA pair
-    bf16x8 kop[D / 16];
+// 32 heads per wave, V_MFMA_F32_32X32X16_BF16:
+//   S^T = K Q^T: lane l holds head l%32, keys 8*(r/4) + 4*(l/32) + r%4
+//   O^T += V^T P^T: P^T straight from the S^T registers; V^T by
+//   transposing LDS reads (lane (16g + 4j + a) points at
+//   V[key 16u + 8h + 4kb + j][32dt + 16(g%2) + 4a])
+template <int D>
+struct Heads32 {
+    static constexpr int HPW = 32;
+    f32x16 acc[D / 32];
+    bf16x8 qop[D / 16];
+    float m_run, mb, l_run;
+
+    // qh: the query token's [H][D] rows, from this wave's first head
+    __device__ __forceinline__ void init(const uint16_t* qh) {
+        const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
+        const uint16_t* qp = qh + col * D + 8 * kb;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-        kop[kk] = *reinterpret_cast<const CSA_LDS bf16x8*>(
-            K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 sacc[HG];
-#pragma unroll
-    for (int h = 0; h < HG; ++h) sacc[h] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int h = 0; h < HG; ++h)
-            sacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[h][kk], sacc[h], 0, 0, 0);
-    }
-    // the V^T operands (independent of P) are read while the softmax runs
-    const int g = lane >> 4, wj = (lane >> 2) & 3, wa = lane & 3;
-    bf16x8 vop[2][D / 32];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int d = 32 * dt + 16 * (g & 1) + 4 * wa;
-            const int key0 = 16 * u + 4 * (g >> 1) + wj;
-            const int key1 = key0 + 8;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
-                V + key0 * G::ROWB + slot_of<D>(key0, d / 8) * 16 + (d % 8) * 2));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
-                V + key1 * G::ROWB + slot_of<D>(key1, d / 8) * 16 + (d % 8) * 2));
-            vop[u][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-    if (nvalid < ATT_KT) {                         // wave-uniform
-#pragma unroll
-        for (int h = 0; h < HG; ++h)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r / 4) + 4 * kb + (r % 4) >= nvalid) sacc[h][r] = -INFINITY;
-    }
-    // Lazy rescaling: the reference maximum moves only when a score exceeds
-    // it by more than a factor 2^8 in probability, so p stays <= 256; sum
-    // and accumulators share the reference, so the quotient is unchanged.
-    // (tmax - m_run) is NaN while both are -inf: no move.
-    float tmax[HG];
-    bool grow[HG], any = false;
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-        float t = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[h][r]);
-        tmax[h] = fmaxf(t, __shfl_xor(t, 32, 64));
-        grow[h] = (tmax[h] - S.m_run[h]) * scale_log2 > 8.f;
-        any |= grow[h];
-    }
-    if (__ballot(any)) {
-#pragma unroll
-        for (int h = 0; h < HG; ++h) {
-            float alpha = 1.f;
-            if (grow[h]) {
-                alpha = __builtin_amdgcn_exp2f((S.m_run[h] - tmax[h]) * scale_log2);   // 0 from -inf
-                S.m_run[h] = tmax[h];
-                S.mb[h] = -tmax[h] * scale_log2;
-            }
-            S.l_run[h] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) S.acc[h][dt][r] *= alpha;
-        }
-    }
-    uint32_t pb[HG][8];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[h][r], scale_log2, S.mb[h]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[h][r + 1], scale_log2, S.mb[h]));
-            pb[h][r / 2] = pack_bf16x2(p0, p1);
-        }
-        // the sum takes the same bf16 values the PV product takes
-        float psum = S.l_run[h];
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[h][x]), ones,
-                                                   psum, false);
-        S.l_run[h] = psum;
-    }
-    // O^T += V^T P^T.  k-step u covers keys 16u..16u+15; k-slot s of lane
-    // half kb is key 16u + 8*(s/4) + 4*kb + s%4 (the S^T register order).
-    // Each half of the V^T operand is one transposing LDS read: lane
-    // (16g + 4j + a) points at V[key 16u + 8h + 4kb + j][32dt + 16(g%2) + 4a].
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        bf16x8 pop[HG];
-#pragma unroll
-        for (int h = 0; h < HG; ++h) {
-            u32x4 w = {pb[h][4 * u], pb[h][4 * u + 1], pb[h][4 * u + 2], pb[h][4 * u + 3]};
-            pop[h] = __builtin_bit_cast(bf16x8, w);
-        }
+        for (int kk = 0; kk < D / 16; ++kk) qop[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int h = 0; h < HG; ++h)
-                S.acc[h][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop[h],
-                                                                       S.acc[h][dt], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+        m_run = -INFINITY;
+        mb = 0.f;
+        l_run = 0.f;
     }
-}
+
+    __device__ __forceinline__ void tile(const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
+                                         int nvalid, float scale_log2) {
+        using G = TileGeom<D>;
+        const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
+        // every K operand read is issued before the chain
+        bf16x8 kop[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            kop[kk] = *reinterpret_cast<const CSA_LDS bf16x8*>(
+                K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sacc = {};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], sacc, 0, 0, 0);
+        // the V^T operands (independent of P) are read while the softmax runs
+        const int g = lane >> 4, wj = (lane >> 2) & 3, wa = lane & 3;
+        bf16x8 vop[2][D / 32];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int d = 32 * dt + 16 * (g & 1) + 4 * wa;
+                const int key0 = 16 * u + 4 * (g >> 1) + wj;
+                const int key1 = key0 + 8;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
+                    V + key0 * G::ROWB + slot_of<D>(key0, d / 8) * 16 + (d % 8) * 2));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4*)(
+                    V + key1 * G::ROWB + slot_of<D>(key1, d / 8) * 16 + (d % 8) * 2));
+                vop[u][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        if (nvalid < ATT_KT) {                     // wave-uniform
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r / 4) + 4 * kb + (r % 4) >= nvalid) sacc[r] = -INFINITY;
+        }
+        float t = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[r]);
+        const float tmax = fmaxf(t, __shfl_xor(t, 32, 64));
+        const bool grow = (tmax - m_run) * scale_log2 > 8.f;
+        if (__ballot(grow)) {
+            float alpha = 1.f;
+            if (grow) {
+                alpha = __builtin_amdgcn_exp2f((m_run - tmax) * scale_log2);   // 0 from -inf
+                m_run = tmax;
+                mb = -tmax * scale_log2;
+            }
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        }
+        uint32_t pb[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            pb[r / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, mb)),
+                                    __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, mb)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float psum = l_run;
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[x]), ones, psum,
+                                                   false);
+        l_run = psum;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const u32x4 w = {pb[4 * u], pb[4 * u + 1], pb[4 * u + 2], pb[4 * u + 3]};
+            const bf16x8 pop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop, acc[dt], 0, 0, 0);
+        }
+    }
+
+    // oh: output rows [HPW][D] of this wave's heads (splits == 1), else pr:
+    // partial records [HPW][D + 2] (accumulators, max in the exp2 domain, sum)
+    __device__ __forceinline__ void store(uint16_t* oh, float* pr, float scale_log2) {
+        const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
+        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        if (oh) {
+            const float inv = 1.f / l_tot;
+            uint16_t* op = oh + col * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int d = 32 * dt + 8 * gg + 4 * kb;
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[dt][4 * gg] * inv, acc[dt][4 * gg + 1] * inv);
+                    w[1] = pack_bf16x2(acc[dt][4 * gg + 2] * inv, acc[dt][4 * gg + 3] * inv);
+                    *reinterpret_cast<u32x2*>(op + d) = w;
+                }
+        } else {
+            float* p = pr + col * (D + 2);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int d = 32 * dt + 8 * gg + 4 * kb;
+                    const f32x4 w = {acc[dt][4 * gg], acc[dt][4 * gg + 1], acc[dt][4 * gg + 2],
+                                     acc[dt][4 * gg + 3]};
+                    *reinterpret_cast<f32x4*>(p + d) = w;
+                }
+            if (kb == 0) {
+                p[D] = m_run == -INFINITY ? -INFINITY : m_run * scale_log2;
+                p[D + 1] = l_tot;
+            }
+        }
+    }
+};
 
 // vmcnt wait (other counters untouched) leaving n copies in flight
 #define CSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x3f70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -260,8 +285,8 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int NW, int D, int HG>
-__global__ void __launch_bounds__(NW * 64, HG == 1 ? 2 : 1)
+template <int NW, int D, class E>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
               const uint16_t* __restrict__ cv, const int32_t* __restrict__ topk,
               const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
@@ -270,7 +295,7 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
               int64_t raw_len, int splits) {
     using G = TileGeom<D>;
     constexpr int NT = NW * 64;
-    constexpr int H = NW * 32 * HG;
+    constexpr int H = NW * E::HPW;
     constexpr int KT = G::KT;
     constexpr int PER = 2 * ((G::NINS + NW - 1) / NW);   // copies per wave per tile
     // the stages live in distinct arrays, so the compiler can tell which
@@ -286,7 +311,6 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     const int split = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int col = lane & 31, kb = lane >> 5;
     const int64_t t = q_pos0 + i;
     const bool sparse = topk != nullptr;
     const int nc_t = (int)n_candidates(t, m, W);
@@ -336,24 +360,8 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     const char* rkb = reinterpret_cast<const char*>(rk + b * raw_len * D);
     const char* rvb = reinterpret_cast<const char*>(rv + b * raw_len * D);
 
-    // Q^T operand of group h: head (wave * HG + h) * 32 + col, d = 16*kk + 8*kb + 0..7
-    bf16x8 qop[HG][D / 16];
-    Online<D, HG> S;
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-        const int hq = (wave * HG + h) * 32 + col;
-        const uint16_t* qp = q + ((b * Tq + i) * H + hq) * D + 8 * kb;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qop[h][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S.acc[h][dt][r] = 0.f;
-        S.m_run[h] = -INFINITY;
-        S.mb[h] = 0.f;
-        S.l_run[h] = 0.f;
-    }
+    E eng;
+    eng.init(q + ((b * Tq + i) * H + wave * E::HPW) * D);
 
     auto issue = [&](int tau, uint8_t* sk, uint8_t* sv) {
         if (tau < tau1)
@@ -370,8 +378,7 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         lds_barrier();
         issue(tau + G::NST - 1, nk_, nv_);
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
-        tile_compute<D, HG>(S, qop, (const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_,
-                        nvalid, scale_log2);
+        eng.tile((const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_, nvalid, scale_log2);
     };
 
     issue(tau0, sK0, sV0);
@@ -386,43 +393,11 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         if (tau + 3 >= tau1) break;
         step(tau + 3, sK3, sV3, sK2, sV2);
     }
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-        const int hq = (wave * HG + h) * 32 + col;
-        const float l_tot = S.l_run[h] + __shfl_xor(S.l_run[h], 32, 64);
-        if (splits == 1) {
-            const float inv = 1.f / l_tot;
-            uint16_t* op = o + ((b * Tq + i) * H + hq) * D;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int d = 32 * dt + 8 * gg + 4 * kb;
-                    u32x2 w;
-                    w[0] = pack_bf16x2(S.acc[h][dt][4 * gg] * inv, S.acc[h][dt][4 * gg + 1] * inv);
-                    w[1] = pack_bf16x2(S.acc[h][dt][4 * gg + 2] * inv,
-                                       S.acc[h][dt][4 * gg + 3] * inv);
-                    *reinterpret_cast<u32x2*>(op + d) = w;
-                }
-        } else {
-            // partial record per (query, split, head): D accumulators, max, sum;
-            // the max is stored in the exp2 domain of the combine kernel
-            float* pr = part + (((b * Tq + i) * splits + split) * H + hq) * (D + 2);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int d = 32 * dt + 8 * gg + 4 * kb;
-                    f32x4 w = {S.acc[h][dt][4 * gg], S.acc[h][dt][4 * gg + 1],
-                               S.acc[h][dt][4 * gg + 2], S.acc[h][dt][4 * gg + 3]};
-                    *reinterpret_cast<f32x4*>(pr + d) = w;
-                }
-            if (kb == 0) {
-                pr[D] = S.m_run[h] == -INFINITY ? -INFINITY : S.m_run[h] * scale_log2;
-                pr[D + 1] = l_tot;
-            }
-        }
-    }
+    if (splits == 1)
+        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, scale_log2);
+    else
+        eng.store(nullptr, part + (((b * Tq + i) * splits + split) * H + wave * E::HPW) * (D + 2),
+                  scale_log2);
 }
 
 // Log-sum-exp merge of the split partials.  Grid (query, sequence, head
@@ -542,21 +517,21 @@ AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int6
     return p;
 }
 
-// NW waves per block, HG groups of 32 heads per wave (H = 32 * NW * HG)
-template <int D, int NW, int HG>
+// NW waves per block, E::HPW heads per wave
+template <int D, int NW, class E>
 static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, int64_t m,
                         int64_t W, int k, int64_t q_pos0, float scale, const void* q,
                         const void* ck, const void* cv, const int32_t* topk, const void* rk,
                         const void* rv, int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
                         hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((k_attend_bf16<NW, D, HG>),
+    hipLaunchKernelGGL((k_attend_bf16<NW, D, E>),
                        dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64), 0, st,
                        (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
                        (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq, Nc,
                        m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {
-        const int H = NW * 32 * HG;
+        const int H = NW * E::HPW;
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,
                            dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
                            st, (const float*)ws, (uint16_t*)o, Tq, H, D, p.splits);
@@ -577,26 +552,26 @@ hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int
         return hipGetLastError();
     }
     const int nw = (int)(H / 32);
-#define CSA_ATT_CASE(DD, NN, GG)                                                              \
-    launch_bf16<DD, NN, GG>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, topk, rk, rv, \
-                            raw_pos0, raw_len, o, ws, st)
-    // one group of 32 heads per wave: at two groups (every K/V operand read
-    // feeding both) the registers allow one wave per SIMD, which measured
-    // slower than two waves of one group
+#define CSA_ATT_CASE(DD, NN, EE)                                                              \
+    launch_bf16<DD, NN, EE<DD>>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, topk, rk, \
+                                rv, raw_pos0, raw_len, o, ws, st)
+    // 32 heads per wave.  (A 16-head engine on V_MFMA_F32_16X16X32_BF16 fits
+    // four waves per SIMD but doubles the LDS operand reads per flop, and
+    // measured slower.)
     if (D == 128) {
         switch (nw) {
-            case 1: CSA_ATT_CASE(128, 1, 1); break;
-            case 2: CSA_ATT_CASE(128, 2, 1); break;
-            case 4: CSA_ATT_CASE(128, 4, 1); break;
-            case 8: CSA_ATT_CASE(128, 8, 1); break;
+            case 1: CSA_ATT_CASE(128, 1, Heads32); break;
+            case 2: CSA_ATT_CASE(128, 2, Heads32); break;
+            case 4: CSA_ATT_CASE(128, 4, Heads32); break;
+            case 8: CSA_ATT_CASE(128, 8, Heads32); break;
             default: return hipErrorInvalidValue;
         }
     } else {
         switch (nw) {
-            case 1: CSA_ATT_CASE(64, 1, 1); break;
-            case 2: CSA_ATT_CASE(64, 2, 1); break;
-            case 4: CSA_ATT_CASE(64, 4, 1); break;
-            case 8: CSA_ATT_CASE(64, 8, 1); break;
+            case 1: CSA_ATT_CASE(64, 1, Heads32); break;
+            case 2: CSA_ATT_CASE(64, 2, Heads32); break;
+            case 4: CSA_ATT_CASE(64, 4, Heads32); break;
+            case 8: CSA_ATT_CASE(64, 8, Heads32); break;
             default: return hipErrorInvalidValue;
         }
     }
