@@ -131,7 +131,7 @@ k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     const int kbytes = dI / 2, kscales = dI / 32;
     const TileSrc ts{kc + (b * Nc + c0) * kbytes, ks + (b * Nc + c0) * kscales, kbytes, kscales,
                      nkeys, row, kb};
-    stream_tiles<DS_NT, 8, true>(ts, (nkeys + 31) / 32, 1, aop, sa,
+    stream_tiles<DS_NT, 4, true>(ts, (nkeys + 31) / 32, 1, aop, sa,
                                  [&](const f32x16& acc, int jt) {
         const int jj = jt + row;
         const int64_t j = c0 + jj;
