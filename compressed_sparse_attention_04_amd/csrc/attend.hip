@@ -401,32 +401,65 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
 }
 
 // Log-sum-exp merge of the split partials.  Grid (query, sequence, head
-// group of 8); one thread per (head, 4 dims).
+// group of 8); D/4 threads per head, 4 dims each.  The threads of a head
+// read the splits' maxima and sums in parallel (at most 64 splits) and
+// share the weights through LDS; the accumulator loads are unrolled so
+// several are in flight.
+constexpr int CMB_MAXS = 64;
+
 template <typename TO>
 __global__ void __launch_bounds__(256)
 k_attend_combine(const float* __restrict__ part, TO* __restrict__ o, int64_t Tq, int H, int D,
                  int splits) {
+    __shared__ float sw[8][CMB_MAXS];
+    __shared__ float sl[8];
     const int64_t i = blockIdx.x, b = blockIdx.y;
-    const int per_head = D / 4;
-    const int h = blockIdx.z * 8 + threadIdx.x / per_head;
-    const int d0 = (threadIdx.x % per_head) * 4;
-    if (threadIdx.x >= 8 * per_head || h >= H) return;
+    const int per_head = D / 4;                     // 32 or 16: a power of two <= 32
+    const int hh = threadIdx.x / per_head, t = threadIdx.x % per_head;
+    const int h = blockIdx.z * 8 + hh;
+    const bool live = threadIdx.x < 8 * per_head && h < H;
     const int64_t sstride = (int64_t)H * (D + 2);
-    const float* base = part + ((b * Tq + i) * splits * H + h) * (int64_t)(D + 2);
+    const float* base = part + ((b * Tq + i) * splits * H + (live ? h : 0)) * (int64_t)(D + 2);
+    // maxima and sums of the splits t, t + per_head, ...
+    float ms[CMB_MAXS / 16], ls[CMB_MAXS / 16];
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * sstride + D]);
-    float Lsum = 0.f;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-        const float* pr = base + s * sstride;
-        const float ms = pr[D];
-        if (ms == -INFINITY) continue;
-        const float wgt = __builtin_amdgcn_exp2f(ms - M);
-        Lsum += pr[D + 1] * wgt;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(pr + d0);
-        a[0] += v[0] * wgt; a[1] += v[1] * wgt; a[2] += v[2] * wgt; a[3] += v[3] * wgt;
+#pragma unroll
+    for (int x = 0; x < CMB_MAXS / 16; ++x) {
+        const int sp = t + x * per_head;
+        const bool ok = live && sp < splits;
+        ms[x] = ok ? base[sp * sstride + D] : -INFINITY;
+        ls[x] = ok ? base[sp * sstride + D + 1] : 0.f;
+        M = fmaxf(M, ms[x]);
     }
-    const float inv = 1.f / Lsum;
+    for (int off = per_head / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float L = 0.f;
+#pragma unroll
+    for (int x = 0; x < CMB_MAXS / 16; ++x) {
+        const int sp = t + x * per_head;
+        const float w = ms[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[x] - M);
+        L += ls[x] * w;
+        if (live && sp < splits) sw[hh][sp] = w;
+    }
+    for (int off = per_head / 2; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+    if (live && t == 0) sl[hh] = L;
+    __syncthreads();
+    if (!live) return;
+    const int d0 = t * 4;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 8;
+    for (int s0 = 0; s0 < splits; s0 += U) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = s0 + u < splits ? *reinterpret_cast<const f32x4*>(base + (s0 + u) * sstride + d0)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = s0 + u < splits ? sw[hh][s0 + u] : 0.f;
+            a[0] += v[u][0] * w; a[1] += v[u][1] * w; a[2] += v[u][2] * w; a[3] += v[u][3] * w;
+        }
+    }
+    const float inv = 1.f / sl[hh];
     TO* op = o + ((b * Tq + i) * H + h) * (int64_t)D + d0;
     if constexpr (sizeof(TO) == 2) {
         u32x2 w;
