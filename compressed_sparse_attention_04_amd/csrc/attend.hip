@@ -61,8 +61,8 @@ __device__ __forceinline__ int64_t list_row(const KeyList& L, int64_t s, const i
 // Key rows of one tile are copied straight from global memory into LDS
 // (global_load_lds, 16 bytes per lane, lane-contiguous).  A row of D bf16 is
 // CH = D/8 chunks of 16 bytes; chunk c of tile row r sits in slot
-// c ^ (r % CH) so that the 32 rows read by one MFMA operand load hit
-// different LDS banks.
+// c ^ f(r) (row_swz below) so that the rows read together by one operand
+// load hit different LDS banks.
 template <int D>
 struct TileGeom {
     static constexpr int KT = 32;                   // keys per tile
@@ -74,32 +74,39 @@ struct TileGeom {
     static constexpr int BYTES = KT * ROWB;         // bytes per tile and tensor
 };
 
-// Swizzle of row r: an injective map of r mod CH whose values for four
-// consecutive rows (4-aligned) differ above bit 0.  Chunk c of row r sits in
-// slot c ^ f(r), so the 16 rows of one MFMA K read and the 4 rows x 2
-// chunks of one transposing V read land on distinct banks.
+// Swizzle of row r, chunk c -> slot c ^ f(r).  With 64 banks of 4 bytes, a
+// 16-lane pass of a K operand read (16 rows, one 16-byte chunk each) and a
+// 32-lane pass of a transposing V read (4 consecutive rows x 4 chunks)
+// touch every bank once:
+//   D = 128 (16 slots): f(r) = 4 (r mod 4) + (r / 4 mod 4), a bijection of
+//     r mod 16 whose four values on rows 4m .. 4m + 3 lie in distinct
+//     4-slot groups;
+//   D = 64 (8 slots, a row covers half the banks): f(r) maps bits 1, 2, 3
+//     of r to bits 2, 0, 1; the odd rows use the other half of the banks.
 template <int D>
 __device__ __forceinline__ int row_swz(int r) {
-    if constexpr (TileGeom<D>::CH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return ((r & 3) << 1) | ((r >> 2) & 1);
+    if constexpr (TileGeom<D>::CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
 }
 template <int D>
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ row_swz<D>(r); }
 
-// Issue this wave's copies of the K and V rows of tile tau.  The key list
+// Issue the copies of wave `wave` (of the NW that share a tile) of the K
+// and V rows of tile tau.  The key list
 // of a query is cut into ct tiles of compressed rows (row ssel[s] for CSA,
 // row s for HCA; s < nval) followed by the tiles of its raw window (nwin
 // rows from raw_first), so every tile reads from one source.  Rows past the
 // end of a part repeat a row that exists and are masked by the caller.
 // All offsets fit 32 bits (validated on the host).
 template <int NW, int D>
-__device__ __forceinline__ void issue_tile(int tau, int ct, int nval, int nwin, int raw_first,
+__device__ __forceinline__ void issue_tile(int wave, int tau, int ct, int nval, int nwin,
+                                           int raw_first,
                                            bool sparse, const CSA_LDS int32_t* ssel,
                                            const char* ckb, const char* cvb, const char* rkb,
                                            const char* rvb, CSA_LDS uint8_t* sk,
                                            CSA_LDS uint8_t* sv) {
     using G = TileGeom<D>;
-    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
     const bool comp = tau < ct;
     const int base = comp ? ATT_KT * tau : ATT_KT * (tau - ct);
     const char* kb = comp ? ckb : rkb;
@@ -117,6 +124,19 @@ __device__ __forceinline__ void issue_tile(int tau, int ct, int nval, int nwin, 
         __builtin_amdgcn_global_load_lds(vb + off, (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB),
                                          16, 0, 0);
     }
+}
+
+// Maximum / sum of a value over lanes l and l ^ 32 (a VALU lane swap, so it
+// does not queue behind LDS reads)
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Per-wave attention engine.  An engine owns HPW heads of the block's
@@ -159,26 +179,40 @@ struct Heads32 {
         l_run = 0.f;
     }
 
-    __device__ __forceinline__ void tile(const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
-                                         int nvalid, float scale_log2) {
+    // state carried between the phases of a tile
+    f32x16 sacc;                  // S^T of the current tile
+    uint32_t pb[8];               // its probabilities as packed bf16 (P^T operand)
+    bf16x8 vop[2][D / 32];        // its V^T operands
+
+    // K operands kk in [K0, K1) of a tile (row col, 8 dims per lane and K step)
+    template <int K0 = 0, int K1 = D / 16>
+    __device__ __forceinline__ void read_k(const CSA_LDS uint8_t* K, bf16x8 (&kop)[D / 16]) const {
         using G = TileGeom<D>;
         const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
-        // every K operand read is issued before the chain
-        bf16x8 kop[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
+        for (int kk = K0; kk < K1; ++kk)
             kop[kk] = *reinterpret_cast<const CSA_LDS bf16x8*>(
                 K + col * G::ROWB + slot_of<D>(col, 2 * kk + kb) * 16);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 sacc = {};
+    }
+
+    // S^T = K Q^T
+    __device__ __forceinline__ void qk(const bf16x8 (&kop)[D / 16]) {
+        f32x16 s = {};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], sacc, 0, 0, 0);
-        // the V^T operands (independent of P) are read while the softmax runs
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], s, 0, 0, 0);
+        sacc = s;
+    }
+
+    // V^T operands of a tile (keys 16u .. 16u + 15 for u in [U0, U1)) by
+    // transposing reads
+    template <int U0 = 0, int U1 = 2>
+    __device__ __forceinline__ void read_v(const CSA_LDS uint8_t* V) {
+        using G = TileGeom<D>;
+        const int lane = threadIdx.x % 64;
         const int g = lane >> 4, wj = (lane >> 2) & 3, wa = lane & 3;
-        bf16x8 vop[2][D / 32];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = U0; u < U1; ++u)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
                 const int d = 32 * dt + 16 * (g & 1) + 4 * wa;
@@ -190,15 +224,27 @@ struct Heads32 {
                     V + key1 * G::ROWB + slot_of<D>(key1, d / 8) * 16 + (d % 8) * 2));
                 vop[u][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+    }
+
+    // online softmax of S^T (the first nvalid keys count): state update
+    // (mask, maximum, rescaling), then probabilities into pb and row sums
+    __device__ __forceinline__ void softmax(int nvalid, float scale_log2) {
+        softmax_max(nvalid, scale_log2);
+        softmax_exp(scale_log2);
+    }
+    __device__ __forceinline__ void softmax_max(int nvalid, float scale_log2) {
+        const int lane = threadIdx.x % 64, kb = lane >> 5;
         if (nvalid < ATT_KT) {                     // wave-uniform
+            // key 8 (r/4) + 4 kb + r%4 is masked when 8 (r/4) + r%4 >= lim
+            const int lim = nvalid - 4 * kb;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (8 * (r / 4) + 4 * kb + (r % 4) >= nvalid) sacc[r] = -INFINITY;
+                if (8 * (r / 4) + (r % 4) >= lim) sacc[r] = -INFINITY;
         }
         float t = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[r]);
-        const float tmax = fmaxf(t, __shfl_xor(t, 32, 64));
+        const float tmax = max_halves(t);
         const bool grow = (tmax - m_run) * scale_log2 > 8.f;
         if (__ballot(grow)) {
             float alpha = 1.f;
@@ -213,7 +259,8 @@ struct Heads32 {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
         }
-        uint32_t pb[8];
+    }
+    __device__ __forceinline__ void softmax_exp(float scale_log2) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
             pb[r / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, mb)),
@@ -225,21 +272,41 @@ struct Heads32 {
             psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[x]), ones, psum,
                                                    false);
         l_run = psum;
+    }
+
+    // O^T += V^T P^T over keys 16u .. 16u + 15 of the tile
+    __device__ __forceinline__ void pv_half(int u) {
+        const u32x4 w = {pb[4 * u], pb[4 * u + 1], pb[4 * u + 2], pb[4 * u + 3]};
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const u32x4 w = {pb[4 * u], pb[4 * u + 1], pb[4 * u + 2], pb[4 * u + 3]};
-            const bf16x8 pop = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop, acc[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[u][dt], pop, acc[dt], 0, 0, 0);
+    }
+    __device__ __forceinline__ void pv() {
+        pv_half(0);
+        pv_half(1);
+    }
+
+    // one whole tile: every K operand read is issued before the QK chain,
+    // the V^T operands (independent of P) are read while the softmax runs
+    __device__ __forceinline__ void tile(const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
+                                         int nvalid, float scale_log2) {
+        bf16x8 kop[D / 16];
+        read_k(K, kop);
+        __builtin_amdgcn_sched_barrier(0);
+        qk(kop);
+        read_v<0, 1>(V);
+        softmax_max(nvalid, scale_log2);
+        read_v<1, 2>(V);
+        softmax_exp(scale_log2);
+        pv();
     }
 
     // oh: output rows [HPW][D] of this wave's heads (splits == 1), else pr:
     // partial records [HPW][D + 2] (accumulators, max in the exp2 domain, sum)
     __device__ __forceinline__ void store(uint16_t* oh, float* pr, float scale_log2) {
         const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
-        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        const float l_tot = sum_halves(l_run);
         if (oh) {
             const float inv = 1.f / l_tot;
             uint16_t* op = oh + col * D;
@@ -365,7 +432,7 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
 
     auto issue = [&](int tau, uint8_t* sk, uint8_t* sv) {
         if (tau < tau1)
-            issue_tile<NW, D>(tau, ct, nval, nwin, raw_first, sparse, ssel, ckb, cvb, rkb, rvb,
+            issue_tile<NW, D>(wave, tau, ct, nval, nwin, raw_first, sparse, ssel, ckb, cvb, rkb, rvb,
                               (CSA_LDS uint8_t*)sk, (CSA_LDS uint8_t*)sv);
     };
     // one tile: wait for its copies, barrier (the stage written next is then
@@ -559,10 +626,10 @@ static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, 
                         hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL((k_attend_bf16<NW, D, E>),
-                       dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
-                       (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq, Nc,
-                       m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
+                       dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64), 0,
+                       st, (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
+                       (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq,
+                       Nc, m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {
         const int H = NW * E::HPW;
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,

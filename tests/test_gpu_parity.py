@@ -223,6 +223,7 @@ def rows(a, n):
     dict(dtype="bf16", H=128, D=128, T=3000, m=4, W=128, k=64, q_rows=rows(2900, 33)),
     dict(dtype="bf16", H=128, D=128, T=6000, m=4, W=128, k=512, q_rows=rows(5500, 9), B=2),
     dict(dtype="bf16", H=32, D=64, T=2000, m=4, W=40, k=100, q_rows=rows(1000, 17)),
+    dict(dtype="bf16", H=128, D=64, T=2500, m=4, W=100, k=200, q_rows=rows(1, 51)),
     dict(dtype="bf16", H=256, D=128, T=2000, m=4, W=128, k=32, q_rows=rows(1900, 3)),
 ])
 def test_csa_attend(case):
@@ -234,6 +235,7 @@ def test_csa_attend(case):
     dict(dtype="f32", H=4, D=64, T=2000, m=128, W=128, k=0, q_rows=rows(1900, 20)),
     dict(dtype="bf16", H=128, D=128, T=5000, m=128, W=128, k=0, q_rows=rows(4950, 40)),
     dict(dtype="bf16", H=128, D=128, T=700, m=4, W=64, k=0, q_rows=rows(0, 30)),
+    dict(dtype="bf16", H=128, D=64, T=3000, m=16, W=128, k=0, q_rows=rows(2000, 37)),
 ])
 def test_hca_attend(case):
     say("hca_attend", case)
@@ -249,6 +251,8 @@ def test_hca_attend(case):
          B=2, decode_tail=True),
     dict(dtype="bf16", H=128, D=128, T=4 * 20000, m=4, W=128, k=0, q_rows=[4 * 20000 - 1],
          B=1, decode_tail=True),
+    dict(dtype="bf16", H=128, D=64, T=4 * 7001, m=4, W=128, k=300, q_rows=[4 * 7001 - 3],
+         B=3, decode_tail=True),
 ])
 def test_decode_split(case):
     say("decode split", case)
