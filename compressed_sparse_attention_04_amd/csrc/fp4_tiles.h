@@ -48,17 +48,23 @@ __device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stri
     const int wave = threadIdx.x / WAVE;
     u32x4 kwA[UNR], kwB[UNR];
     int ksA[UNR], ksB[UNR];
+    auto mfma = [&](const u32x4& kw, int ksv) {
+        const i32x8 bop = {(int)kw[0], (int)kw[1], (int)kw[2], (int)kw[3], 0, 0, 0, 0};
+        const f32x16 zero = {};
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, zero, 4, 4, 0, sa, 0,
+                                                                ksv);
+    };
+    // the MFMA of tile x + 1 is issued before the scores of tile x are
+    // used, so its latency is hidden behind f
     auto run = [&](const u32x4 (&kw)[UNR], const int (&ksv)[UNR], int v0) {
+        f32x16 next = mfma(kw[0], ksv[0]);
 #pragma unroll
         for (int x = 0; x < UNR; ++x) {
             if (v0 + x >= nv) break;
-            const i32x8 bop = {(int)kw[x][0], (int)kw[x][1], (int)kw[x][2], (int)kw[x][3],
-                               0, 0, 0, 0};
-            f32x16 acc = {};
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc, 4, 4, 0, sa, 0,
-                                                                   ksv[x]);
+            const f32x16 acc = next;
+            if (x + 1 < UNR) next = mfma(kw[x + 1], ksv[x + 1]);
             f(acc, (v0 + x) * stride * 32);
-            // one tile's scores live at a time (no hoisting of later MFMAs)
+            // at most two tiles' scores live at a time
             __builtin_amdgcn_sched_barrier(0);
         }
     };

@@ -40,9 +40,8 @@ constexpr int ST_BUF = ST_SEG * (ST_NT / WAVE);
 constexpr int ST_MAXW = 1024;          // bitmap words per row -> 32768 candidates
 constexpr int ST_SAMPLE = 8;           // one key tile in ST_SAMPLE is sampled
 constexpr int ST_SAMPLE_MIN = 2048;    // candidates a row needs for the sampled path
-// key tiles per wave and batch: 8, or 4 when HI < 4 (more query slots per
-// lane leave fewer registers)
-template <int HI> constexpr int st_unr() { return HI == 4 ? 8 : 4; }
+// key tiles per wave and batch (two batches and two tiles' scores are live)
+template <int HI> constexpr int st_unr() { return 4; }
 
 enum : int { M_DONE = 0, M_HIST1 = 1, M_HIST = 2, M_COLLECT = 3, M_SAMPLED = 4 };
 
@@ -228,7 +227,11 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
                 const bool above = ok && key >= hi[u];
                 const bool in = ok && !above && key >= lo[u];
                 const int q = qslot[u] < ST_QT ? qslot[u] : 0;
-                if (above) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
+                // the 32 lanes of a half-wave hold the tile's 32 keys of
+                // one query, and each bitmap word is written by one tile
+                // only (sel starts at zero for sampled rows)
+                const uint64_t bab = __ballot(above);
+                if (row == 0 && act[u]) S.sel[q][j0 >> 5] = kb ? (uint32_t)(bab >> 32) : (uint32_t)bab;
                 const uint64_t bin = __ballot(in);
                 if (bin != 0ull) {
                     const uint32_t h0 = (uint32_t)bin, h1 = (uint32_t)(bin >> 32);
