@@ -259,6 +259,45 @@ def test_decode_split(case):
     attend_case(**case)
 
 
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_attend_wide_score_range(kind):
+    """A key far above the first tile's scores (about 90 in the exp2 domain)
+    in a later tile of every row: the fixed-reference softmax of the 64-head
+    kernel must notice and redo the rows with the true maximum."""
+    H, D, T, W = 128, 128, 3000, 128
+    m = 4 if kind == "csa" else 16
+    k = 64
+    q_rows = rows(2900, 5)
+    w = I.Workload("t", "csa", seed=57, dtype="bf16", B=1, T=T, m=m, H=H, D=D, W=W, k=k,
+                   Tq=len(q_rows), q_pos0=q_rows[0])
+    say("wide score range", kind)
+    Nc = T // m
+    q = torch.full((1, len(q_rows), H, D), 0.25, dtype=torch.bfloat16)
+    ck = I.draw_cache(w, "ck", Nc)
+    cv = I.draw_cache(w, "cv", Nc)
+    rk = I.draw_cache(w, "rk", T)
+    rv = I.draw_cache(w, "rv", T)
+    q_pos = np.asarray(q_rows)
+    if kind == "csa":
+        rng = np.random.default_rng(5)
+        tk = np.array([[random_selection(rng, oracle.n_cand(t, m, W), k) for t in q_pos]],
+                      np.int32)
+        for r in range(len(q_rows)):
+            ck[0, int(tk[0, r, 45])] = 2.0          # kept-list position 45: the second tile
+        ref = oracle.attend(f64(q), f64(ck), f64(cv), tk, f64(rk), f64(rv), 0, q_pos, m, W)
+        got = csa.csa_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), torch.from_numpy(tk).to(DEV),
+                             rk.to(DEV), rv.to(DEV), m=m, W=W, q_pos0=int(q_pos[0]), raw_pos0=0)
+    else:
+        ck[0, 100] = 2.0                             # the fourth compressed tile
+        ref = oracle.attend(f64(q), f64(ck), f64(cv), None, f64(rk), f64(rv), 0, q_pos, m, W)
+        got = csa.hca_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), rk.to(DEV), rv.to(DEV), m=m,
+                             W=W, q_pos0=int(q_pos[0]), raw_pos0=0)
+    torch.cuda.synchronize()
+    err = maxerr(got, ref)
+    say("  max err", err)
+    assert err <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- end to end
 def test_tiny_config_end_to_end():
     """compress -> MXFP4 keys -> index/top-k -> attend on the tiny fp32 CSA
