@@ -45,7 +45,7 @@ DEFAULT = "pair_prefill_128k"
 # profiles/traffic.json for a stage is reported only while the digest of
 # these sources (comments and blank space removed) still matches.
 _IDX = ["indexer.hip", "index_stream.hip", "index_decode.hip", "wave_select.h", "select.h",
-        "mxfp4.h", "common.h", "internal.h"]
+        "mxfp4.h", "fp4_tiles.h", "common.h", "internal.h"]
 STAGE_SOURCES = {
     "index_topk": _IDX,
     "csa_attend": ["attend.hip", "common.h", "internal.h"],
