@@ -69,7 +69,9 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     StreamSmem& S = *reinterpret_cast<StreamSmem*>(smem_raw);
     constexpr int NU = 16 / HI;                     // query slots per lane in an MFMA tile
 
-    const int64_t q0 = (int64_t)blockIdx.x * ST_QT;
+    // the longest row groups (latest queries, most candidates) go first, so
+    // the kernel's last blocks are its shortest
+    const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * ST_QT;
     const int64_t b = blockIdx.y;
     const int qv = (int)min((int64_t)ST_QT, Tq - q0);
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
