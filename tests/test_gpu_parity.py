@@ -175,9 +175,11 @@ def test_index_one_head_small_k():
 
 
 # ---------------------------------------------------------------- attention
-def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False):
+def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False, corrupt=False):
     """Stage-wise: q, compressed and raw caches drawn directly; kept sets
-    drawn at random (k > 0) or every candidate (k == 0, HCA)."""
+    drawn at random (k > 0) or every candidate (k == 0, HCA).  corrupt: about
+    one kept entry in eight replaced by -1 or an index past the candidates
+    (entries that contribute nothing)."""
     w = I.Workload("t", "csa", seed=seed, dtype=dtype, B=B, T=T, m=m, H=H, D=D, W=W, k=max(k, 1),
                    Tq=len(q_rows), q_pos0=int(q_rows[0]))
     Nc = T // m
@@ -197,6 +199,11 @@ def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False
     if k > 0:
         tk = np.array([[random_selection(rng, oracle.n_cand(t, m, W), k) for t in q_pos]
                        for _ in range(B)], np.int32)
+        if corrupt:
+            nc = np.array([oracle.n_cand(t, m, W) for t in q_pos])
+            bad = rng.random(tk.shape) < 0.125
+            junk = np.where(rng.random(tk.shape) < 0.5, -1, nc[None, :, None] + 3)
+            tk = np.where(bad, junk, tk).astype(np.int32)
         ref = oracle.attend(f64(q), f64(ck), f64(cv), tk, f64(rk), f64(rv), raw_pos0, q_pos, m, W)
         got = csa.csa_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), torch.from_numpy(tk).to(DEV),
                              rk.to(DEV), rv.to(DEV), m=m, W=W, q_pos0=int(q_pos[0]),
@@ -242,6 +249,26 @@ def test_hca_attend(case):
     attend_case(**case)
 
 
+# Many query rows (>= 512): one block per row, no split of the key list;
+# rows from position 0 have one-tile key lists, and a corrupted kept list
+# has invalid entries in the middle of its tiles.
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", H=128, D=128, T=3000, m=4, W=128, k=64, q_rows=rows(0, 600)),
+    dict(dtype="bf16", H=128, D=128, T=5000, m=4, W=128, k=512, q_rows=rows(4400, 600)),
+    dict(dtype="bf16", H=128, D=64, T=2500, m=4, W=100, k=200, q_rows=rows(1500, 300), B=2),
+    dict(dtype="bf16", H=256, D=128, T=2000, m=4, W=128, k=32, q_rows=rows(1400, 520)),
+    dict(dtype="bf16", H=256, D=64, T=2000, m=4, W=128, k=48, q_rows=rows(1000, 530)),
+    dict(dtype="bf16", H=128, D=128, T=3000, m=4, W=128, k=100, q_rows=rows(2000, 700),
+         corrupt=True),
+    dict(dtype="bf16", H=128, D=128, T=1200, m=4, W=64, k=0, q_rows=rows(0, 1100)),
+    dict(dtype="bf16", H=128, D=64, T=3000, m=16, W=128, k=0, q_rows=rows(2200, 400), B=2),
+    dict(dtype="bf16", H=256, D=128, T=5000, m=128, W=128, k=0, q_rows=rows(4400, 600)),
+])
+def test_attend_many_rows(case):
+    say("attend many rows", case)
+    attend_case(**case)
+
+
 @pytest.mark.parametrize("case", [
     # decode rows: one query per sequence, raw rows hold only the window,
     # the key list is split over blocks and merged
@@ -262,8 +289,8 @@ def test_decode_split(case):
 @pytest.mark.parametrize("kind", ["csa", "hca"])
 def test_attend_wide_score_range(kind):
     """A key far above the first tile's scores (about 90 in the exp2 domain)
-    in a later tile of every row: the fixed-reference softmax of the 64-head
-    kernel must notice and redo the rows with the true maximum."""
+    in a later tile of every row: the running maximum must move by far more
+    than the lazy rescaling threshold, with the split partials merged."""
     H, D, T, W = 128, 128, 3000, 128
     m = 4 if kind == "csa" else 16
     k = 64
@@ -355,3 +382,41 @@ def test_determinism_bitwise():
     a, b = run(), run()
     assert torch.equal(a[0], b[0])
     assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_attend_wide_score_many_rows(kind):
+    """Raw row 2700 far above the other keys (about 90 in the exp2 domain):
+    the 128 rows whose window holds it meet it in a later tile than the
+    first, so their running maximum must move by far more than the lazy
+    rescaling threshold; the other rows of the launch never see it."""
+    H, D, T, W = 128, 128, 3000, 128
+    m = 4 if kind == "csa" else 16
+    k = 64
+    q_rows = rows(2400, 600)
+    w = I.Workload("t", "csa", seed=58, dtype="bf16", B=1, T=T, m=m, H=H, D=D, W=W, k=k,
+                   Tq=len(q_rows), q_pos0=q_rows[0])
+    say("wide score range, many rows", kind)
+    Nc = T // m
+    q = torch.full((1, len(q_rows), H, D), 0.25, dtype=torch.bfloat16)
+    ck = I.draw_cache(w, "ck", Nc)
+    cv = I.draw_cache(w, "cv", Nc)
+    rk = I.draw_cache(w, "rk", T)
+    rv = I.draw_cache(w, "rv", T)
+    rk[0, 2700] = 2.0
+    q_pos = np.asarray(q_rows)
+    if kind == "csa":
+        rng = np.random.default_rng(6)
+        tk = np.array([[random_selection(rng, oracle.n_cand(t, m, W), k) for t in q_pos]],
+                      np.int32)
+        ref = oracle.attend(f64(q), f64(ck), f64(cv), tk, f64(rk), f64(rv), 0, q_pos, m, W)
+        got = csa.csa_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), torch.from_numpy(tk).to(DEV),
+                             rk.to(DEV), rv.to(DEV), m=m, W=W, q_pos0=int(q_pos[0]), raw_pos0=0)
+    else:
+        ref = oracle.attend(f64(q), f64(ck), f64(cv), None, f64(rk), f64(rv), 0, q_pos, m, W)
+        got = csa.hca_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), rk.to(DEV), rv.to(DEV), m=m,
+                             W=W, q_pos0=int(q_pos[0]), raw_pos0=0)
+    torch.cuda.synchronize()
+    err = maxerr(got, ref)
+    say("  max err", err)
+    assert err <= TOL["bf16"]
