@@ -105,8 +105,10 @@ class Stage:
         self.name, self.fn, self.flops, self.bytes, self.peak_key = name, fn, flops, bytes_, peak_key
 
 
-def setup_prefill(dev, layers):
-    """CSA (and optionally HCA) prefill layers over one sequence."""
+def setup_prefill(dev, layers, shared_kv=False):
+    """CSA (and optionally HCA) prefill layers over one sequence.  shared_kv:
+    one vector per entry and raw token serves as key and value (only K is
+    compressed, and the same buffers are passed as K and V)."""
     import torch
     from compressed_sparse_attention_04_amd import binding as csa
     from compressed_sparse_attention_04_amd import inputs as I
@@ -119,14 +121,18 @@ def setup_prefill(dev, layers):
         T, D, H, m, W = w.T, w.D, w.H, w.m, w.W
         tokens = w.Tq
         ck = torch.empty((1, w.Nc, D), dtype=q.dtype, device=dev)
-        cv = torch.empty_like(ck)
+        cv = ck if shared_kv else torch.empty_like(ck)
+        rv = raw["k"] if shared_kv else raw["v"]
         q_pos = np.arange(w.q_pos0, w.q_pos0 + w.Tq)
-        cbytes = 2.0 * (T * D * 2 + T * D * 2) + 2.0 * w.Nc * D * 2
-        stages.append(Stage(f"compress_m{m}",
-                            lambda raw=raw, m=m, ck=ck, cv=cv: (
-                                csa.hca_compress(raw["k"], raw["gk"], m, out=ck),
-                                csa.hca_compress(raw["v"], raw["gv"], m, out=cv)),
-                            bytes_=cbytes, peak_key="hbm_GBps"))
+        nvec = 1 if shared_kv else 2
+        cbytes = nvec * (T * D * 2 + T * D * 2 + w.Nc * D * 2)
+        if shared_kv:
+            compress = lambda raw=raw, m=m, ck=ck: csa.hca_compress(raw["k"], raw["gk"], m, out=ck)
+        else:
+            compress = lambda raw=raw, m=m, ck=ck, cv=cv: (
+                csa.hca_compress(raw["k"], raw["gk"], m, out=ck),
+                csa.hca_compress(raw["v"], raw["gv"], m, out=cv))
+        stages.append(Stage(f"compress_m{m}", compress, bytes_=cbytes, peak_key="hbm_GBps"))
         if w.kind == "csa":
             k_idx = I.draw_indexer_keys(w, device=dev)
             q_idx = I.draw_indexer_queries(w, device=dev)
@@ -149,25 +155,26 @@ def setup_prefill(dev, layers):
                                 flops=2.0 * w.HI * w.dI * float(nc.sum()),
                                 peak_key="fp4_TFLOPs"))
             stages.append(Stage("csa_attend",
-                                lambda q=q, ck=ck, cv=cv, topk=topk, raw=raw, o=o, w=w:
-                                csa.csa_attend(q, ck, cv, topk, raw["k"], raw["v"], m=w.m, W=w.W,
+                                lambda q=q, ck=ck, cv=cv, topk=topk, raw=raw, rv=rv, o=o, w=w:
+                                csa.csa_attend(q, ck, cv, topk, raw["k"], rv, m=w.m, W=w.W,
                                                q_pos0=w.q_pos0, raw_pos0=0, out=o),
                                 flops=4.0 * H * D * float(nkeys.sum()),
                                 bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
         else:
             nkeys, nc = attend_keys(q_pos, m, W, 0)
             stages.append(Stage("hca_attend",
-                                lambda q=q, ck=ck, cv=cv, raw=raw, o=o, w=w:
-                                csa.hca_attend(q, ck, cv, raw["k"], raw["v"], m=w.m, W=w.W,
+                                lambda q=q, ck=ck, cv=cv, raw=raw, rv=rv, o=o, w=w:
+                                csa.hca_attend(q, ck, cv, raw["k"], rv, m=w.m, W=w.W,
                                                q_pos0=w.q_pos0, raw_pos0=0, out=o),
                                 flops=4.0 * H * D * float(nkeys.sum()),
                                 bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
     return stages, tokens, notes
 
 
-def _decode_caches(w, dev, with_keys):
+def _decode_caches(w, dev, with_keys, shared_kv=False):
     """Precompress every sequence's 1M-token raw context chunk by chunk on the
-    GPU; keep the last W raw rows.  Untimed."""
+    GPU; keep the last W raw rows.  Untimed.  shared_kv: K only, passed as
+    both K and V."""
     import torch
     from compressed_sparse_attention_04_amd import binding as csa
     from compressed_sparse_attention_04_amd import inputs as I
@@ -175,18 +182,20 @@ def _decode_caches(w, dev, with_keys):
     L = I.chunk_len(w)
     per = L // w.m
     ck = torch.empty((w.B, w.Nc, w.D), dtype=torch.bfloat16, device=dev)
-    cv = torch.empty_like(ck)
+    cv = ck if shared_kv else torch.empty_like(ck)
     rk = torch.empty((w.B, w.W, w.D), dtype=torch.bfloat16, device=dev)
-    rv = torch.empty_like(rk)
+    rv = rk if shared_kv else torch.empty_like(rk)
     nchunks = w.T // L
     for b in range(w.B):
         for c in range(nchunks):
             x = {n: I.draw_chunk(w, n, b, c, device=dev)[None] for n in ("k", "v", "gk", "gv")}
             csa.hca_compress(x["k"], x["gk"], w.m, out=ck[b:b + 1, c * per:(c + 1) * per])
-            csa.hca_compress(x["v"], x["gv"], w.m, out=cv[b:b + 1, c * per:(c + 1) * per])
+            if not shared_kv:
+                csa.hca_compress(x["v"], x["gv"], w.m, out=cv[b:b + 1, c * per:(c + 1) * per])
             if c == nchunks - 1:
                 rk[b].copy_(x["k"][0, -w.W:])
-                rv[b].copy_(x["v"][0, -w.W:])
+                if not shared_kv:
+                    rv[b].copy_(x["v"][0, -w.W:])
     out = {"ck": ck, "cv": cv, "rk": rk, "rv": rv}
     if with_keys:
         k_idx = I.draw_indexer_keys(w, device=dev)
@@ -197,23 +206,29 @@ def _decode_caches(w, dev, with_keys):
     return out
 
 
-def setup_decode(dev, w, min_bytes=600e6):
+def setup_decode(dev, w, min_bytes=600e6, shared_kv=False):
     import torch
     from compressed_sparse_attention_04_amd import binding as csa
     from compressed_sparse_attention_04_amd import inputs as I
 
     sparse = w.kind == "csa"
-    base = _decode_caches(w, dev, sparse)
+    base = _decode_caches(w, dev, sparse, shared_kv)
     q = I.draw_queries(w, device=dev)
     t = w.q_pos0
     nkeys, nc = attend_keys([t], w.m, w.W, w.k if sparse else 0)
-    kv_bytes = float(nkeys[0]) * w.D * 2 * 2
+    kv_bytes = float(nkeys[0]) * w.D * 2 * (1 if shared_kv else 2)
     qo_bytes = w.H * w.D * 2 * 2
     key_bytes = float(nc[0]) * (w.dI // 2 + w.dI // 32) if sparse else 0.0
     step_bytes = w.B * (kv_bytes + qo_bytes + key_bytes)
     # rotate over enough copies that the step's working set is not cached
     ncopy = max(2, int(np.ceil(min_bytes / step_bytes)) + 1)
-    copies = [base] + [{n: v.clone() for n, v in base.items()} for _ in range(ncopy - 1)]
+    def clone(c):
+        d = {n: v.clone() for n, v in c.items() if not (shared_kv and n in ("cv", "rv"))}
+        if shared_kv:
+            d["cv"], d["rv"] = d["ck"], d["rk"]
+        return d
+
+    copies = [base] + [clone(base) for _ in range(ncopy - 1)]
     o = torch.empty_like(q)
     state = {"i": 0}
     stages = []
@@ -336,6 +351,9 @@ def main():
                     choices=["pair_prefill_128k", "csa_prefill_32k", "hca_decode_1m",
                              "csa_decode_1m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-kv", action="store_true",
+                    help="one vector per compressed entry and raw token serves as key and "
+                         "value (the same buffers passed as K and V); default: separate K, V")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -367,24 +385,26 @@ def main():
     warmup = args.warmup if args.warmup is not None else (5 if decode else 2)
 
     if args.workload == "pair_prefill_128k":
-        stages, tokens, notes = setup_prefill(dev, [I.PAIR_CSA_128K, I.PAIR_HCA_128K])
+        stages, tokens, notes = setup_prefill(dev, [I.PAIR_CSA_128K, I.PAIR_HCA_128K],
+                                              args.shared_kv)
         wl = {"workload": "csa_hca_layer_pair_prefill", "seq_len": 131072, "batch": 1,
               "heads": 128, "kv_heads": 1, "head_dim": 128, "m_csa": 4, "m_hca": 128,
               "top_k": 512, "indexer": "4x64 MXFP4", "window": 128}
         metric, unit = "prefill tokens/s", "tokens/s"
     elif args.workload == "csa_prefill_32k":
-        stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K])
+        stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K], args.shared_kv)
         wl = {"workload": "csa_prefill", "seq_len": 32768, "batch": 1, "heads": 128,
               "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
               "window": 128}
         metric, unit = "prefill tokens/s", "tokens/s"
     else:
         w = I.HCA_DECODE_1M if args.workload == "hca_decode_1m" else I.CSA_DECODE_1M
-        stages, tokens, notes = setup_decode(dev, w)
+        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv)
         wl = {"workload": args.workload.replace("_1m", "") + "_1m_ctx", "context": w.T,
               "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
               "top_k": w.k if w.kind == "csa" else None, "window": w.W}
         metric, unit = "1M-ctx decode tokens/s/GPU", "tokens/s"
+    wl["kv"] = "one vector as key and value" if args.shared_kv else "separate K and V"
 
     stream = torch.cuda.current_stream()
 
@@ -428,7 +448,8 @@ def main():
         roof = {"bound": "mfma", "achieved": d.flops / sec / 1e12, "peak": PEAK[d.peak_key],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(args.workload, d.name)
+    # (counter passes exist for the default inputs only)
+    roof["traffic"] = None if args.shared_kv else recorded_traffic(args.workload, d.name)
     roof["kernel"] = d.name
     roof["ms_per_launch"] = stage_ms[dom]
 

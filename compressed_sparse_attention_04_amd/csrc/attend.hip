@@ -98,7 +98,9 @@ __device__ __forceinline__ int slot_of(int r, int c) { return c ^ row_swz<D>(r);
 // rows from raw_first), so every tile reads from one source.  Rows past the
 // end of a part repeat a row that exists and are masked by the caller.
 // All offsets fit 32 bits (validated on the host).
-template <int NW, int D>
+// SHARED: one vector serves as key and value (the same rows passed as K and
+// V), so only the K rows are copied and the V operands are read from them.
+template <int NW, int D, bool SHARED>
 __device__ __forceinline__ void issue_tile(int wave, int tau, int ct, int nval, int nwin,
                                            int raw_first,
                                            bool sparse, const CSA_LDS int32_t* ssel,
@@ -121,8 +123,10 @@ __device__ __forceinline__ void issue_tile(int wave, int tau, int ct, int nval, 
         const uint32_t off = (uint32_t)row * (uint32_t)G::ROWB + (uint32_t)cb;
         __builtin_amdgcn_global_load_lds(kb + off, (CSA_LDS void*)(sk + ins * G::RPI * G::ROWB),
                                          16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + off, (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB),
-                                         16, 0, 0);
+        if constexpr (!SHARED)
+            __builtin_amdgcn_global_load_lds(vb + off,
+                                             (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB), 16, 0,
+                                             0);
     }
 }
 
@@ -352,7 +356,7 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int NW, int D, class E>
+template <int NW, int D, class E, bool SHARED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
               const uint16_t* __restrict__ cv, const int32_t* __restrict__ topk,
@@ -364,7 +368,7 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     constexpr int NT = NW * 64;
     constexpr int H = NW * E::HPW;
     constexpr int KT = G::KT;
-    constexpr int PER = 2 * ((G::NINS + NW - 1) / NW);   // copies per wave per tile
+    constexpr int PER = (SHARED ? 1 : 2) * ((G::NINS + NW - 1) / NW);   // copies per wave per tile
     // the stages live in distinct arrays, so the compiler can tell which
     // stage an LDS read touches and never waits on another stage's copies
     __shared__ __attribute__((aligned(16))) uint8_t sK0[G::BYTES], sV0[G::BYTES];
@@ -432,7 +436,8 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
 
     auto issue = [&](int tau, uint8_t* sk, uint8_t* sv) {
         if (tau < tau1)
-            issue_tile<NW, D>(wave, tau, ct, nval, nwin, raw_first, sparse, ssel, ckb, cvb, rkb, rvb,
+            issue_tile<NW, D, SHARED>(wave, tau, ct, nval, nwin, raw_first, sparse, ssel, ckb, cvb,
+                                      rkb, rvb,
                               (CSA_LDS uint8_t*)sk, (CSA_LDS uint8_t*)sv);
     };
     // one tile: wait for its copies, barrier (the stage written next is then
@@ -445,7 +450,8 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         lds_barrier();
         issue(tau + G::NST - 1, nk_, nv_);
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
-        eng.tile((const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)cv_, nvalid, scale_log2);
+        eng.tile((const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)(SHARED ? ck_ : cv_), nvalid,
+                 scale_log2);
     };
 
     issue(tau0, sK0, sV0);
@@ -625,9 +631,11 @@ static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, 
                         const void* rv, int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
                         hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((k_attend_bf16<NW, D, E>),
-                       dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64), 0,
-                       st, (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
+    // the same rows passed as keys and values: copy them once
+    const bool shared = ck == cv && rk == rv;
+    auto kern = shared ? k_attend_bf16<NW, D, E, true> : k_attend_bf16<NW, D, E, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64),
+                       0, st, (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
                        (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq,
                        Nc, m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {

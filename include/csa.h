@@ -152,6 +152,9 @@ csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64
  *   o[b][i][h] = sum_{s in S} softmax_s( scale * q[b][i][h] . key_s ) val_s
  * with key/val = ck/cv rows for entries and rk/rv rows for raw tokens.
  * Slots holding -1 or a non-candidate index contribute nothing.
+ * One vector per entry and raw token may serve as both key and value (the
+ * "shared key-value" reading of the same post): pass the same buffer as ck
+ * and cv and as rk and rv, and each row is then read once.
  *   q      [B, Tq, H, D]   dt         o   [B, Tq, H, D]  dt
  *   ck, cv [B, Nc, D]      dt         topk [B, Tq, k]    int32
  *   rk, rv [B, raw_len, D] dt, must cover positions w0..t of every query

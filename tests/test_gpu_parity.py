@@ -175,11 +175,14 @@ def test_index_one_head_small_k():
 
 
 # ---------------------------------------------------------------- attention
-def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False, corrupt=False):
+def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False, corrupt=False,
+                shared_kv=False):
     """Stage-wise: q, compressed and raw caches drawn directly; kept sets
     drawn at random (k > 0) or every candidate (k == 0, HCA).  corrupt: about
     one kept entry in eight replaced by -1 or an index past the candidates
-    (entries that contribute nothing)."""
+    (entries that contribute nothing).  shared_kv: one vector per entry and
+    raw token serves as key and value (the same device buffers passed as K
+    and V)."""
     w = I.Workload("t", "csa", seed=seed, dtype=dtype, B=B, T=T, m=m, H=H, D=D, W=W, k=max(k, 1),
                    Tq=len(q_rows), q_pos0=int(q_rows[0]))
     Nc = T // m
@@ -194,7 +197,12 @@ def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False
         raw_pos0 = 0
         rk = I.draw_cache(w, "rk", T)
         rv = I.draw_cache(w, "rv", T)
+    if shared_kv:
+        cv, rv = ck, rk
     q_pos = np.asarray(q_rows)
+    d_ck, d_rk = ck.to(DEV), rk.to(DEV)
+    d_cv = d_ck if shared_kv else cv.to(DEV)
+    d_rv = d_rk if shared_kv else rv.to(DEV)
     rng = np.random.default_rng(seed)
     if k > 0:
         tk = np.array([[random_selection(rng, oracle.n_cand(t, m, W), k) for t in q_pos]
@@ -205,14 +213,13 @@ def attend_case(dtype, H, D, T, m, W, k, q_rows, B=1, seed=31, decode_tail=False
             junk = np.where(rng.random(tk.shape) < 0.5, -1, nc[None, :, None] + 3)
             tk = np.where(bad, junk, tk).astype(np.int32)
         ref = oracle.attend(f64(q), f64(ck), f64(cv), tk, f64(rk), f64(rv), raw_pos0, q_pos, m, W)
-        got = csa.csa_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), torch.from_numpy(tk).to(DEV),
-                             rk.to(DEV), rv.to(DEV), m=m, W=W, q_pos0=int(q_pos[0]),
-                             raw_pos0=raw_pos0)
+        got = csa.csa_attend(q.to(DEV), d_ck, d_cv, torch.from_numpy(tk).to(DEV), d_rk, d_rv,
+                             m=m, W=W, q_pos0=int(q_pos[0]), raw_pos0=raw_pos0)
     else:
         ref = oracle.attend(f64(q), f64(ck), f64(cv), None, f64(rk), f64(rv), raw_pos0, q_pos, m,
                             W)
-        got = csa.hca_attend(q.to(DEV), ck.to(DEV), cv.to(DEV), rk.to(DEV), rv.to(DEV), m=m, W=W,
-                             q_pos0=int(q_pos[0]), raw_pos0=raw_pos0)
+        got = csa.hca_attend(q.to(DEV), d_ck, d_cv, d_rk, d_rv, m=m, W=W, q_pos0=int(q_pos[0]),
+                             raw_pos0=raw_pos0)
     torch.cuda.synchronize()
     err = maxerr(got, ref)
     say("  max err", err)
@@ -267,6 +274,26 @@ def test_hca_attend(case):
 def test_attend_many_rows(case):
     say("attend many rows", case)
     attend_case(**case)
+
+
+# One vector as key and value (the shared key-value reading): the library
+# copies each row once and reads the value operands from the key tiles.
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", H=128, D=128, T=3000, m=4, W=128, k=64, q_rows=rows(2900, 33)),
+    dict(dtype="bf16", H=128, D=128, T=3000, m=4, W=128, k=100, q_rows=rows(2000, 600),
+         corrupt=True),
+    dict(dtype="bf16", H=64, D=64, T=2000, m=4, W=40, k=100, q_rows=rows(1000, 17)),
+    dict(dtype="bf16", H=128, D=128, T=1200, m=4, W=64, k=0, q_rows=rows(0, 700)),
+    dict(dtype="bf16", H=256, D=64, T=3000, m=16, W=128, k=0, q_rows=rows(2000, 37)),
+    dict(dtype="bf16", H=128, D=128, T=128 * 3000, m=128, W=128, k=0, q_rows=[128 * 3000 - 1],
+         B=3, decode_tail=True),
+    dict(dtype="bf16", H=128, D=128, T=4 * 20000, m=4, W=128, k=512, q_rows=[4 * 20000 - 1],
+         B=2, decode_tail=True),
+    dict(dtype="f32", H=8, D=64, T=1024, m=4, W=128, k=16, q_rows=rows(1008, 16)),
+])
+def test_attend_shared_kv(case):
+    say("attend shared kv", case)
+    attend_case(shared_kv=True, **case)
 
 
 @pytest.mark.parametrize("case", [
