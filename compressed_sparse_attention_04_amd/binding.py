@@ -26,6 +26,8 @@ _SIGS = {
     "csa_last_error": ([], ctypes.c_char_p),
     "hca_compress": ([ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p], ctypes.c_int),
     "csa_quantize_mxfp4": ([ctypes.c_int, _i64, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "hca_append": ([ctypes.c_int] + [_i64] * 5 + [_p] * 4 + [_i64, _p, _p, _i64,
+                   ctypes.POINTER(_i64)] + [_p] * 4 + [_i64, _p], ctypes.c_int),
     "csa_index_topk_workspace": ([_i64] * 9 + [ctypes.POINTER(_sz)], ctypes.c_int),
     "csa_index_topk": ([ctypes.c_int] + [_i64] * 9 + [_p] * 5 + [_sz, _p], ctypes.c_int),
     "csa_attend_workspace": ([ctypes.c_int] + [_i64] * 6 + [ctypes.POINTER(_sz)], ctypes.c_int),
@@ -111,6 +113,21 @@ def hca_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out=None, stream=N
     _call("hca_compress", _dt(x), B, T, C, m, _ptr(x), _ptr(gate), gate.shape[-1], _ptr(out),
           _stream(x, stream))
     return out
+
+
+def hca_append(k_new, v_new, gk_new, gv_new, rk, rv, gk_blk, gv_blk, ck, cv, *, m: int, W: int,
+               t: int, win_pos0: int, stream=None) -> int:
+    """One decode step of cache upkeep: token t [B, C] (gates [B, 1|C]) joins
+    the window buffer rk/rv [B, wcap, C] (row r = position win_pos0 + r) and
+    the block's gate slots gk_blk/gv_blk [B, m, 1|C]; a completed block is
+    pooled into ck/cv [B, nc_cap, C].  Returns the window buffer's first
+    position after the call."""
+    B, C = k_new.shape
+    p0 = ctypes.c_int64(int(win_pos0))
+    _call("hca_append", _dt(k_new), B, C, m, W, t, _ptr(k_new), _ptr(v_new), _ptr(gk_new),
+          _ptr(gv_new), gk_new.shape[1], _ptr(rk), _ptr(rv), rk.shape[1], ctypes.byref(p0),
+          _ptr(gk_blk), _ptr(gv_blk), _ptr(ck), _ptr(cv), ck.shape[1], _stream(k_new, stream))
+    return p0.value
 
 
 def csa_quantize_mxfp4(x: torch.Tensor, codes=None, scales=None, stream=None):

@@ -97,6 +97,48 @@ csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m
                                          (int)gate_channels, stream), fn);
 }
 
+csa_status hca_append(csa_dtype dt, int64_t B, int64_t C, int64_t m, int64_t W, int64_t t,
+                      const void* k_new, const void* v_new, const void* gk_new,
+                      const void* gv_new, int64_t gate_channels, void* rk, void* rv,
+                      int64_t wcap, int64_t* win_pos0, void* gk_blk, void* gv_blk, void* ck,
+                      void* cv, int64_t nc_cap, hipStream_t stream) {
+    const char* fn = "hca_append";
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    CHECK(win_pos0, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(B >= 1 && B < 65536 * 1024LL, CSA_EINVAL, "%s: B out of range", fn);
+    CHECK(C >= 8 && C % 8 == 0 && C <= 1024, CSA_EINVAL,
+          "%s: C must be a multiple of 8 in [8, 1024] (got %lld)", fn, (long long)C);
+    CHECK(m >= 1 && W >= m, CSA_EINVAL, "%s: need 1 <= m <= W (got m = %lld, W = %lld)", fn,
+          (long long)m, (long long)W);
+    CHECK(wcap >= 2 * W && wcap < ((int64_t)1 << 31) / C, CSA_EINVAL,
+          "%s: the window buffer needs 2W <= wcap rows (got %lld)", fn, (long long)wcap);
+    CHECK(gate_channels == 1 || gate_channels == C, CSA_EINVAL,
+          "%s: gate_channels must be 1 or C", fn);
+    const int64_t p0 = *win_pos0;
+    const int64_t keep = t < W - 1 ? t : W - 1;          // rows the window buffer must hold
+    CHECK(t >= 0 && p0 >= 0 && p0 <= t - keep && t - p0 <= wcap, CSA_EINVAL,
+          "%s: the window buffer holds positions %lld .. %lld but token %lld needs its %lld "
+          "predecessors and at most %lld rows",
+          fn, (long long)p0, (long long)t - 1, (long long)t, (long long)keep, (long long)wcap);
+    CHECK(nc_cap >= (t + 1) / m && nc_cap < ((int64_t)1 << 31) / C, CSA_EINVAL,
+          "%s: nc_cap = %lld cannot hold entry %lld", fn, (long long)nc_cap,
+          (long long)((t + 1) / m - 1));
+    CHECK(k_new && v_new && gk_new && gv_new && rk && rv && gk_blk && gv_blk && ck && cv,
+          CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(k_new) && aligned16(v_new) && aligned16(rk) && aligned16(rv) &&
+              aligned16(ck) && aligned16(cv) &&
+              (gate_channels == 1 ||
+               (aligned16(gk_new) && aligned16(gv_new) && aligned16(gk_blk) && aligned16(gv_blk))),
+          CSA_EINVAL, "%s: rows (and per-channel gates) must be 16-byte aligned", fn);
+    int64_t np0 = p0;
+    const csa_status st = launched(
+        csa::launch_append((int)dt, B, C, m, W, t, p0, wcap, gate_channels, nc_cap, k_new, v_new,
+                           gk_new, gv_new, rk, rv, gk_blk, gv_blk, ck, cv, &np0, stream),
+        fn);
+    if (st == CSA_OK) *win_pos0 = np0;
+    return st;
+}
+
 csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, const void* x,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream) {
     const char* fn = "csa_quantize_mxfp4";

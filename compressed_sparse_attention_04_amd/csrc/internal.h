@@ -11,6 +11,14 @@ namespace csa {
 hipError_t launch_compress(int dt, const void* x, const void* gate, void* out, int64_t B,
                            int64_t T, int C, int m, int gc, hipStream_t st);
 
+// one decode step of cache upkeep (see hca_append); *new_win_pos0 gets the
+// window buffer's first position after the call
+hipError_t launch_append(int dt, int64_t B, int64_t C, int64_t m, int64_t W, int64_t t,
+                         int64_t win_pos0, int64_t wcap, int64_t gc, int64_t nc_cap,
+                         const void* k_new, const void* v_new, const void* gk_new,
+                         const void* gv_new, void* rk, void* rv, void* gk_blk, void* gv_blk,
+                         void* ck, void* cv, int64_t* new_win_pos0, hipStream_t st);
+
 hipError_t launch_quant_mxfp4(int dt, const void* x, uint8_t* codes, uint8_t* scales,
                               int64_t rows, int d, hipStream_t st);
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -92,6 +92,42 @@ const char *csa_last_error(void);
 csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m,
                         const void *x, const void *gate, int64_t gate_channels,
                         void *out, hipStream_t stream);
+
+/*
+ * hca_append -- one decode step of cache upkeep (jiwasawa.github.io post,
+ * CSA token-level compression: every m adjacent tokens become one entry;
+ * the sliding-window branch keeps the newest tokens uncompressed).  The
+ * token at position t joins the raw window rows and the gate logits of its
+ * block; when it completes a block (t + 1 a multiple of m), the block's m
+ * rows are pooled into entry (t + 1)/m - 1 of ck, cv exactly as
+ * hca_compress pools them (the same arithmetic, so the entries are
+ * bit-identical to a pooling of the whole sequence).  For CSA, the new
+ * entry's indexer key is encoded separately with csa_quantize_mxfp4.
+ *   k_new, v_new   [B, C]                 dt   the token's K and V rows
+ *   gk_new, gv_new [B, gate_channels]     dt   its gate logits for K and V
+ *   rk, rv         [B, wcap, C]           dt   window buffer: row r holds
+ *                  position *win_pos0 + r; on entry positions *win_pos0 ..
+ *                  t - 1, on return *win_pos0 .. t (pass raw_pos0 =
+ *                  *win_pos0 and raw_len = t - *win_pos0 + 1 to attention)
+ *   *win_pos0      host, in/out: when the buffer is full (t - *win_pos0 ==
+ *                  wcap), its newest W - 1 rows move to the front first and
+ *                  *win_pos0 becomes t - W + 1
+ *   gk_blk, gv_blk [B, m, gate_channels]  dt   gate logits of the block's
+ *                  tokens so far (slot = position mod m); owned by the caller,
+ *                  written only by this call
+ *   ck, cv         [B, nc_cap, C]         dt   compressed caches
+ * Passing the same buffers as K and V (k_new == v_new, rk == rv, ck == cv)
+ * keeps one vector per token and entry.
+ * Requires C % 8 == 0 (C <= 1024), 1 <= m <= W, wcap >= 2 W, the window
+ * buffer holding the min(t, W - 1) positions before t (*win_pos0 <= t -
+ * min(t, W - 1)), and nc_cap >= (t + 1)/m.  On an error nothing is written
+ * and *win_pos0 is unchanged.
+ */
+csa_status hca_append(csa_dtype dt, int64_t B, int64_t C, int64_t m, int64_t W, int64_t t,
+                      const void *k_new, const void *v_new, const void *gk_new,
+                      const void *gv_new, int64_t gate_channels, void *rk, void *rv,
+                      int64_t wcap, int64_t *win_pos0, void *gk_blk, void *gv_blk, void *ck,
+                      void *cv, int64_t nc_cap, hipStream_t stream);
 
 /*
  * csa_quantize_mxfp4 -- MXFP4 encoding of rows (studioglobal.ai answer,

@@ -33,14 +33,14 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared()
     assert {"hca_compress", "csa_index_topk", "csa_attend", "hca_attend",
-            "csa_quantize_mxfp4"} <= set(names)
+            "csa_quantize_mxfp4", "hca_append"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGS), "binding and header disagree"
 
 
 def test_version(L):
-    assert L.csa_abi_version() == 1
+    assert L.csa_abi_version() == 2
 
 
 def err(L):
@@ -57,6 +57,29 @@ def test_compress_rejects(L):
     assert "null" in err(L)
     assert L.hca_compress(1, 1, 8, 8, 4, ctypes.c_void_p(0x1002), P, 1, P, None) == EINVAL
     assert "aligned" in err(L)
+
+
+def test_append_rejects(L):
+    def call(dt=1, B=1, C=128, m=4, W=128, t=10, gc=128, wcap=256, p0=0, nc_cap=64, kn=P):
+        pos = ctypes.c_int64(p0)
+        st = L.hca_append(dt, B, C, m, W, t, kn, P, P, P, gc, P, P, wcap, ctypes.byref(pos), P,
+                          P, P, P, nc_cap, None)
+        return st, pos.value
+    assert call(dt=7)[0] == EINVAL and "dtype" in err(L)
+    assert call(C=12)[0] == EINVAL                        # C % 8
+    assert call(m=0)[0] == EINVAL and call(m=200)[0] == EINVAL   # 1 <= m <= W
+    assert call(wcap=200)[0] == EINVAL                    # wcap >= 2W
+    assert call(gc=3)[0] == EINVAL                        # gate channels
+    assert call(t=300, p0=200)[0] == EINVAL               # buffer lacks positions 173 .. 199
+    assert "window buffer" in err(L)
+    assert call(t=600, p0=300)[0] == EINVAL               # past the buffer's capacity
+    assert call(t=5, p0=1)[0] == EINVAL                   # lacks position 0
+    assert call(t=399, p0=200, nc_cap=99)[0] == EINVAL    # entry 99 does not fit
+    assert "nc_cap" in err(L)
+    assert call(kn=None)[0] == EINVAL and "null" in err(L)
+    assert call(kn=ctypes.c_void_p(0x1002))[0] == EINVAL and "aligned" in err(L)
+    st, pos = call(t=300, p0=200)
+    assert st == EINVAL and pos == 200                    # unchanged on an error
 
 
 def test_quantize_rejects(L):
