@@ -49,6 +49,11 @@ def lib():
         L.oracle_quant_mxfp4.argtypes = [_i64, _i64, _ptr, _ptr, _ptr]
         L.oracle_mxfp4_value.argtypes = [ctypes.c_int, ctypes.c_int]
         L.oracle_mxfp4_value.restype = ctypes.c_double
+        L.oracle_quant_mxfp8.argtypes = [_i64, _i64, _ptr, _ptr, _ptr]
+        L.oracle_mxfp8_value.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.oracle_mxfp8_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_value.restype = ctypes.c_double
         L.oracle_n_cand.argtypes = [_i64, _i64, _i64]
         L.oracle_n_cand.restype = _i64
         L.oracle_index_scores.argtypes = [_i64] * 7 + [_ptr] * 7
@@ -56,7 +61,7 @@ def lib():
         L.oracle_index_topk.argtypes = [_i64] * 8 + [_ptr] * 7
         L.oracle_attend.argtypes = ([_i64] * 8 + [_ptr, ctypes.c_double] + [_ptr] * 6
                                     + [_i64, _i64, _ptr])
-        for f in ("oracle_compress", "oracle_quant_mxfp4", "oracle_index_scores",
+        for f in ("oracle_compress", "oracle_quant_mxfp4", "oracle_quant_mxfp8", "oracle_index_scores",
                   "oracle_select_topk", "oracle_index_topk", "oracle_attend"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -106,6 +111,39 @@ def quant_mxfp4(x):
 
 def mxfp4_value(code: int, scale: int) -> float:
     return lib().oracle_mxfp4_value(int(code), int(scale))
+
+
+def quant_mxfp8(x):
+    """MXFP8 (E4M3) encoding of rows of x [..., d] (d % 32 == 0), the storage
+    of the compressed KV entries (ai-papers.net article, hybrid attention
+    section: most KV entries in FP8): returns (codes [..., d] uint8,
+    scales [..., d/32] uint8)."""
+    x = _f64(x)
+    shape = x.shape
+    d = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    codes = np.zeros(shape, np.uint8)
+    scales = np.zeros(shape[:-1] + (d // 32,), np.uint8)
+    _check(lib().oracle_quant_mxfp8(rows, d, _p(x), _p(codes), _p(scales)), "quant_mxfp8")
+    return codes, scales
+
+
+def mxfp8_value(code: int, scale: int) -> float:
+    return lib().oracle_mxfp8_value(int(code), int(scale))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(int(code))
+
+
+def dequant_mxfp8(codes, scales) -> np.ndarray:
+    """Exact values (fp64) of MXFP8 rows: codes [..., d], scales [..., d/32]."""
+    c = np.ascontiguousarray(codes, np.uint8)
+    s = np.ascontiguousarray(scales, np.uint8)
+    mag = np.array([e4m3_value(v) for v in range(128)], np.float64)
+    val = mag[c & 0x7F] * np.where(c & 0x80, -1.0, 1.0)
+    sc = np.ldexp(1.0, s.astype(np.int64) - 127)
+    return val * np.repeat(sc, 32, axis=-1)
 
 
 def n_cand(t: int, m: int, W: int) -> int:

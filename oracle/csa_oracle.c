@@ -156,6 +156,84 @@ double oracle_mxfp4_value(int code, int scale)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Step 2b: FP8 storage of the compressed KV entries.                       */
+/*                                                                          */
+/* [P5, hybrid attention section]: most KV entries are stored in FP8, the   */
+/* indexer runs at FP4.  [P4, FP4/FP8 mixed precision]: the FP4 side is     */
+/* MXFP4.  Reading: "most" are the compressed entries (the raw window of W  */
+/* tokens stays in the compute type), in the FP8 member of the same OCP     */
+/* Microscaling family, MXFP8 E4M3: every run of 32 values shares a scale   */
+/* 2^e stored as the byte e+127 with                                        */
+/*     e = floor(log2(max |x|)) - 8     (8 = largest exponent of E4M3),     */
+/* clamped to [-127, 127]; an all-zero run takes e = -127.  Each x*2^-e is  */
+/* rounded to the nearest E4M3 magnitude (bias 7, three mantissa bits,      */
+/* subnormals k*2^-9, largest finite 448; the all-ones code is NaN and is   */
+/* never produced), ties to the even code, anything beyond 448 saturating   */
+/* to 448; bit 7 copies the sign bit of x.                                  */
+/* ------------------------------------------------------------------------ */
+
+/* magnitude of E4M3 code c in 0..126 */
+double oracle_e4m3_value(int c)
+{
+    c &= 0x7F;
+    if (c < 8) return ldexp((double)c, -9);
+    return ldexp(1.0 + (c & 7) / 8.0, (c >> 3) - 7);
+}
+
+static int e4m3_round(double y)       /* y >= 0; nearest, ties to even code */
+{
+    int best = 0;
+    double bestd = y;
+    for (int c = 1; c < 127; ++c) {
+        double d = fabs(y - oracle_e4m3_value(c));
+        if (d < bestd || (d == bestd && (c % 2 == 0) && (best % 2 != 0))) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+int oracle_quant_mxfp8(int64_t rows, int64_t d, const double *x,
+                       uint8_t *codes, uint8_t *scales)
+{
+    if (rows < 0 || d <= 0 || d % 32 != 0) return 1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t blk = 0; blk < d / 32; ++blk) {
+            const double *v = x + r * d + blk * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i)
+                if (fabs(v[i]) > amax) amax = fabs(v[i]);
+            int e;
+            if (amax == 0.0) {
+                e = -127;
+            } else {
+                int ex;
+                frexp(amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1) */
+                e = (ex - 1) - 8;          /* floor(log2 amax) - 8 */
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            scales[r * (d / 32) + blk] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i) {
+                double y = ldexp(fabs(v[i]), -e);
+                codes[r * d + blk * 32 + i] =
+                    (uint8_t)(e4m3_round(y) | (signbit(v[i]) ? 0x80 : 0));
+            }
+        }
+    }
+    return 0;
+}
+
+/* Value of one MXFP8 element: (-1)^s * e4m3[code & 127] * 2^(scale-127). */
+double oracle_mxfp8_value(int code, int scale)
+{
+    double g = oracle_e4m3_value(code & 0x7F);
+    if (code & 0x80) g = -g;
+    return ldexp(g, scale - 127);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Candidate set of a query.                                                */
 /*                                                                          */
 /* [P1 CSA bullets; P3 SWA branch; P4 CSA/HCA section]: a branch that      */
