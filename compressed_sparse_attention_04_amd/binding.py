@@ -36,6 +36,11 @@ _SIGS = {
     "hca_attend_workspace": ([ctypes.c_int] + [_i64] * 8 + [ctypes.POINTER(_sz)], ctypes.c_int),
     "hca_attend": ([ctypes.c_int] + [_i64] * 8 + [ctypes.c_float] + [_p] * 5 + [_i64, _i64]
                    + [_p, _p, _sz, _p], ctypes.c_int),
+    "csa_quantize_mxfp8": ([ctypes.c_int, _i64, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "csa_attend_mxfp8": ([_i64] * 9 + [ctypes.c_float] + [_p] * 8 + [_i64, _i64]
+                         + [_p, _p, _sz, _p], ctypes.c_int),
+    "hca_attend_mxfp8": ([_i64] * 8 + [ctypes.c_float] + [_p] * 7 + [_i64, _i64]
+                         + [_p, _p, _sz, _p], ctypes.c_int),
 }
 
 
@@ -206,4 +211,52 @@ def hca_attend(q, ck, cv, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0: int,
     _call("hca_attend", _dt(q), B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck),
           _ptr(cv), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws), wsb,
           _stream(q, stream))
+    return out
+
+
+def csa_quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):
+    """MXFP8 (E4M3) encoding of rows of x [..., d]: (codes [..., d], scales [..., d/32])."""
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+    _call("csa_quantize_mxfp8", _dt(x), rows, d, _ptr(x), _ptr(codes), _ptr(scales),
+          _stream(x, stream))
+    return codes, scales
+
+
+def csa_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, topk, rk, rv, *, m: int, W: int,
+                     q_pos0: int, raw_pos0: int, scale: float = 1.0, out=None, ws=None,
+                     stream=None):
+    """csa_attend with MXFP8 compressed entries (codes [B,Nc,128] uint8,
+    scales [B,Nc,4] uint8); q, window rows and output bf16."""
+    B, Tq, H, D = q.shape
+    Nc = ck.shape[1]
+    k = topk.shape[2]
+    raw_len = rk.shape[1]
+    nbytes = csa_attend_workspace(CSA_BF16, B, Tq, H, D, k, W)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    if out is None:
+        out = torch.empty_like(q)
+    _call("csa_attend_mxfp8", B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
+          _ptr(cv), _ptr(ck_scales), _ptr(cv_scales), _ptr(topk), _ptr(rk), _ptr(rv), raw_pos0,
+          raw_len, _ptr(out), _ptr(ws), wsb, _stream(q, stream))
+    return out
+
+
+def hca_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, rk, rv, *, m: int, W: int, q_pos0: int,
+                     raw_pos0: int, scale: float = 1.0, out=None, ws=None, stream=None):
+    """hca_attend with MXFP8 compressed entries."""
+    B, Tq, H, D = q.shape
+    Nc = ck.shape[1]
+    raw_len = rk.shape[1]
+    nbytes = hca_attend_workspace(CSA_BF16, B, Tq, H, D, Nc, m, W, q_pos0)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    if out is None:
+        out = torch.empty_like(q)
+    _call("hca_attend_mxfp8", B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck), _ptr(cv),
+          _ptr(ck_scales), _ptr(cv_scales), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out),
+          _ptr(ws), wsb, _stream(q, stream))
     return out

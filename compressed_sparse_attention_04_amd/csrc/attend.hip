@@ -473,6 +473,261 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
                   scale_log2);
 }
 
+// ---- compressed entries stored as MXFP8 -------------------------------------
+// (ai-papers.net article, hybrid attention section: most KV entries are kept
+// in FP8.)  Compressed K/V rows arrive as E4M3 codes [Nc][128] with one
+// power-of-two scale byte per 32 values [Nc][4]; the raw window stays bf16.
+// Per block and tile of 32 compressed rows the codes and scales are copied
+// into an LDS staging slot (global_load_lds, half the bytes of bf16 rows),
+// three tiles ahead; one tile ahead, the block converts the staged tile into
+// the swizzled bf16 layout of the engine above (each value times its scale
+// is exact in bf16), so the MFMA work and its numerics are those of the
+// bf16 kernel.  Window tiles are copied straight into the bf16 buffer one
+// tile ahead.
+//
+// Staging slot (D = 128): K codes [32][128] | V codes [32][128] | K scales
+// [32][4] | V scales [32][4].  A wave-wide copy moves 8 code rows (64 lanes
+// x 16 bytes); one more copy moves both tensors' scale rows (lanes 0-31 K,
+// 32-63 V, 4 bytes each).  Copies are dealt to the waves round-robin.
+struct Mx8Geom {
+    static constexpr int D = 128;
+    static constexpr int CODE_B = ATT_KT * D;             // 4096 bytes per tensor
+    static constexpr int SC_OFF = 2 * CODE_B;             // scales after the codes
+    static constexpr int BYTES = SC_OFF + 2 * ATT_KT * 4; // 8448
+    static constexpr int NCOPY_CODES = CODE_B / 1024;     // 4 per tensor
+};
+
+// vmcnt wait leaving n (wave-uniform, 0 .. 18) copies in flight
+__device__ __forceinline__ void wait_vm_leaving(int n) {
+    switch (n) {
+#define CSA_WCASE(x) case x: CSA_WAIT_VM(x); break;
+        CSA_WCASE(1) CSA_WCASE(2) CSA_WCASE(3) CSA_WCASE(4) CSA_WCASE(5) CSA_WCASE(6)
+        CSA_WCASE(7) CSA_WCASE(8) CSA_WCASE(9) CSA_WCASE(10) CSA_WCASE(11) CSA_WCASE(12)
+        CSA_WCASE(13) CSA_WCASE(14) CSA_WCASE(15) CSA_WCASE(16) CSA_WCASE(17) CSA_WCASE(18)
+#undef CSA_WCASE
+        default: CSA_WAIT_VM(0); break;
+    }
+}
+
+// copies of this wave for one compressed tile
+template <int NW, bool SHARED>
+__device__ __forceinline__ int mx8_comp_copies(int wave) {
+    constexpr int n = (SHARED ? 1 : 2) * Mx8Geom::NCOPY_CODES + 1;
+    return n / NW + (wave < n % NW ? 1 : 0);
+}
+
+// row of tile entry r (0..31) of compressed tile tau (CSA: kept list; HCA:
+// every candidate, clamped to the last one)
+__device__ __forceinline__ int mx8_row(bool sparse, const CSA_LDS int32_t* ssel, int base, int r,
+                                       int nval) {
+    return sparse ? ssel[base + r] : min(base + r, nval - 1);
+}
+
+template <int NW, bool SHARED>
+__device__ __forceinline__ void mx8_issue_comp(int wave, int tau, int nval, bool sparse,
+                                               const CSA_LDS int32_t* ssel, const uint8_t* ckb,
+                                               const uint8_t* cvb, const uint8_t* ksb,
+                                               const uint8_t* vsb, CSA_LDS uint8_t* stg) {
+    using M = Mx8Geom;
+    const int lane = threadIdx.x % 64;
+    const int base = ATT_KT * tau;
+    constexpr int NT = SHARED ? 1 : 2;
+    constexpr int n = NT * M::NCOPY_CODES + 1;
+#pragma unroll
+    for (int c0 = 0; c0 < n; c0 += NW) {
+        const int c = c0 + wave;
+        if (c >= n) break;
+        if (c < NT * M::NCOPY_CODES) {
+            const int tensor = c / M::NCOPY_CODES, ins = c % M::NCOPY_CODES;
+            const int r = ins * 8 + lane / 8;
+            const uint32_t off = (uint32_t)mx8_row(sparse, ssel, base, r, nval) * M::D +
+                                 (uint32_t)(lane % 8) * 16;
+            __builtin_amdgcn_global_load_lds((tensor ? cvb : ckb) + off,
+                                             (CSA_LDS void*)(stg + tensor * M::CODE_B + ins * 1024),
+                                             16, 0, 0);
+        } else {
+            const int tensor = SHARED ? 0 : lane / 32;
+            const uint32_t off = (uint32_t)mx8_row(sparse, ssel, base, lane % 32, nval) * 4;
+            __builtin_amdgcn_global_load_lds((tensor ? vsb : ksb) + off,
+                                             (CSA_LDS void*)(stg + M::SC_OFF), 4, 0, 0);
+        }
+    }
+}
+
+// staged tile -> bf16 tile buffers (every thread of the block takes items
+// of 16 values: tensor, row r, 16-value group c)
+template <int NW, bool SHARED>
+__device__ __forceinline__ void mx8_convert(const CSA_LDS uint8_t* stg, CSA_LDS uint8_t* bk,
+                                            CSA_LDS uint8_t* bv) {
+    using M = Mx8Geom;
+    using G = TileGeom<128>;
+    constexpr int NTEN = SHARED ? 1 : 2;
+    constexpr int ITEMS = NTEN * ATT_KT * 8;
+#pragma unroll 1
+    for (int it = threadIdx.x; it < ITEMS; it += NW * 64) {
+        const int tensor = it / (ATT_KT * 8), r = (it / 8) % ATT_KT, c = it % 8;
+        const u32x4 w = *reinterpret_cast<const CSA_LDS u32x4*>(stg + tensor * M::CODE_B +
+                                                                r * M::D + c * 16);
+        // the scale rows of the tile follow each other (4 bytes per row);
+        // in SHARED mode lanes 32-63 of the scale copy held K rows again
+        const uint32_t sb = stg[M::SC_OFF + (SHARED ? 0 : tensor * 128) + r * 4 + c / 2];
+        const float sc = sb ? __uint_as_float(sb << 23) : 0x1p-127f;
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[2 * j] = __builtin_bit_cast(uint32_t,
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], sc, false));
+            o[2 * j + 1] = __builtin_bit_cast(uint32_t,
+                                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], sc, true));
+        }
+        CSA_LDS uint8_t* dst = (tensor ? bv : bk) + r * G::ROWB;
+        *reinterpret_cast<CSA_LDS u32x4*>(dst + slot_of<128>(r, 2 * c) * 16) =
+            u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<CSA_LDS u32x4*>(dst + slot_of<128>(r, 2 * c + 1) * 16) =
+            u32x4{o[4], o[5], o[6], o[7]};
+    }
+}
+
+template <int NW, class E, bool SHARED>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
+             const uint8_t* __restrict__ cv, const uint8_t* __restrict__ cks,
+             const uint8_t* __restrict__ cvs, const int32_t* __restrict__ topk,
+             const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
+             uint16_t* __restrict__ o, float* __restrict__ part, int64_t Tq, int64_t Nc,
+             int64_t m, int64_t W, int k, int64_t q_pos0, float scale_log2, int64_t raw_pos0,
+             int64_t raw_len, int splits) {
+    constexpr int D = 128;
+    using G = TileGeom<D>;
+    using M = Mx8Geom;
+    constexpr int NT = NW * 64;
+    constexpr int H = NW * E::HPW;
+    constexpr int KT = G::KT;
+    // distinct arrays per stage, so the compiler can tell which stage an LDS
+    // access touches
+    __shared__ __attribute__((aligned(16))) uint8_t sS0[M::BYTES], sS1[M::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sS2[M::BYTES], sS3[M::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sK0[G::BYTES], sV0[G::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sK1[G::BYTES], sV1[G::BYTES];
+    __shared__ int32_t sSel[2048];
+    __shared__ int sCnt[NW];
+
+    const int i = (int)blockIdx.x;
+    const int split = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int64_t t = q_pos0 + i;
+    const bool sparse = topk != nullptr;
+    const int nc_t = (int)n_candidates(t, m, W);
+    const int64_t w0 = t - W + 1 < 0 ? 0 : t - W + 1;
+    const int nwin = (int)(t - w0 + 1), raw_first = (int)(w0 - raw_pos0);
+
+    int nval = nc_t;
+    if (sparse) {
+        const int nsel = min(k, nc_t);
+        const int32_t* sel = topk + (b * Tq + i) * k;
+        nval = 0;
+        int jn = tid < nsel ? sel[tid] : -1;
+        for (int x0 = 0; x0 < nsel; x0 += NT) {
+            const int j = jn;
+            jn = x0 + NT + tid < nsel ? sel[x0 + NT + tid] : -1;
+            const bool ok = j >= 0 && j < nc_t;
+            const uint64_t bal = __ballot(ok);
+            if (lane == 0) sCnt[wave] = __popcll(bal);
+            __syncthreads();
+            int before = nval, total = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int c = sCnt[w];
+                before += w < wave ? c : 0;
+                total += c;
+            }
+            if (ok) sSel[before + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+            nval += total;
+            __syncthreads();
+        }
+        for (int x = nval + tid; x < ((nval + KT - 1) & ~(KT - 1)); x += NT) sSel[x] = 0;
+        __syncthreads();
+    }
+    const CSA_LDS int32_t* ssel = (const CSA_LDS int32_t*)sSel;
+
+    const int ct = (nval + KT - 1) / KT;
+    const int ntile = ct + (nwin + KT - 1) / KT;
+    const int tps = (ntile + splits - 1) / splits;
+    const int tau0 = split * tps;
+    const int tau1 = min(ntile, tau0 + tps);
+
+    const uint8_t* ckb = ck + b * Nc * D;
+    const uint8_t* cvb = cv + b * Nc * D;
+    const uint8_t* ksb = cks + b * Nc * (D / 32);
+    const uint8_t* vsb = cvs + b * Nc * (D / 32);
+    const char* rkb = reinterpret_cast<const char*>(rk + b * raw_len * D);
+    const char* rvb = reinterpret_cast<const char*>(rv + b * raw_len * D);
+    const int percomp = mx8_comp_copies<NW, SHARED>(wave);
+
+    E eng;
+    eng.init(q + ((b * Tq + i) * H + wave * E::HPW) * D);
+
+    // staging copies of compressed tile tau (nothing for other tiles)
+    auto stage = [&](int tau, uint8_t* stg) {
+        if (tau < tau1 && tau < ct)
+            mx8_issue_comp<NW, SHARED>(wave, tau, nval, sparse, ssel, ckb, cvb, ksb, vsb,
+                                       (CSA_LDS uint8_t*)stg);
+    };
+    // bf16 tile tau: convert its staging slot, or copy its window rows
+    auto fill = [&](int tau, const uint8_t* stg, uint8_t* bk, uint8_t* bv) {
+        if (tau >= tau1) return;
+        if (tau < ct)
+            mx8_convert<NW, SHARED>((const CSA_LDS uint8_t*)stg, (CSA_LDS uint8_t*)bk,
+                                    (CSA_LDS uint8_t*)bv);
+        else
+            issue_tile<NW, D, SHARED>(wave, tau, ct, nval, nwin, raw_first, false, ssel, nullptr,
+                                      nullptr, rkb, rvb, (CSA_LDS uint8_t*)bk,
+                                      (CSA_LDS uint8_t*)bv);
+    };
+    // one step: wait, barrier (stage tau's bf16 tile complete everywhere; the
+    // other bf16 buffer and staging slot of tau - 1 free), fill tile tau + 1,
+    // stage tile tau + 3, compute tile tau
+    auto step = [&](int tau, const uint8_t* stg1, uint8_t* stg3, uint8_t* ck_, uint8_t* cv_,
+                    uint8_t* nk_, uint8_t* nv_) {
+        // still in flight: the staging of tile tau + 2, issued after the
+        // copies that tile tau and the conversion of tau + 1 need
+        wait_vm_leaving(tau + 2 < tau1 && tau + 2 < ct ? percomp : 0);
+        lds_barrier();
+        fill(tau + 1, stg1, nk_, nv_);
+        stage(tau + 3, stg3);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
+        eng.tile((const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)(SHARED ? ck_ : cv_), nvalid,
+                 scale_log2);
+    };
+
+    // prologue: stage tau0 .. tau0 + 2, then tile tau0's bf16 buffer
+    stage(tau0, sS0);
+    stage(tau0 + 1, sS1);
+    stage(tau0 + 2, sS2);
+    if (tau0 < tau1 && tau0 < ct) {
+        wait_vm_leaving((tau0 + 1 < tau1 && tau0 + 1 < ct ? percomp : 0) +
+                        (tau0 + 2 < tau1 && tau0 + 2 < ct ? percomp : 0));
+        lds_barrier();
+    }
+    fill(tau0, sS0, sK0, sV0);
+    for (int tau = tau0; tau < tau1; tau += 4) {
+        step(tau, sS1, sS3, sK0, sV0, sK1, sV1);
+        if (tau + 1 >= tau1) break;
+        step(tau + 1, sS2, sS0, sK1, sV1, sK0, sV0);
+        if (tau + 2 >= tau1) break;
+        step(tau + 2, sS3, sS1, sK0, sV0, sK1, sV1);
+        if (tau + 3 >= tau1) break;
+        step(tau + 3, sS0, sS2, sK1, sV1, sK0, sV0);
+    }
+    if (splits == 1)
+        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, scale_log2);
+    else
+        eng.store(nullptr, part + (((b * Tq + i) * splits + split) * H + wave * E::HPW) * (D + 2),
+                  scale_log2);
+}
+
 // Log-sum-exp merge of the split partials.  Grid (query, sequence, head
 // group of 8); D/4 threads per head, 4 dims each.  The threads of a head
 // read the splits' maxima and sums in parallel (at most 64 splits) and
@@ -684,6 +939,49 @@ hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int
         }
     }
 #undef CSA_ATT_CASE
+    return hipGetLastError();
+}
+
+template <int NW>
+static void launch_mx8_nw(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, int64_t m,
+                          int64_t W, int k, int64_t q_pos0, float scale, const void* q,
+                          const uint8_t* ck, const uint8_t* cv, const uint8_t* cks,
+                          const uint8_t* cvs, const int32_t* topk, const void* rk, const void* rv,
+                          int64_t raw_pos0, int64_t raw_len, void* o, void* ws, hipStream_t st) {
+    constexpr int D = 128;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const bool shared = ck == cv && cks == cvs && rk == rv;
+    auto kern = shared ? k_attend_mx8<NW, Heads32<D>, true> : k_attend_mx8<NW, Heads32<D>, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64),
+                       0, st, (const uint16_t*)q, ck, cv, cks, cvs, topk, (const uint16_t*)rk,
+                       (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq, Nc, m, W, k, q_pos0,
+                       scale_log2, raw_pos0, raw_len, p.splits);
+    if (p.splits > 1) {
+        const int H = NW * 32;
+        hipLaunchKernelGGL(k_attend_combine<uint16_t>,
+                           dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
+                           st, (const float*)ws, (uint16_t*)o, Tq, H, D, p.splits);
+    }
+}
+
+hipError_t launch_attend_mx8(const AttendPlan& p, int64_t B, int64_t Tq, int64_t H, int64_t Nc,
+                             int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                             const void* q, const uint8_t* ck, const uint8_t* cv,
+                             const uint8_t* cks, const uint8_t* cvs, const int32_t* topk,
+                             const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
+                             void* o, void* ws, hipStream_t st) {
+    if (B == 0 || Tq == 0) return hipSuccess;
+#define CSA_MX8_CASE(NN)                                                                        \
+    launch_mx8_nw<NN>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, cks, cvs, topk, rk, \
+                      rv, raw_pos0, raw_len, o, ws, st)
+    switch (H / 32) {
+        case 1: CSA_MX8_CASE(1); break;
+        case 2: CSA_MX8_CASE(2); break;
+        case 4: CSA_MX8_CASE(4); break;
+        case 8: CSA_MX8_CASE(8); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef CSA_MX8_CASE
     return hipGetLastError();
 }
 

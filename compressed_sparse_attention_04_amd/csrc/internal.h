@@ -55,4 +55,16 @@ hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int
                          const void* cv, const int32_t* topk, const void* rk, const void* rv,
                          int64_t raw_pos0, int64_t raw_len, void* o, void* ws, hipStream_t st);
 
+// bf16 queries and window rows, compressed K/V rows as MXFP8 (E4M3 codes
+// [Nc][128] and E8M0 scales [Nc][4]); D = 128, the plan of the bf16 kernel
+hipError_t launch_attend_mx8(const AttendPlan& p, int64_t B, int64_t Tq, int64_t H, int64_t Nc,
+                             int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                             const void* q, const uint8_t* ck, const uint8_t* cv,
+                             const uint8_t* cks, const uint8_t* cvs, const int32_t* topk,
+                             const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
+                             void* o, void* ws, hipStream_t st);
+
+hipError_t launch_quant_mxfp8(int dt, const void* x, uint8_t* codes, uint8_t* scales,
+                              int64_t rows, int d, hipStream_t st);
+
 }  // namespace csa

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -223,6 +223,54 @@ csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
                       const void *q, const void *ck, const void *cv, const void *rk,
                       const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_quantize_mxfp8 -- MXFP8 (E4M3) encoding of rows, the storage of the
+ * compressed KV entries (ai-papers.net article, hybrid attention section:
+ * most KV entries are kept in FP8; the block format is the OCP Microscaling
+ * one of the FP4 indexer keys).  Per run of 32 values: scale exponent
+ * e = floor(log2 max|x|) - 8 clamped to [-127, 127] (-127 for an all-zero
+ * run), stored as the byte e + 127; each value x * 2^-e is rounded to the
+ * nearest E4M3 value (bias 7, subnormals k * 2^-9, largest 448; ties to the
+ * even code, larger magnitudes saturate to 448), bit 7 = x's sign bit.
+ *   x       [rows, d]      dt, finite values, 16-byte aligned
+ *   codes   [rows, d]      uint8, 16-byte aligned
+ *   scales  [rows, d/32]   uint8 (E8M0)
+ * Requires d % 32 == 0.  Caller-owned device memory; nothing is allocated.
+ */
+csa_status csa_quantize_mxfp8(csa_dtype dt, int64_t rows, int64_t d, const void *x,
+                              void *codes, void *scales, hipStream_t stream);
+
+/*
+ * csa_attend_mxfp8 / hca_attend_mxfp8 -- csa_attend / hca_attend (bf16) with
+ * the compressed entries stored as MXFP8 (ai-papers.net article, hybrid
+ * attention section: most KV entries in FP8).  The key and value of entry j
+ * are the exact values code * 2^(scale - 127) of csa_quantize_mxfp8 output;
+ * queries, the raw window rows and the output stay bf16, and the arithmetic
+ * is that of the bf16 path (every such value is exact in bf16).
+ *   ck, cv               [B, Nc, 128]   uint8 E4M3 codes, 16-byte aligned
+ *   ck_scales, cv_scales [B, Nc, 4]     uint8 E8M0, 4-byte aligned
+ *   q, o [B, Tq, H, 128] bf16; rk, rv [B, raw_len, 128] bf16; topk as for
+ *   csa_attend; ws of at least csa_attend_workspace / hca_attend_workspace
+ *   (CSA_BF16, same sizes) bytes.
+ * Passing the same buffers as ck and cv, ck_scales and cv_scales, and rk and
+ * rv selects the one-vector key-and-value reading (each row read once).
+ * Requires D = 128 and H in {32, 64, 128, 256}; other arguments and errors
+ * as for csa_attend / hca_attend.
+ */
+csa_status csa_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                            int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                            const void *q, const void *ck, const void *cv,
+                            const void *ck_scales, const void *cv_scales,
+                            const int32_t *topk, const void *rk, const void *rv,
+                            int64_t raw_pos0, int64_t raw_len, void *o, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+csa_status hca_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                            int64_t m, int64_t W, int64_t q_pos0, float scale,
+                            const void *q, const void *ck, const void *cv,
+                            const void *ck_scales, const void *cv_scales, const void *rk,
+                            const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

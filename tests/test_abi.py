@@ -33,14 +33,15 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared()
     assert {"hca_compress", "csa_index_topk", "csa_attend", "hca_attend",
-            "csa_quantize_mxfp4", "hca_append"} <= set(names)
+            "csa_quantize_mxfp4", "hca_append", "csa_quantize_mxfp8", "csa_attend_mxfp8",
+            "hca_attend_mxfp8"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGS), "binding and header disagree"
 
 
 def test_version(L):
-    assert L.csa_abi_version() == 2
+    assert L.csa_abi_version() == 3
 
 
 def err(L):
@@ -85,6 +86,26 @@ def test_append_rejects(L):
 def test_quantize_rejects(L):
     assert L.csa_quantize_mxfp4(1, 4, 48, P, P, P, None) == EINVAL
     assert L.csa_quantize_mxfp4(1, 4, 64, P, None, P, None) == EINVAL
+
+
+def test_mxfp8_rejects(L):
+    assert L.csa_quantize_mxfp8(1, 4, 48, P, P, P, None) == EINVAL            # d % 32
+    assert L.csa_quantize_mxfp8(1, 4, 64, P, None, P, None) == EINVAL         # null
+    assert L.csa_quantize_mxfp8(5, 4, 64, P, P, P, None) == EINVAL            # dtype
+    S = ctypes.c_void_p(0x1004)                        # 4-byte aligned scales are fine
+    def hca(D=128, H=128, cks=S, q=P):
+        return L.hca_attend_mxfp8(1, 1, H, D, 300, 4, 128, 1199, 1.0, q, P, P, cks, S, P, P,
+                                  1072, 128, P, None, 0, None)
+    assert hca(D=64) == EUNSUP and "D = 128" in err(L)
+    assert hca(H=96) == EUNSUP
+    assert hca(cks=ctypes.c_void_p(0x1002)) == EINVAL and "4-byte" in err(L)
+    assert hca(q=None) == EINVAL and "null" in err(L)
+    st = L.csa_attend_mxfp8(1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, S, S, None, P,
+                            P, 1072, 128, P, None, 0, None)
+    assert st == EINVAL and "null" in err(L)                # topk
+    st = L.csa_attend_mxfp8(1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, S, S, P, P, P,
+                            1073, 127, P, None, 0, None)
+    assert st == EINVAL and "raw rows" in err(L)
 
 
 def ws_index(L, *a):
