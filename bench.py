@@ -105,10 +105,12 @@ class Stage:
         self.name, self.fn, self.flops, self.bytes, self.peak_key = name, fn, flops, bytes_, peak_key
 
 
-def setup_prefill(dev, layers, shared_kv=False):
+def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16"):
     """CSA (and optionally HCA) prefill layers over one sequence.  shared_kv:
     one vector per entry and raw token serves as key and value (only K is
-    compressed, and the same buffers are passed as K and V)."""
+    compressed, and the same buffers are passed as K and V).  kv_fmt
+    "mxfp8": the compressed entries are encoded to MXFP8 after pooling (a
+    timed stage) and attention reads them in that form."""
     import torch
     from compressed_sparse_attention_04_amd import binding as csa
     from compressed_sparse_attention_04_amd import inputs as I
@@ -133,6 +135,20 @@ def setup_prefill(dev, layers, shared_kv=False):
                 csa.hca_compress(raw["k"], raw["gk"], m, out=ck),
                 csa.hca_compress(raw["v"], raw["gv"], m, out=cv))
         stages.append(Stage(f"compress_m{m}", compress, bytes_=cbytes, peak_key="hbm_GBps"))
+        mx = None
+        if kv_fmt == "mxfp8":
+            kc8 = torch.empty((1, w.Nc, D), dtype=torch.uint8, device=dev)
+            ks8 = torch.empty((1, w.Nc, D // 32), dtype=torch.uint8, device=dev)
+            vc8, vs8 = (kc8, ks8) if shared_kv else (torch.empty_like(kc8), torch.empty_like(ks8))
+            mx = (kc8, vc8, ks8, vs8)
+
+            def encode(ck=ck, cv=cv, mx=mx):
+                csa.csa_quantize_mxfp8(ck, codes=mx[0], scales=mx[2])
+                if not shared_kv:
+                    csa.csa_quantize_mxfp8(cv, codes=mx[1], scales=mx[3])
+
+            stages.append(Stage("encode_mxfp8", encode,
+                                bytes_=nvec * w.Nc * (D * 2 + D + D // 32), peak_key="hbm_GBps"))
         if w.kind == "csa":
             k_idx = I.draw_indexer_keys(w, device=dev)
             q_idx = I.draw_indexer_queries(w, device=dev)
@@ -154,24 +170,34 @@ def setup_prefill(dev, layers, shared_kv=False):
                                                    q_pos0=w.q_pos0, topk=topk, ws=iws),
                                 flops=2.0 * w.HI * w.dI * float(nc.sum()),
                                 peak_key="fp4_TFLOPs"))
-            stages.append(Stage("csa_attend",
-                                lambda q=q, ck=ck, cv=cv, topk=topk, raw=raw, rv=rv, o=o, w=w:
-                                csa.csa_attend(q, ck, cv, topk, raw["k"], rv, m=w.m, W=w.W,
-                                               q_pos0=w.q_pos0, raw_pos0=0, out=o),
+            if mx is None:
+                attend = lambda q=q, ck=ck, cv=cv, topk=topk, raw=raw, rv=rv, o=o, w=w: \
+                    csa.csa_attend(q, ck, cv, topk, raw["k"], rv, m=w.m, W=w.W, q_pos0=w.q_pos0,
+                                   raw_pos0=0, out=o)
+            else:
+                attend = lambda q=q, mx=mx, topk=topk, raw=raw, rv=rv, o=o, w=w: \
+                    csa.csa_attend_mxfp8(q, mx[0], mx[1], mx[2], mx[3], topk, raw["k"], rv,
+                                         m=w.m, W=w.W, q_pos0=w.q_pos0, raw_pos0=0, out=o)
+            stages.append(Stage("csa_attend", attend,
                                 flops=4.0 * H * D * float(nkeys.sum()),
                                 bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
         else:
             nkeys, nc = attend_keys(q_pos, m, W, 0)
-            stages.append(Stage("hca_attend",
-                                lambda q=q, ck=ck, cv=cv, raw=raw, rv=rv, o=o, w=w:
-                                csa.hca_attend(q, ck, cv, raw["k"], rv, m=w.m, W=w.W,
-                                               q_pos0=w.q_pos0, raw_pos0=0, out=o),
+            if mx is None:
+                attend = lambda q=q, ck=ck, cv=cv, raw=raw, rv=rv, o=o, w=w: \
+                    csa.hca_attend(q, ck, cv, raw["k"], rv, m=w.m, W=w.W, q_pos0=w.q_pos0,
+                                   raw_pos0=0, out=o)
+            else:
+                attend = lambda q=q, mx=mx, raw=raw, rv=rv, o=o, w=w: \
+                    csa.hca_attend_mxfp8(q, mx[0], mx[1], mx[2], mx[3], raw["k"], rv, m=w.m,
+                                         W=w.W, q_pos0=w.q_pos0, raw_pos0=0, out=o)
+            stages.append(Stage("hca_attend", attend,
                                 flops=4.0 * H * D * float(nkeys.sum()),
                                 bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
     return stages, tokens, notes
 
 
-def _decode_caches(w, dev, with_keys, shared_kv=False):
+def _decode_caches(w, dev, with_keys, shared_kv=False, kv_fmt="bf16"):
     """Precompress every sequence's 1M-token raw context chunk by chunk on the
     GPU; keep the last W raw rows.  Untimed.  shared_kv: K only, passed as
     both K and V."""
@@ -197,6 +223,13 @@ def _decode_caches(w, dev, with_keys, shared_kv=False):
                 if not shared_kv:
                     rv[b].copy_(x["v"][0, -w.W:])
     out = {"ck": ck, "cv": cv, "rk": rk, "rv": rv}
+    if kv_fmt == "mxfp8":
+        out["ck"], out["cks"] = csa.csa_quantize_mxfp8(ck)
+        if shared_kv:
+            out["cv"], out["cvs"] = out["ck"], out["cks"]
+        else:
+            out["cv"], out["cvs"] = csa.csa_quantize_mxfp8(cv)
+        del ck, cv
     if with_keys:
         k_idx = I.draw_indexer_keys(w, device=dev)
         kc, ks = csa.csa_quantize_mxfp4(k_idx)
@@ -206,26 +239,32 @@ def _decode_caches(w, dev, with_keys, shared_kv=False):
     return out
 
 
-def setup_decode(dev, w, min_bytes=600e6, shared_kv=False):
+def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
     import torch
     from compressed_sparse_attention_04_amd import binding as csa
     from compressed_sparse_attention_04_amd import inputs as I
 
     sparse = w.kind == "csa"
-    base = _decode_caches(w, dev, sparse, shared_kv)
+    mx8 = kv_fmt == "mxfp8"
+    base = _decode_caches(w, dev, sparse, shared_kv, kv_fmt)
     q = I.draw_queries(w, device=dev)
     t = w.q_pos0
     nkeys, nc = attend_keys([t], w.m, w.W, w.k if sparse else 0)
-    kv_bytes = float(nkeys[0]) * w.D * 2 * (1 if shared_kv else 2)
+    nwin = min(w.W, t + 1)
+    entry_bytes = (w.D + w.D // 32) if mx8 else w.D * 2
+    kv_bytes = ((float(nkeys[0]) - nwin) * entry_bytes + nwin * w.D * 2) * (1 if shared_kv else 2)
     qo_bytes = w.H * w.D * 2 * 2
     key_bytes = float(nc[0]) * (w.dI // 2 + w.dI // 32) if sparse else 0.0
     step_bytes = w.B * (kv_bytes + qo_bytes + key_bytes)
     # rotate over enough copies that the step's working set is not cached
     ncopy = max(2, int(np.ceil(min_bytes / step_bytes)) + 1)
     def clone(c):
-        d = {n: v.clone() for n, v in c.items() if not (shared_kv and n in ("cv", "rv"))}
+        d = {n: v.clone() for n, v in c.items()
+             if not (shared_kv and n in ("cv", "rv", "cvs"))}
         if shared_kv:
             d["cv"], d["rv"] = d["ck"], d["rk"]
+            if mx8:
+                d["cvs"] = d["cks"]
         return d
 
     copies = [base] + [clone(base) for _ in range(ncopy - 1)]
@@ -248,8 +287,13 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False):
 
         def attend():
             c = copies[state["i"] % ncopy]
-            csa.csa_attend(q, c["ck"], c["cv"], topk, c["rk"], c["rv"], m=w.m, W=w.W, q_pos0=t,
-                           raw_pos0=t - w.W + 1, out=o, ws=aws)
+            if mx8:
+                csa.csa_attend_mxfp8(q, c["ck"], c["cv"], c["cks"], c["cvs"], topk, c["rk"],
+                                     c["rv"], m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1,
+                                     out=o, ws=aws)
+            else:
+                csa.csa_attend(q, c["ck"], c["cv"], topk, c["rk"], c["rv"], m=w.m, W=w.W,
+                               q_pos0=t, raw_pos0=t - w.W + 1, out=o, ws=aws)
             state["i"] += 1
 
         stages.append(Stage("index_topk", index, flops=2.0 * w.HI * w.dI * float(nc[0]) * w.B,
@@ -262,8 +306,13 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False):
 
         def attend():
             c = copies[state["i"] % ncopy]
-            csa.hca_attend(q, c["ck"], c["cv"], c["rk"], c["rv"], m=w.m, W=w.W, q_pos0=t,
-                           raw_pos0=t - w.W + 1, out=o, ws=aws)
+            if mx8:
+                csa.hca_attend_mxfp8(q, c["ck"], c["cv"], c["cks"], c["cvs"], c["rk"], c["rv"],
+                                     m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1, out=o,
+                                     ws=aws)
+            else:
+                csa.hca_attend(q, c["ck"], c["cv"], c["rk"], c["rv"], m=w.m, W=w.W, q_pos0=t,
+                               raw_pos0=t - w.W + 1, out=o, ws=aws)
             state["i"] += 1
 
         stages.append(Stage("hca_attend", attend, flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
@@ -354,6 +403,10 @@ def main():
     ap.add_argument("--shared-kv", action="store_true",
                     help="one vector per compressed entry and raw token serves as key and "
                          "value (the same buffers passed as K and V); default: separate K, V")
+    ap.add_argument("--kv-format", default="bf16", choices=["bf16", "mxfp8"],
+                    help="storage of the compressed entries: bf16 (default) or MXFP8 E4M3 "
+                         "codes with a power-of-two scale per 32 values (the raw window "
+                         "stays bf16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -386,25 +439,29 @@ def main():
 
     if args.workload == "pair_prefill_128k":
         stages, tokens, notes = setup_prefill(dev, [I.PAIR_CSA_128K, I.PAIR_HCA_128K],
-                                              args.shared_kv)
+                                              args.shared_kv, args.kv_format)
         wl = {"workload": "csa_hca_layer_pair_prefill", "seq_len": 131072, "batch": 1,
               "heads": 128, "kv_heads": 1, "head_dim": 128, "m_csa": 4, "m_hca": 128,
               "top_k": 512, "indexer": "4x64 MXFP4", "window": 128}
         metric, unit = "prefill tokens/s", "tokens/s"
     elif args.workload == "csa_prefill_32k":
-        stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K], args.shared_kv)
+        stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K], args.shared_kv,
+                                              args.kv_format)
         wl = {"workload": "csa_prefill", "seq_len": 32768, "batch": 1, "heads": 128,
               "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
               "window": 128}
         metric, unit = "prefill tokens/s", "tokens/s"
     else:
         w = I.HCA_DECODE_1M if args.workload == "hca_decode_1m" else I.CSA_DECODE_1M
-        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv)
+        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv,
+                                             kv_fmt=args.kv_format)
         wl = {"workload": args.workload.replace("_1m", "") + "_1m_ctx", "context": w.T,
               "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
               "top_k": w.k if w.kind == "csa" else None, "window": w.W}
         metric, unit = "1M-ctx decode tokens/s/GPU", "tokens/s"
     wl["kv"] = "one vector as key and value" if args.shared_kv else "separate K and V"
+    wl["kv_format"] = ("compressed entries MXFP8 (E4M3), window bf16" if args.kv_format == "mxfp8"
+                       else "bf16")
 
     stream = torch.cuda.current_stream()
 
@@ -449,7 +506,8 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # (counter passes exist for the default inputs only)
-    roof["traffic"] = None if args.shared_kv else recorded_traffic(args.workload, d.name)
+    roof["traffic"] = (None if args.shared_kv or args.kv_format != "bf16"
+                       else recorded_traffic(args.workload, d.name))
     roof["kernel"] = d.name
     roof["ms_per_launch"] = stage_ms[dom]
 
