@@ -19,8 +19,9 @@
 //   online softmax in fp32 (exp2 domain) with lazy rescaling
 //   O^T += V^T P^T       (P^T straight from the S^T registers as bf16; V^T
 //                         by transposing LDS reads, ds_read_b64_tr_b16)
-// With more than one split the unnormalised (acc, max, sum) go to the
-// workspace and k_attend_combine merges them (log-sum-exp).
+// With more than one split each split's normalised output (bf16) and its
+// (max, sum) go to the workspace and k_attend_combine merges them
+// (log-sum-exp weights).
 #include "common.h"
 #include "internal.h"
 
@@ -306,39 +307,31 @@ struct Heads32 {
         pv();
     }
 
-    // oh: output rows [HPW][D] of this wave's heads (splits == 1), else pr:
-    // partial records [HPW][D + 2] (accumulators, max in the exp2 domain, sum)
-    __device__ __forceinline__ void store(uint16_t* oh, float* pr, float scale_log2) {
+    // oh: output rows [HPW][D] of this wave's heads (splits == 1), else the
+    // split's partial record: po [HPW][D] bf16, the split's own normalised
+    // output (zero for a split without keys), and pml [HPW][2] fp32, its
+    // maximum in the exp2 domain and its sum
+    __device__ __forceinline__ void store(uint16_t* oh, uint16_t* po, float* pml,
+                                          float scale_log2) {
         const int lane = threadIdx.x % 64, col = lane & 31, kb = lane >> 5;
         const float l_tot = sum_halves(l_run);
-        if (oh) {
-            const float inv = 1.f / l_tot;
-            uint16_t* op = oh + col * D;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* op = (oh ? oh : po) + col * D;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int d = 32 * dt + 8 * gg + 4 * kb;
-                    u32x2 w;
-                    w[0] = pack_bf16x2(acc[dt][4 * gg] * inv, acc[dt][4 * gg + 1] * inv);
-                    w[1] = pack_bf16x2(acc[dt][4 * gg + 2] * inv, acc[dt][4 * gg + 3] * inv);
-                    *reinterpret_cast<u32x2*>(op + d) = w;
-                }
-        } else {
-            float* p = pr + col * (D + 2);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int d = 32 * dt + 8 * gg + 4 * kb;
-                    const f32x4 w = {acc[dt][4 * gg], acc[dt][4 * gg + 1], acc[dt][4 * gg + 2],
-                                     acc[dt][4 * gg + 3]};
-                    *reinterpret_cast<f32x4*>(p + d) = w;
-                }
-            if (kb == 0) {
-                p[D] = m_run == -INFINITY ? -INFINITY : m_run * scale_log2;
-                p[D + 1] = l_tot;
+            for (int gg = 0; gg < 4; ++gg) {
+                const int d = 32 * dt + 8 * gg + 4 * kb;
+                const float a0 = acc[dt][4 * gg] * inv, a1 = acc[dt][4 * gg + 1] * inv;
+                const float a2 = acc[dt][4 * gg + 2] * inv, a3 = acc[dt][4 * gg + 3] * inv;
+                u32x2 w;
+                w[0] = pack_bf16x2(a0, a1);
+                w[1] = pack_bf16x2(a2, a3);
+                *reinterpret_cast<u32x2*>(op + d) = w;
             }
+        if (!oh && kb == 0) {
+            pml[2 * col] = m_run == -INFINITY ? -INFINITY : m_run * scale_log2;
+            pml[2 * col + 1] = l_tot;
         }
     }
 };
@@ -466,11 +459,15 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         if (tau + 3 >= tau1) break;
         step(tau + 3, sK3, sV3, sK2, sV2);
     }
-    if (splits == 1)
-        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, scale_log2);
-    else
-        eng.store(nullptr, part + (((b * Tq + i) * splits + split) * H + wave * E::HPW) * (D + 2),
+    if (splits == 1) {
+        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, nullptr, scale_log2);
+    } else {
+        const int64_t rec = ((b * Tq + i) * splits + split) * H + wave * E::HPW;
+        const int64_t nrec = (int64_t)gridDim.x * gridDim.y * gridDim.z * H;
+        uint16_t* po = reinterpret_cast<uint16_t*>(part);
+        eng.store(nullptr, po + rec * D, reinterpret_cast<float*>(po + nrec * D) + rec * 2,
                   scale_log2);
+    }
 }
 
 // ---- compressed entries stored as MXFP8 -------------------------------------
@@ -721,11 +718,15 @@ k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
         if (tau + 3 >= tau1) break;
         step(tau + 3, sS0, sS2, sK1, sV1, sK0, sV0);
     }
-    if (splits == 1)
-        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, scale_log2);
-    else
-        eng.store(nullptr, part + (((b * Tq + i) * splits + split) * H + wave * E::HPW) * (D + 2),
+    if (splits == 1) {
+        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, nullptr, scale_log2);
+    } else {
+        const int64_t rec = ((b * Tq + i) * splits + split) * H + wave * E::HPW;
+        const int64_t nrec = (int64_t)gridDim.x * gridDim.y * gridDim.z * H;
+        uint16_t* po = reinterpret_cast<uint16_t*>(part);
+        eng.store(nullptr, po + rec * D, reinterpret_cast<float*>(po + nrec * D) + rec * 2,
                   scale_log2);
+    }
 }
 
 // Log-sum-exp merge of the split partials.  Grid (query, sequence, head
@@ -737,17 +738,15 @@ constexpr int CMB_MAXS = 64;
 
 template <typename TO>
 __global__ void __launch_bounds__(256)
-k_attend_combine(const float* __restrict__ part, TO* __restrict__ o, int64_t Tq, int H, int D,
-                 int splits) {
+k_attend_combine(const uint16_t* __restrict__ po, const float* __restrict__ pml,
+                 TO* __restrict__ o, int64_t Tq, int H, int D, int splits) {
     __shared__ float sw[8][CMB_MAXS];
-    __shared__ float sl[8];
     const int64_t i = blockIdx.x, b = blockIdx.y;
     const int per_head = D / 4;                     // 32 or 16: a power of two <= 32
     const int hh = threadIdx.x / per_head, t = threadIdx.x % per_head;
     const int h = blockIdx.z * 8 + hh;
     const bool live = threadIdx.x < 8 * per_head && h < H;
-    const int64_t sstride = (int64_t)H * (D + 2);
-    const float* base = part + ((b * Tq + i) * splits * H + (live ? h : 0)) * (int64_t)(D + 2);
+    const int64_t rec0 = (b * Tq + i) * splits * (int64_t)H + (live ? h : 0);
     // maxima and sums of the splits t, t + per_head, ...
     float ms[CMB_MAXS / 16], ls[CMB_MAXS / 16];
     float M = -INFINITY;
@@ -755,47 +754,57 @@ k_attend_combine(const float* __restrict__ part, TO* __restrict__ o, int64_t Tq,
     for (int x = 0; x < CMB_MAXS / 16; ++x) {
         const int sp = t + x * per_head;
         const bool ok = live && sp < splits;
-        ms[x] = ok ? base[sp * sstride + D] : -INFINITY;
-        ls[x] = ok ? base[sp * sstride + D + 1] : 0.f;
+        const float* r = pml + (rec0 + (int64_t)sp * H) * 2;
+        ms[x] = ok ? r[0] : -INFINITY;
+        ls[x] = ok ? r[1] : 0.f;
         M = fmaxf(M, ms[x]);
     }
     for (int off = per_head / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    // weight of split s: 2^(m_s - M) l_s / sum over the splits of the same
+    float wl[CMB_MAXS / 16];
     float L = 0.f;
 #pragma unroll
     for (int x = 0; x < CMB_MAXS / 16; ++x) {
-        const int sp = t + x * per_head;
-        const float w = ms[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[x] - M);
-        L += ls[x] * w;
-        if (live && sp < splits) sw[hh][sp] = w;
+        wl[x] = ms[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[x] - M) * ls[x];
+        L += wl[x];
     }
     for (int off = per_head / 2; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-    if (live && t == 0) sl[hh] = L;
+    const float invL = 1.f / L;
+#pragma unroll
+    for (int x = 0; x < CMB_MAXS / 16; ++x) {
+        const int sp = t + x * per_head;
+        if (live && sp < splits) sw[hh][sp] = wl[x] * invL;
+    }
     __syncthreads();
     if (!live) return;
     const int d0 = t * 4;
+    const uint16_t* base = po + rec0 * D + d0;
+    const int64_t sstride = (int64_t)H * D;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     constexpr int U = 8;
     for (int s0 = 0; s0 < splits; s0 += U) {
-        f32x4 v[U];
+        u32x2 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = s0 + u < splits ? *reinterpret_cast<const f32x4*>(base + (s0 + u) * sstride + d0)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            v[u] = s0 + u < splits ? *reinterpret_cast<const u32x2*>(base + (s0 + u) * sstride)
+                                   : u32x2{0u, 0u};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float w = s0 + u < splits ? sw[hh][s0 + u] : 0.f;
-            a[0] += v[u][0] * w; a[1] += v[u][1] * w; a[2] += v[u][2] * w; a[3] += v[u][3] * w;
+            a[0] += bf16_bits_to_f32(v[u][0] & 0xffffu) * w;
+            a[1] += bf16_bits_to_f32(v[u][0] >> 16) * w;
+            a[2] += bf16_bits_to_f32(v[u][1] & 0xffffu) * w;
+            a[3] += bf16_bits_to_f32(v[u][1] >> 16) * w;
         }
     }
-    const float inv = 1.f / sl[hh];
     TO* op = o + ((b * Tq + i) * H + h) * (int64_t)D + d0;
     if constexpr (sizeof(TO) == 2) {
         u32x2 w;
-        w[0] = f32_to_bf16_bits(a[0] * inv) | (f32_to_bf16_bits(a[1] * inv) << 16);
-        w[1] = f32_to_bf16_bits(a[2] * inv) | (f32_to_bf16_bits(a[3] * inv) << 16);
+        w[0] = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+        w[1] = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
         *reinterpret_cast<u32x2*>(op) = w;
     } else {
-        f32x4 w = {a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv};
+        f32x4 w = {a[0], a[1], a[2], a[3]};
         *reinterpret_cast<f32x4*>(op) = w;
     }
 }
@@ -874,7 +883,8 @@ AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int6
             if (p.splits < 1) p.splits = 1;
         }
     }
-    p.ws_bytes = p.splits > 1 ? (size_t)(B * Tq * p.splits * H * (D + 2)) * sizeof(float) : 0;
+    // per split and head: the normalised output in bf16, maximum and sum in fp32
+    p.ws_bytes = p.splits > 1 ? (size_t)(B * Tq * p.splits * H) * (D * 2 + 8) : 0;
     return p;
 }
 
@@ -895,9 +905,11 @@ static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, 
                        Nc, m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {
         const int H = NW * E::HPW;
+        const uint16_t* po = (const uint16_t*)ws;
+        const float* pml = (const float*)(po + B * Tq * p.splits * H * D);
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,
                            dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
-                           st, (const float*)ws, (uint16_t*)o, Tq, H, D, p.splits);
+                           st, po, pml, (uint16_t*)o, Tq, H, D, p.splits);
     }
 }
 
@@ -958,9 +970,11 @@ static void launch_mx8_nw(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc
                        scale_log2, raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {
         const int H = NW * 32;
+        const uint16_t* po = (const uint16_t*)ws;
+        const float* pml = (const float*)(po + B * Tq * p.splits * H * D);
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,
                            dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
-                           st, (const float*)ws, (uint16_t*)o, Tq, H, D, p.splits);
+                           st, po, pml, (uint16_t*)o, Tq, H, D, p.splits);
     }
 }
 
