@@ -21,6 +21,19 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 _sz = ctypes.c_size_t
 
+CSA_LAYER_CSA, CSA_LAYER_HCA = 0, 1
+
+
+class LayerDesc(ctypes.Structure):
+    """csa_layer_desc: one layer of a stack (kind, m, Nc and device pointers)."""
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("m", ctypes.c_int64), ("Nc", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("ck", ctypes.c_void_p), ("cv", ctypes.c_void_p),
+                ("rk", ctypes.c_void_p), ("rv", ctypes.c_void_p), ("q_idx", ctypes.c_void_p),
+                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("topk", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
 _SIGS = {
     "csa_abi_version": ([], ctypes.c_int),
     "csa_last_error": ([], ctypes.c_char_p),
@@ -36,6 +49,11 @@ _SIGS = {
     "hca_attend_workspace": ([ctypes.c_int] + [_i64] * 8 + [ctypes.POINTER(_sz)], ctypes.c_int),
     "hca_attend": ([ctypes.c_int] + [_i64] * 8 + [ctypes.c_float] + [_p] * 5 + [_i64, _i64]
                    + [_p, _p, _sz, _p], ctypes.c_int),
+    "csa_layer_schedule": ([_i64, _p], ctypes.c_int),
+    "csa_stack_workspace": ([ctypes.c_int, _i64, _p] + [_i64] * 9 + [ctypes.POINTER(_sz)],
+                            ctypes.c_int),
+    "csa_stack_attend": ([ctypes.c_int, _i64, _p] + [_i64] * 9 + [ctypes.c_float, _i64, _i64, _p,
+                                                                   _sz, _p], ctypes.c_int),
     "csa_quantize_mxfp8": ([ctypes.c_int, _i64, _i64, _p, _p, _p, _p], ctypes.c_int),
     "csa_attend_mxfp8": ([_i64] * 9 + [ctypes.c_float] + [_p] * 8 + [_i64, _i64]
                          + [_p, _p, _sz, _p], ctypes.c_int),
@@ -260,3 +278,45 @@ def hca_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, rk, rv, *, m: int, W: int,
           _ptr(ck_scales), _ptr(cv_scales), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out),
           _ptr(ws), wsb, _stream(q, stream))
     return out
+
+
+def csa_layer_schedule(n_layers: int) -> list:
+    """Layer kinds of an n-layer stack (CSA_LAYER_CSA / CSA_LAYER_HCA)."""
+    kinds = (ctypes.c_int32 * max(1, n_layers))()
+    _call("csa_layer_schedule", n_layers, ctypes.cast(kinds, ctypes.c_void_p))
+    return list(kinds)[:n_layers]
+
+
+def _layer_array(layers):
+    """layers: dicts with kind, m and the layer's tensors (q, ck, cv, rk, rv, o;
+    CSA also q_idx, k_codes, k_scales, topk)."""
+    arr = (LayerDesc * max(1, len(layers)))()
+    for i, L in enumerate(layers):
+        d = arr[i]
+        d.kind, d.m, d.Nc = int(L["kind"]), int(L["m"]), int(L["ck"].shape[1])
+        for f in ("q", "ck", "cv", "rk", "rv", "q_idx", "k_codes", "k_scales", "topk", "o"):
+            setattr(d, f, _ptr(L.get(f)))
+    return arr
+
+
+def csa_stack_workspace(dtype: int, layers, B, Tq, H, D, HI, dI, W, k, q_pos0) -> int:
+    n = _sz(0)
+    arr = _layer_array(layers)
+    _call("csa_stack_workspace", dtype, len(layers), ctypes.cast(arr, ctypes.c_void_p), B, Tq, H,
+          D, HI, dI, W, k, q_pos0, ctypes.byref(n))
+    return n.value
+
+
+def csa_stack_attend(layers, *, W: int, k: int, q_pos0: int, raw_pos0: int, scale: float = 1.0,
+                     HI: int = 4, dI: int = 64, ws=None, stream=None):
+    """Run every layer of the stack in order (see csa_stack_attend in csa.h);
+    each layer's output goes to its "o" tensor (and a CSA layer's selection
+    to its "topk")."""
+    q = layers[0]["q"]
+    B, Tq, H, D = q.shape
+    raw_len = layers[0]["rk"].shape[1]
+    arr = _layer_array(layers)
+    nbytes = csa_stack_workspace(_dt(q), layers, B, Tq, H, D, HI, dI, W, k, q_pos0)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _call("csa_stack_attend", _dt(q), len(layers), ctypes.cast(arr, ctypes.c_void_p), B, Tq, H, D,
+          HI, dI, W, k, q_pos0, scale, raw_pos0, raw_len, _ptr(ws), wsb, _stream(q, stream))

@@ -181,11 +181,12 @@ csa_status csa_index_topk_workspace(int64_t B, int64_t Tq, int64_t HI, int64_t d
     return ok();
 }
 
-csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
-                          int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
-                          const void* q_idx, const uint8_t* k_codes, const uint8_t* k_scales,
-                          int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
-    const char* fn = "csa_index_topk";
+// run == false: every check of the entry point, no launch
+static csa_status index_topk_do(bool run, const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
+                                int64_t HI, int64_t dI, int64_t Nc, int64_t m, int64_t W,
+                                int64_t k, int64_t q_pos0, const void* q_idx,
+                                const uint8_t* k_codes, const uint8_t* k_scales, int32_t* topk,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
     if (csa_status s = check_dtype(dt, fn)) return s;
     if (csa_status s = index_args(fn, B, Tq, HI, dI, Nc, m, W, k, q_pos0)) return s;
     CHECK(q_idx && k_codes && k_scales && topk, CSA_EINVAL, "%s: null pointer", fn);
@@ -194,9 +195,18 @@ csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64
     csa::IndexPlan p = csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0);
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    if (!run) return CSA_OK;
     return launched(csa::launch_index_topk((int)dt, p, B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k,
                                            q_pos0, q_idx, k_codes, k_scales, topk, ws, stream),
                     fn);
+}
+
+csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                          int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                          const void* q_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                          int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return index_topk_do(true, "csa_index_topk", dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx,
+                         k_codes, k_scales, topk, ws, ws_bytes, stream);
 }
 
 static csa_status attend_shape(const char* fn, csa_dtype dt, int64_t B, int64_t Tq, int64_t H,
@@ -238,12 +248,13 @@ csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, 
     return ok();
 }
 
-csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
-                      int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
-                      const void* q, const void* ck, const void* cv, const int32_t* topk,
-                      const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
-                      void* o, void* ws, size_t ws_bytes, hipStream_t stream) {
-    const char* fn = "csa_attend";
+static csa_status csa_attend_do(bool run, const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
+                                int64_t H, int64_t D, int64_t Nc, int64_t m, int64_t W,
+                                int64_t k, int64_t q_pos0, float scale, const void* q,
+                                const void* ck, const void* cv, const int32_t* topk,
+                                const void* rk, const void* rv, int64_t raw_pos0,
+                                int64_t raw_len, void* o, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
     if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
     CHECK(k >= 1 && k <= 2048, CSA_EINVAL, "%s: k must be in [1, 2048]", fn);
     CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
@@ -255,9 +266,19 @@ csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
     csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, k + W);
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    if (!run) return CSA_OK;
     return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck,
                                        cv, topk, rk, rv, raw_pos0, raw_len, o, ws, stream),
                     fn);
+}
+
+csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                      int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                      const void* q, const void* ck, const void* cv, const int32_t* topk,
+                      const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
+                      void* o, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return csa_attend_do(true, "csa_attend", dt, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck,
+                         cv, topk, rk, rv, raw_pos0, raw_len, o, ws, ws_bytes, stream);
 }
 
 static int64_t hca_max_keys(int64_t Tq, int64_t m, int64_t W, int64_t q_pos0) {
@@ -275,12 +296,12 @@ csa_status hca_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, 
     return ok();
 }
 
-csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
-                      int64_t m, int64_t W, int64_t q_pos0, float scale, const void* q,
-                      const void* ck, const void* cv, const void* rk, const void* rv,
-                      int64_t raw_pos0, int64_t raw_len, void* o, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
-    const char* fn = "hca_attend";
+static csa_status hca_attend_do(bool run, const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
+                                int64_t H, int64_t D, int64_t Nc, int64_t m, int64_t W,
+                                int64_t q_pos0, float scale, const void* q, const void* ck,
+                                const void* cv, const void* rk, const void* rv,
+                                int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
     if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
     CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
     if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
@@ -291,9 +312,121 @@ csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
     csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0));
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    if (!run) return CSA_OK;
     return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, 0, q_pos0, scale, q, ck,
                                        cv, nullptr, rk, rv, raw_pos0, raw_len, o, ws, stream),
                     fn);
+}
+
+csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                      int64_t m, int64_t W, int64_t q_pos0, float scale, const void* q,
+                      const void* ck, const void* cv, const void* rk, const void* rv,
+                      int64_t raw_pos0, int64_t raw_len, void* o, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    return hca_attend_do(true, "hca_attend", dt, B, Tq, H, D, Nc, m, W, q_pos0, scale, q, ck, cv,
+                         rk, rv, raw_pos0, raw_len, o, ws, ws_bytes, stream);
+}
+
+// ---- a stack of layers ------------------------------------------------------
+
+csa_status csa_layer_schedule(int64_t n_layers, int32_t* kinds) {
+    const char* fn = "csa_layer_schedule";
+    CHECK(n_layers >= 0 && n_layers <= 4096, CSA_EINVAL, "%s: n_layers must be in [0, 4096]", fn);
+    CHECK(kinds || n_layers == 0, CSA_EINVAL, "%s: null pointer", fn);
+    for (int64_t l = 0; l < n_layers; ++l)
+        kinds[l] = l < 2 ? CSA_LAYER_HCA : (l % 2 == 0 ? CSA_LAYER_CSA : CSA_LAYER_HCA);
+    return ok();
+}
+
+// workspace of one layer (the stack reuses one buffer, layer after layer)
+static size_t layer_ws(csa_dtype dt, const csa_layer_desc& L, int64_t B, int64_t Tq, int64_t H,
+                       int64_t D, int64_t HI, int64_t dI, int64_t W, int64_t k, int64_t q_pos0) {
+    if (L.kind == CSA_LAYER_HCA)
+        return csa::plan_attend((int)dt, B, Tq, H, D, hca_max_keys(Tq, L.m, W, q_pos0)).ws_bytes;
+    const size_t a = csa::plan_attend((int)dt, B, Tq, H, D, k + W).ws_bytes;
+    const size_t i = csa::plan_index(B, Tq, (int)HI, (int)dI, L.Nc, L.m, W, (int)k, q_pos0).ws_bytes;
+    return a > i ? a : i;
+}
+
+static csa_status stack_args(const char* fn, csa_dtype dt, int64_t n_layers,
+                             const csa_layer_desc* layers, int64_t B, int64_t Tq, int64_t H,
+                             int64_t D, int64_t HI, int64_t dI, int64_t W, int64_t k,
+                             int64_t q_pos0) {
+    if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
+    CHECK(n_layers >= 0 && n_layers <= 4096, CSA_EINVAL, "%s: n_layers must be in [0, 4096]", fn);
+    CHECK(layers || n_layers == 0, CSA_EINVAL, "%s: null pointer", fn);
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const csa_layer_desc& L = layers[l];
+        CHECK(L.kind == CSA_LAYER_CSA || L.kind == CSA_LAYER_HCA, CSA_EINVAL,
+              "%s: layer %lld: unknown kind %d", fn, (long long)l, (int)L.kind);
+        csa_status s = L.kind == CSA_LAYER_CSA
+                           ? index_args(fn, B, Tq, HI, dI, L.Nc, L.m, W, k, q_pos0)
+                           : check_positions(fn, Tq, L.Nc, L.m, W, q_pos0, 0, -1);
+        if (s != CSA_OK) {
+            char inner[512];
+            snprintf(inner, sizeof(inner), "%s", g_err);
+            return fail(s, "layer %lld: %s", (long long)l, inner);
+        }
+    }
+    return CSA_OK;
+}
+
+csa_status csa_stack_workspace(csa_dtype dt, int64_t n_layers, const csa_layer_desc* layers,
+                               int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t HI,
+                               int64_t dI, int64_t W, int64_t k, int64_t q_pos0, size_t* bytes) {
+    const char* fn = "csa_stack_workspace";
+    CHECK(bytes, CSA_EINVAL, "%s: null pointer", fn);
+    if (csa_status s = stack_args(fn, dt, n_layers, layers, B, Tq, H, D, HI, dI, W, k, q_pos0))
+        return s;
+    size_t need = 0;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const size_t n = layer_ws(dt, layers[l], B, Tq, H, D, HI, dI, W, k, q_pos0);
+        need = n > need ? n : need;
+    }
+    *bytes = need;
+    return ok();
+}
+
+// every layer is checked before the first launch
+static csa_status stack_layer(bool run, const char* fn, int64_t l, csa_dtype dt,
+                              const csa_layer_desc& L, int64_t B, int64_t Tq, int64_t H,
+                              int64_t D, int64_t HI, int64_t dI, int64_t W, int64_t k,
+                              int64_t q_pos0, float scale, int64_t raw_pos0, int64_t raw_len,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+    csa_status s;
+    if (L.kind == CSA_LAYER_CSA) {
+        s = index_topk_do(run, "csa_index_topk", dt, B, Tq, HI, dI, L.Nc, L.m, W, k, q_pos0,
+                          L.q_idx, L.k_codes, L.k_scales, L.topk, ws, ws_bytes, stream);
+        if (s == CSA_OK)
+            s = csa_attend_do(run, "csa_attend", dt, B, Tq, H, D, L.Nc, L.m, W, k, q_pos0, scale,
+                              L.q, L.ck, L.cv, L.topk, L.rk, L.rv, raw_pos0, raw_len, L.o, ws,
+                              ws_bytes, stream);
+    } else {
+        s = hca_attend_do(run, "hca_attend", dt, B, Tq, H, D, L.Nc, L.m, W, q_pos0, scale, L.q,
+                          L.ck, L.cv, L.rk, L.rv, raw_pos0, raw_len, L.o, ws, ws_bytes, stream);
+    }
+    if (s != CSA_OK) {
+        char inner[512];
+        snprintf(inner, sizeof(inner), "%s", g_err);
+        return fail(s, "%s: layer %lld: %s", fn, (long long)l, inner);
+    }
+    return CSA_OK;
+}
+
+csa_status csa_stack_attend(csa_dtype dt, int64_t n_layers, const csa_layer_desc* layers,
+                            int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t HI, int64_t dI,
+                            int64_t W, int64_t k, int64_t q_pos0, float scale, int64_t raw_pos0,
+                            int64_t raw_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "csa_stack_attend";
+    if (csa_status s = stack_args(fn, dt, n_layers, layers, B, Tq, H, D, HI, dI, W, k, q_pos0))
+        return s;
+    for (int pass = 0; pass < 2; ++pass)
+        for (int64_t l = 0; l < n_layers; ++l)
+            if (csa_status s = stack_layer(pass == 1, fn, l, dt, layers[l], B, Tq, H, D, HI, dI,
+                                           W, k, q_pos0, scale, raw_pos0, raw_len, ws, ws_bytes,
+                                           stream))
+                return s;
+    return ok();
 }
 
 csa_status csa_quantize_mxfp8(csa_dtype dt, int64_t rows, int64_t d, const void* x, void* codes,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -271,6 +271,56 @@ csa_status hca_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t
                             const void *ck_scales, const void *cv_scales, const void *rk,
                             const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * A stack of attention layers (hazakura.dev note, CSA/HCA bullets: HCA in
+ * the first two layers of V4-Pro, the two kinds interleaved layer by layer;
+ * studioglobal.ai answer, CSA/HCA section: from layer 2 the even layers are
+ * CSA and the odd ones HCA; ai-papers.net article, hybrid attention section:
+ * the 61-layer stack alternates the two).  The attention core of every
+ * layer, run in order on one stream; what lies between layers (projections,
+ * norms, the rest of the model) is not part of this library, so each layer
+ * brings its own queries.
+ */
+typedef enum csa_layer_kind { CSA_LAYER_CSA = 0, CSA_LAYER_HCA = 1 } csa_layer_kind;
+
+typedef struct csa_layer_desc {
+    int32_t kind;              /* csa_layer_kind */
+    int32_t reserved;          /* 0 */
+    int64_t m;                 /* compression ratio of the layer's caches */
+    int64_t Nc;                /* compressed rows held per sequence */
+    const void *q;             /* [B, Tq, H, D] attention queries */
+    const void *ck, *cv;       /* [B, Nc, D] compressed keys and values */
+    const void *rk, *rv;       /* [B, raw_len, D] raw window rows */
+    const void *q_idx;         /* CSA: [B, Tq, HI, dI] indexer queries */
+    const uint8_t *k_codes;    /* CSA: [B, Nc, dI/2] MXFP4 indexer keys */
+    const uint8_t *k_scales;   /* CSA: [B, Nc, dI/32] their E8M0 scales */
+    int32_t *topk;             /* CSA: [B, Tq, k] kept entries (written) */
+    void *o;                   /* [B, Tq, H, D] output (written) */
+} csa_layer_desc;
+
+/* The schedule the pages describe, for n_layers layers: kinds[0] and
+ * kinds[1] are HCA; from layer 2 on, even layers are CSA and odd ones HCA
+ * (61 layers: 30 CSA, 31 HCA). */
+csa_status csa_layer_schedule(int64_t n_layers, int32_t *kinds);
+
+/*
+ * csa_stack_attend -- every layer in order: a CSA layer runs csa_index_topk
+ * (into its topk) and csa_attend, an HCA layer runs hca_attend, with the
+ * layer's own m, Nc and buffers and the shared sizes, window, q_pos0,
+ * raw_pos0, raw_len and scale.  All layers are checked before the first
+ * launch: an invalid layer returns its error (message "layer l: ...") and
+ * nothing runs.  One workspace of csa_stack_workspace bytes serves every
+ * layer in turn (stream order).  dt is the dtype of every floating-point
+ * tensor of every layer.
+ */
+csa_status csa_stack_workspace(csa_dtype dt, int64_t n_layers, const csa_layer_desc *layers,
+                               int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t HI,
+                               int64_t dI, int64_t W, int64_t k, int64_t q_pos0, size_t *bytes);
+csa_status csa_stack_attend(csa_dtype dt, int64_t n_layers, const csa_layer_desc *layers,
+                            int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t HI, int64_t dI,
+                            int64_t W, int64_t k, int64_t q_pos0, float scale, int64_t raw_pos0,
+                            int64_t raw_len, void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -34,14 +34,15 @@ def test_exports_every_declared_symbol(L):
     names = declared()
     assert {"hca_compress", "csa_index_topk", "csa_attend", "hca_attend",
             "csa_quantize_mxfp4", "hca_append", "csa_quantize_mxfp8", "csa_attend_mxfp8",
-            "hca_attend_mxfp8"} <= set(names)
+            "hca_attend_mxfp8", "csa_layer_schedule", "csa_stack_workspace",
+            "csa_stack_attend"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGS), "binding and header disagree"
 
 
 def test_version(L):
-    assert L.csa_abi_version() == 3
+    assert L.csa_abi_version() == 4
 
 
 def err(L):
@@ -106,6 +107,38 @@ def test_mxfp8_rejects(L):
     st = L.csa_attend_mxfp8(1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, S, S, P, P, P,
                             1073, 127, P, None, 0, None)
     assert st == EINVAL and "raw rows" in err(L)
+
+
+def test_layer_schedule():
+    kinds = binding.csa_layer_schedule(61)
+    H, C = binding.CSA_LAYER_HCA, binding.CSA_LAYER_CSA
+    assert kinds[:4] == [H, H, C, H] and kinds[-1] == C
+    assert kinds.count(C) == 30 and kinds.count(H) == 31
+    assert all(kinds[l] == (C if l % 2 == 0 else H) for l in range(2, 61))
+    assert binding.csa_layer_schedule(0) == []
+
+
+def test_stack_rejects_before_any_launch(L):
+    # a valid HCA layer, then a CSA layer whose cache is too short: nothing may
+    # launch (null stream, fake device pointers), and the error names layer 1
+    arr = (binding.LayerDesc * 2)()
+    for d in arr:
+        d.q = d.ck = d.cv = d.rk = d.rv = d.o = 0x1000
+        d.q_idx = d.k_codes = d.k_scales = d.topk = 0x1000
+    arr[0].kind, arr[0].m, arr[0].Nc = binding.CSA_LAYER_HCA, 128, 16
+    arr[1].kind, arr[1].m, arr[1].Nc = binding.CSA_LAYER_CSA, 4, 100
+    args = (1, 2, ctypes.cast(arr, ctypes.c_void_p), 1, 1, 128, 128, 4, 64, 128, 512, 2047)
+    n = ctypes.c_size_t(0)
+    assert L.csa_stack_workspace(*args, ctypes.byref(n)) == EINVAL
+    assert err(L).startswith("layer 1:") and "candidates" in err(L)
+    assert L.csa_stack_attend(*args, 1.0, 1920, 128, None, 0, None) == EINVAL
+    assert "layer 1" in err(L)
+    arr[1].Nc = 600                                    # valid now; layer 0 loses its window
+    assert L.csa_stack_workspace(*args, ctypes.byref(n)) == 0
+    assert L.csa_stack_attend(*args, 1.0, 1921, 128, None, 0, None) == EINVAL
+    assert "csa_stack_attend: layer 0: hca_attend" in err(L)
+    arr[0].kind = 7
+    assert L.csa_stack_workspace(*args, ctypes.byref(n)) == EINVAL and "unknown kind" in err(L)
 
 
 def ws_index(L, *a):
