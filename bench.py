@@ -320,8 +320,55 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
     return stages, w.B, {"cache_copies": ncopy, "step_bytes": step_bytes}
 
 
+def setup_stack_decode(dev, n_layers=61, B=16):
+    """Decode step of an n-layer attention stack at 1M context: the layer
+    schedule of csa_layer_schedule (HCA in layers 0-1, then CSA on even and
+    HCA on odd layers), every layer with its own caches (copies of one
+    precompressed CSA and one HCA cache set, untimed) and queries, run by one
+    csa_stack_attend call."""
+    import torch
+    from compressed_sparse_attention_04_amd import binding as csa
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    wc = I.CSA_DECODE_1M.replace(B=B)
+    wh = I.HCA_DECODE_1M.replace(B=B)
+    base = {csa.CSA_LAYER_CSA: _decode_caches(wc, dev, True),
+            csa.CSA_LAYER_HCA: _decode_caches(wh, dev, False)}
+    t = wc.q_pos0
+    kinds = csa.csa_layer_schedule(n_layers)
+    layers = []
+    step_bytes = 0.0
+    for l, kind in enumerate(kinds):
+        w = (wc if kind == csa.CSA_LAYER_CSA else wh).replace(layer=l)
+        c = base[kind] if l == kinds.index(kind) else {n: v.clone() for n, v in base[kind].items()}
+        L = {"kind": kind, "m": w.m, "q": I.draw_queries(w, device=dev), "ck": c["ck"],
+             "cv": c["cv"], "rk": c["rk"], "rv": c["rv"]}
+        L["o"] = torch.empty_like(L["q"])
+        nkeys, nc = attend_keys([t], w.m, w.W, w.k if kind == csa.CSA_LAYER_CSA else 0)
+        step_bytes += B * (float(nkeys[0]) * w.D * 2 * 2 + w.H * w.D * 2 * 2)
+        if kind == csa.CSA_LAYER_CSA:
+            L["q_idx"] = I.draw_indexer_queries(w, device=dev)
+            L["k_codes"], L["k_scales"] = c["kc"], c["ks"]
+            L["topk"] = torch.empty((B, 1, w.k), dtype=torch.int32, device=dev)
+            step_bytes += B * float(nc[0]) * (w.dI // 2 + w.dI // 32)
+        layers.append(L)
+    torch.cuda.synchronize()
+    ws = torch.empty(max(1, csa.csa_stack_workspace(1, layers, B, 1, wc.H, wc.D, wc.HI, wc.dI,
+                                                    wc.W, wc.k, t)),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        csa.csa_stack_attend(layers, W=wc.W, k=wc.k, q_pos0=t, raw_pos0=t - wc.W + 1,
+                             HI=wc.HI, dI=wc.dI, ws=ws)
+
+    stages = [Stage("stack_attend", run, bytes_=step_bytes, peak_key="hbm_GBps")]
+    ncsa = kinds.count(csa.CSA_LAYER_CSA)
+    return stages, B, {"layers": n_layers, "csa_layers": ncsa, "hca_layers": n_layers - ncsa,
+                       "step_bytes": step_bytes}
+
+
 # --------------------------------------------------------------- CPU baseline
-def cpu_baseline(name, budget_s=20.0):
+def cpu_baseline(name, budget_s=20.0, n_layers=61):
     """Time the oracle, unchanged, on a bounded sample of the same workload."""
     import torch
 
@@ -368,26 +415,39 @@ def cpu_baseline(name, budget_s=20.0):
         return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                 "sample": "; ".join(desc) + " (per-token times summed over the layers)"}
 
-    w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
-    nseq = 1
-    ws = w.replace(B=nseq)
-    t = w.q_pos0
-    ck = f64(I.draw_cache(ws, "ck", w.Nc))
-    cv = f64(I.draw_cache(ws, "cv", w.Nc))
-    rk = f64(I.draw_cache(ws, "rk", w.W))
-    rv = f64(I.draw_cache(ws, "rv", w.W))
-    q = f64(I.draw_queries(ws))
-    t0 = time.perf_counter()
-    if w.kind == "csa":
-        kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(ws)))
+    def decode_seconds(w):
+        """The oracle's decode step of one sequence of workload w."""
+        ws = w.replace(B=1)
+        t = w.q_pos0
+        ck = f64(I.draw_cache(ws, "ck", w.Nc))
+        cv = f64(I.draw_cache(ws, "cv", w.Nc))
+        rk = f64(I.draw_cache(ws, "rk", w.W))
+        rv = f64(I.draw_cache(ws, "rv", w.W))
+        q = f64(I.draw_queries(ws))
         t0 = time.perf_counter()
-        tk, _ = oracle.index_topk(f64(I.draw_indexer_queries(ws)), kc, ks, [t], w.m, w.W, w.k)
-    else:
-        tk = None
-    oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
-    el = time.perf_counter() - t0
-    return {"value": nseq / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"decode step of {nseq} sequence (caches drawn at the workload's shapes)"}
+        if w.kind == "csa":
+            kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(ws)))
+            t0 = time.perf_counter()
+            tk, _ = oracle.index_topk(f64(I.draw_indexer_queries(ws)), kc, ks, [t], w.m, w.W, w.k)
+        else:
+            tk = None
+        oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
+        return time.perf_counter() - t0
+
+    if name == "stack_decode_1m":
+        from compressed_sparse_attention_04_amd import binding as csa
+        kinds = csa.csa_layer_schedule(n_layers)
+        ncsa = kinds.count(csa.CSA_LAYER_CSA)
+        t_csa = decode_seconds(I.CSA_DECODE_1M)
+        t_hca = decode_seconds(I.HCA_DECODE_1M)
+        return {"value": 1.0 / (ncsa * t_csa + (n_layers - ncsa) * t_hca), "unit": "tokens/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"one sequence's decode step of one CSA and one HCA layer, scaled to "
+                          f"{ncsa} CSA + {n_layers - ncsa} HCA layers"}
+    w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
+    el = decode_seconds(w)
+    return {"value": 1.0 / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "decode step of 1 sequence (caches drawn at the workload's shapes)"}
 
 
 # --------------------------------------------------------------- main
@@ -398,7 +458,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=DEFAULT,
                     choices=["pair_prefill_128k", "csa_prefill_32k", "hca_decode_1m",
-                             "csa_decode_1m"])
+                             "csa_decode_1m", "stack_decode_1m"])
+    ap.add_argument("--layers", type=int, default=61,
+                    help="layers of the stack_decode_1m workload (default 61)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-kv", action="store_true",
                     help="one vector per compressed entry and raw token serves as key and "
@@ -451,6 +513,17 @@ def main():
               "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
               "window": 128}
         metric, unit = "prefill tokens/s", "tokens/s"
+    elif args.workload == "stack_decode_1m":
+        if args.kv_format != "bf16" or args.shared_kv:
+            print("stack_decode_1m runs bf16 caches with separate K and V", file=sys.stderr)
+            sys.exit(2)
+        stages, tokens, notes = setup_stack_decode(dev, args.layers)
+        wc = I.CSA_DECODE_1M
+        wl = {"workload": "attention_stack_decode_1m_ctx", "context": wc.T, "batch": tokens,
+              "layers": notes["layers"], "csa_layers": notes["csa_layers"],
+              "hca_layers": notes["hca_layers"], "heads": wc.H, "kv_heads": 1,
+              "head_dim": wc.D, "m_csa": 4, "m_hca": 128, "top_k": wc.k, "window": wc.W}
+        metric, unit = "1M-ctx decode tokens/s/GPU (attention stack)", "tokens/s"
     else:
         w = I.HCA_DECODE_1M if args.workload == "hca_decode_1m" else I.CSA_DECODE_1M
         stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv,
@@ -522,7 +595,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload)
+        cpu = cpu_baseline(args.workload, n_layers=args.layers)
 
     rec = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
            "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
