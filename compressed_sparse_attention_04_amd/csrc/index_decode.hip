@@ -11,7 +11,9 @@
 //   k_dcollect: blocks over (chunk of 4096 stored scores, row) find the
 //              threshold range from the row's histogram, write the chunk's
 //              bitmap words of the surely kept keys (above the range) and
-//              append the keys inside the range to the row's small buffer;
+//              put the keys inside the range in the chunk's own slots of the
+//              row's buffer (no global atomics: same-address device atomics
+//              from every chunk would serialise);
 //   k_dfinal : one block per row resolves the range exactly from the buffer
 //              (or, when the range holds too many keys, narrows it further
 //              by scanning the stored scores) and emits the kept indices in
@@ -29,6 +31,9 @@ constexpr int DS_CH = 4096;            // candidates per scoring block
 constexpr int DL_NT = 1024;
 constexpr int DL_CAP = 1024;           // collected keys per row
 constexpr int DL_MAXW = 8192;          // bitmap words -> 262144 candidates
+constexpr int DC_CH_ = 4096;           // stored scores per collecting block
+constexpr int DC_NB = DL_MAXW * 32 / DC_CH_;   // collecting blocks per row (64)
+constexpr int DC_SLOTS = DL_CAP / DC_NB;       // buffer slots per collecting block (16)
 
 // score rows are padded to whole 16-byte vectors
 __host__ __device__ __forceinline__ int64_t score_stride(int64_t nc) { return (nc + 3) & ~(int64_t)3; }
@@ -39,8 +44,10 @@ __global__ void k_zero_u32(uint32_t* p, int64_t n) {
 }
 
 // Workspace of the decode path (rows = B * Tq; u32 words, counts padded to
-// multiples of 4): hist [rows][1024] | cnt [rows] | thr [rows][4] | bitmap [rows][DL_MAXW] | buffer [rows][DL_CAP] (key,
-// index) | scores [rows][stride]
+// multiples of 4): hist [rows][1024] | cnt [rows][DC_NB] (keys in range per
+// collecting block) | thr [rows][4] | bitmap [rows][DL_MAXW] | buffer
+// [rows][DC_NB][DC_SLOTS] (key, index) | scores [rows][stride].  Only hist
+// starts at zero.
 struct DecodeWs {
     uint32_t* hist;
     uint32_t* cnt;
@@ -58,7 +65,7 @@ __host__ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int64_t B, int6
     w.hist = p;
     p += rows * SEL_NB;
     w.cnt = p;
-    p += pad4(rows);
+    p += rows * DC_NB;
     w.thr = reinterpret_cast<u32x4*>(p);
     p += rows * 4;
     w.bmp = p;
@@ -178,7 +185,7 @@ __device__ __forceinline__ void scan_scores(const uint32_t* __restrict__ sc, int
 }
 
 constexpr int DC_NT = 256;
-constexpr int DC_CH = 4096;            // stored scores per collecting block
+constexpr int DC_CH = DC_CH_;
 
 __global__ void __launch_bounds__(DC_NT)
 k_dcollect(DecodeWs ws, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
@@ -213,12 +220,14 @@ k_dcollect(DecodeWs ws, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
             if (blockIdx.x == 0) ws.thr[rowi] = t;   // for the final kernel
         }
     }
+    __shared__ uint32_t s_cnt;
     for (int w = tid; w < DC_CH / 32; w += DC_NT) words[w] = 0u;
+    if (tid == 0) s_cnt = 0u;
     __syncthreads();
     const uint32_t lo = s_thr[0], hi = s_thr[1];
     const bool collect = s_thr[3] <= (uint32_t)DL_CAP;
-    uint32_t* cnt = ws.cnt + rowi;
-    u32x2* cb = ws.cb + rowi * DL_CAP;
+    uint32_t* cnt = &s_cnt;
+    u32x2* cb = ws.cb + rowi * DL_CAP + blockIdx.x * DC_SLOTS;
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
         const int v = tid + x * DC_NT;
@@ -232,7 +241,7 @@ k_dcollect(DecodeWs ws, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
                 atomicOr(&words[j >> 5], 1u << (j & 31));
             } else if (key >= lo && collect) {
                 const uint32_t pos = atomicAdd(cnt, 1u);
-                if (pos < (uint32_t)DL_CAP) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
+                if (pos < (uint32_t)DC_SLOTS) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
             }
         }
     }
@@ -242,11 +251,13 @@ k_dcollect(DecodeWs ws, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
             atomicOr(&words[j >> 5], 1u << (j & 31));
         } else if (key >= lo && collect) {
             const uint32_t pos = atomicAdd(cnt, 1u);
-            if (pos < (uint32_t)DL_CAP) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
+            if (pos < (uint32_t)DC_SLOTS) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
         }
     }
     __syncthreads();
     for (int w = tid; w < (n + 31) / 32; w += DC_NT) ws.bmp[rowi * DL_MAXW + c0 / 32 + w] = words[w];
+    // more than DC_SLOTS keys here reads as an overflow in the final kernel
+    if (tid == 0) ws.cnt[rowi * DC_NB + blockIdx.x] = s_cnt;
 }
 
 struct DselSmem {
@@ -257,6 +268,7 @@ struct DselSmem {
     uint32_t lo, hi;
     int shift, above, in, mode, cnt, eqmode, need_eq;
     int scratch[DL_NT / WAVE + 1];
+    int boff[DC_NB];                // first buffer position of each collecting block
 };
 
 __global__ void __launch_bounds__(DL_NT)
@@ -282,18 +294,31 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
         S.sel[w] = ws.bmp[rowi * DL_MAXW + w];
         S.eq[w] = 0u;
     }
-    if (tid == 0) {
-        const u32x4 thr = ws.thr[rowi];
-        S.lo = thr[0];
-        S.hi = thr[1];
-        S.above = (int)thr[2];
-        S.in = (int)thr[3];
-        S.cnt = S.in <= DL_CAP ? (int)min(ws.cnt[rowi], (uint32_t)DL_CAP) : -1;
+    const int nblk = (nc + DC_CH_ - 1) / DC_CH_;
+    if (wave == 0) {
+        // per collecting block: keys in range (more than DC_SLOTS: overflow)
+        const uint32_t c = lane < nblk ? ws.cnt[rowi * DC_NB + lane] : 0u;
+        const bool over = __ballot(c > (uint32_t)DC_SLOTS) != 0ull;
+        const int incl = wave_incl_scan((int)c);
+        const int total = __shfl(incl, WAVE - 1, WAVE);
+        S.boff[lane] = incl - (int)c;
+        if (lane == 0) {
+            const u32x4 thr = ws.thr[rowi];
+            S.lo = thr[0];
+            S.hi = thr[1];
+            S.above = (int)thr[2];
+            S.in = (int)thr[3];
+            S.cnt = S.in <= DL_CAP && !over ? total : -1;
+        }
     }
     __syncthreads();
     if (S.cnt >= 0) {
-        // the collecting blocks gathered the range's keys
-        for (int p = tid; p < S.cnt; p += DL_NT) S.cb[p] = ws.cb[rowi * DL_CAP + p];
+        // the collecting blocks gathered the range's keys into their slots
+        for (int p = tid; p < nblk * DC_SLOTS; p += DL_NT) {
+            const int blk = p / DC_SLOTS, e = p % DC_SLOTS;
+            const uint32_t c = ws.cnt[rowi * DC_NB + blk];
+            if (e < (int)c) S.cb[S.boff[blk] + e] = ws.cb[rowi * DL_CAP + p];
+        }
         __syncthreads();
     } else {
         // too many keys in the level-1 range: narrow it over the stored scores
@@ -381,7 +406,7 @@ int decode_max_rows() { return DS_QT; }
 
 size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap) {
     const int64_t rows = B * Tq;
-    const int64_t words = rows * SEL_NB + pad4(rows) + rows * 4 + rows * DL_MAXW +
+    const int64_t words = rows * SEL_NB + rows * DC_NB + rows * 4 + rows * DL_MAXW +
                           rows * DL_CAP * 2 + rows * score_stride(ncap);
     return (size_t)words * sizeof(uint32_t);
 }
@@ -405,8 +430,8 @@ hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, in
     const int64_t rows = B * Tq;
     DecodeWs w = decode_ws(ws, B, rows);
     if (ncand > 0) {
-        // histograms and buffer counters start at zero
-        const int64_t nz = rows * SEL_NB + pad4(rows);
+        // histograms start at zero
+        const int64_t nz = rows * SEL_NB;
         hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st,
                            w.hist, nz);
 #define CSA_DS_CASE(TT, HH) \

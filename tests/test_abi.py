@@ -149,10 +149,10 @@ def ws_index(L, *a):
 
 def test_index_workspace_and_rejects(L):
     # decode rows over 262,112 candidates, per row: histogram (1024 words),
-    # collect counter, threshold (4 words), bitmap (8192 words), buffer of
-    # 1024 (key, index) pairs, every candidate's score (counters padded to 4)
+    # in-range counts of the 64 collecting blocks, threshold (4 words), bitmap
+    # (8192 words), buffer of 64 x 16 (key, index) pairs, every candidate's score
     st, n = ws_index(L, 16, 1, 4, 64, 262144, 4, 128, 512, (1 << 20) - 1)
-    assert st == 0 and n == (16 * (1024 + 4 + 8192 + 2048 + 262112) + 16) * 4
+    assert st == 0 and n == 16 * (1024 + 64 + 4 + 8192 + 2048 + 262112) * 4
     # the streaming path (<= 32768 candidates) needs no workspace
     st, n = ws_index(L, 1, 16, 2, 32, 256, 4, 128, 16, 1008)
     assert st == 0 and n == 0

@@ -167,6 +167,37 @@ def test_index_unrepresentative_sample(T, q_pos0, Tq, shrink):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("copies", [600, 40])
+def test_index_decode_clustered_range(copies):
+    """Decode path: the keys around the k-th score all sit in one chunk of
+    4096 candidates (copies of the row's best key, with 300 keys at twice
+    its score elsewhere), more than that chunk's buffer slots hold when
+    copies = 600: the final kernel must rescan and still keep the lowest
+    indices of the tie."""
+    say("index clustered range", copies)
+    w = I.Workload("t", "csa", seed=26, dtype="bf16", B=1, T=4 * 70000, m=4, H=128, D=128)
+    q_pos0 = 4 * 70000 - 1
+    w = w.replace(Tq=1, q_pos0=q_pos0)
+    k_idx = I.draw_indexer_keys(w)
+    q_idx = I.draw_indexer_queries(w)
+    q_pos = np.array([q_pos0])
+    kc, ks = oracle.quant_mxfp4(f64(k_idx))
+    qc, qs = oracle.quant_mxfp4(f64(q_idx))
+    sc, _ = oracle.index_scores(qc, qs, kc, ks, q_pos, w.m, w.W)
+    best = int(np.argmax(sc[0, 0, :oracle.n_cand(q_pos0, w.m, w.W)]))
+    k_idx[:, 8192:8192 + copies] = k_idx[:, best:best + 1]
+    k_idx[:, 20000:20300] = k_idx[:, best:best + 1] * 2          # exactly twice the score
+    kc, ks = oracle.quant_mxfp4(f64(k_idx))
+    ref, exact = oracle.index_topk(f64(q_idx), kc, ks, q_pos, w.m, w.W, w.k)
+    assert exact
+    gkc, gks = csa.csa_quantize_mxfp4(k_idx.to(DEV))
+    got = csa.csa_index_topk(q_idx.to(DEV), gkc, gks, m=w.m, W=w.W, k=w.k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    assert np.array_equal(g, ref)
+    assert set(range(20000, 20300)) <= set(g[0, 0].tolist())
+
+
 def test_index_one_head_small_k():
     say("index HI=1")
     w = I.Workload("t", "csa", seed=24, dtype="f32", B=2, T=6000, m=4, H=8, D=64, HI=1, dI=64,
