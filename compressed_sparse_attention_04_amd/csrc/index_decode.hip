@@ -289,21 +289,37 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
         for (int s2 = tid; s2 < k; s2 += DL_NT) out[s2] = s2 < nc ? s2 : -1;
         return;
     }
-    // the collecting blocks wrote the bits of the keys above the range
-    for (int w = tid; w < nw; w += DL_NT) {
-        S.sel[w] = ws.bmp[rowi * DL_MAXW + w];
-        S.eq[w] = 0u;
-    }
+    // every global read of this block is issued up front: the bitmap words of
+    // the keys above the range (8 per thread), one buffer slot and its
+    // block's count per thread, the threshold range
+    static_assert(DL_MAXW == 8 * DL_NT && DC_NB * DC_SLOTS == DL_NT, "one pass of loads");
     const int nblk = (nc + DC_CH_ - 1) / DC_CH_;
+    const u32x4* bw = reinterpret_cast<const u32x4*>(ws.bmp + rowi * DL_MAXW) + 2 * tid;
+    const bool wlive = 8 * tid < nw;
+    const u32x4 w0 = wlive ? bw[0] : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 w1 = wlive ? bw[1] : u32x4{0u, 0u, 0u, 0u};
+    const int sblk = tid / DC_SLOTS, sidx = tid % DC_SLOTS;
+    const bool slive = sblk < nblk;
+    const uint32_t scnt = slive ? ws.cnt[rowi * DC_NB + sblk] : 0u;
+    // (read whether or not it holds a key, so it does not wait for the count)
+    const u32x2 slot = slive ? ws.cb[rowi * DL_CAP + tid] : u32x2{0u, 0u};
+    const uint32_t c = lane < nblk ? ws.cnt[rowi * DC_NB + lane] : 0u;   // (wave 0)
+    const u32x4 thr = ws.thr[rowi];
+    // (words past nw are never read: every bitmap pass stops at nw)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        S.sel[8 * tid + x] = w0[x];
+        S.sel[8 * tid + 4 + x] = w1[x];
+        S.eq[8 * tid + x] = 0u;
+        S.eq[8 * tid + 4 + x] = 0u;
+    }
     if (wave == 0) {
         // per collecting block: keys in range (more than DC_SLOTS: overflow)
-        const uint32_t c = lane < nblk ? ws.cnt[rowi * DC_NB + lane] : 0u;
         const bool over = __ballot(c > (uint32_t)DC_SLOTS) != 0ull;
         const int incl = wave_incl_scan((int)c);
         const int total = __shfl(incl, WAVE - 1, WAVE);
         S.boff[lane] = incl - (int)c;
         if (lane == 0) {
-            const u32x4 thr = ws.thr[rowi];
             S.lo = thr[0];
             S.hi = thr[1];
             S.above = (int)thr[2];
@@ -314,11 +330,7 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
     __syncthreads();
     if (S.cnt >= 0) {
         // the collecting blocks gathered the range's keys into their slots
-        for (int p = tid; p < nblk * DC_SLOTS; p += DL_NT) {
-            const int blk = p / DC_SLOTS, e = p % DC_SLOTS;
-            const uint32_t c = ws.cnt[rowi * DC_NB + blk];
-            if (e < (int)c) S.cb[S.boff[blk] + e] = ws.cb[rowi * DL_CAP + p];
-        }
+        if (slive && sidx < (int)scnt) S.cb[S.boff[sblk] + sidx] = slot;
         __syncthreads();
     } else {
         // too many keys in the level-1 range: narrow it over the stored scores
