@@ -390,7 +390,7 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
             bool valid[EPT];
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
-                const int p = lane * EPT + e;
+                const int p = e * WAVE + lane;          // lane-contiguous: no bank conflicts
                 valid[e] = p < n;
                 key[e] = valid[e] ? S.cb[p][0] : 0u;
             }
@@ -399,7 +399,7 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
                 if (!valid[e]) continue;
-                const uint32_t j = S.cb[lane * EPT + e][1];
+                const uint32_t j = S.cb[e * WAVE + lane][1];
                 if (key[e] > thr) atomicOr(&S.sel[j >> 5], 1u << (j & 31));
                 else if (key[e] == thr) atomicOr(&S.eq[j >> 5], 1u << (j & 31));
             }
@@ -408,8 +408,7 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
         if (lane == 0) S.need_eq = need_eq;
     }
     __syncthreads();
-    block_merge_first_bits<DL_NT>(S.sel, S.eq, nw, S.need_eq, S.scratch);
-    block_emit_bitmap<DL_NT>(S.sel, nw, out, k, S.scratch);
+    block_merge_emit8<DL_NT>(S.sel, S.eq, nw, S.need_eq, out, k, S.scratch);
 }
 
 size_t dselect_smem_bytes() { return sizeof(DselSmem); }

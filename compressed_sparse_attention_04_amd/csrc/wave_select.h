@@ -236,6 +236,70 @@ __device__ __forceinline__ void block_merge_first_bits(uint32_t* sel, const uint
     __syncthreads();
 }
 
+// block_merge_first_bits and block_emit_bitmap in one pass over registers:
+// thread t owns words 8t .. 8t + 7 (NT * 8 words, those from nw on read as
+// empty), read once as two 16-byte vectors from sel and eq.  The first
+// need_eq set bits of eq (candidate order) join sel, and the set bits of the
+// result go to out in ascending order (at most k), then -1 up to k.
+template <int NT>
+__device__ __forceinline__ void block_merge_emit8(const uint32_t* sel, const uint32_t* eq, int nw,
+                                                  int need_eq, int32_t* out, int k,
+                                                  int* scratch) {
+    const int w0 = 8 * (int)threadIdx.x;
+    uint32_t s8[8], e8[8];
+    {
+        const u32x4 a = reinterpret_cast<const u32x4*>(sel + w0)[0];
+        const u32x4 b = reinterpret_cast<const u32x4*>(sel + w0)[1];
+        const u32x4 c = reinterpret_cast<const u32x4*>(eq + w0)[0];
+        const u32x4 d = reinterpret_cast<const u32x4*>(eq + w0)[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s8[i] = a[i]; s8[4 + i] = b[i];
+            e8[i] = c[i]; e8[4 + i] = d[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (w0 + i >= nw) s8[i] = e8[i] = 0u;
+    int ceq = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ceq += __popc(e8[i]);
+    int tot;
+    int before = block_excl_scan_i<NT>(ceq, scratch, &tot);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t bits = before < need_eq ? e8[i] : 0u;
+        const int c = __popc(bits);
+        if (before + c > need_eq) {
+            uint32_t kept = 0;
+            for (int x = 0; x < need_eq - before; ++x) {
+                const uint32_t low = bits & (0u - bits);
+                kept |= low;
+                bits ^= low;
+            }
+            bits = kept;
+        }
+        s8[i] |= bits;
+        before += c;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += __popc(s8[i]);
+    int total;
+    int pos = block_excl_scan_i<NT>(cnt, scratch, &total);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t bits = s8[i];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            if (pos < k) out[pos] = (w0 + i) * 32 + b;
+            pos++;
+        }
+    }
+    for (int x = total + (int)threadIdx.x; x < k; x += NT) out[x] = -1;
+}
+
 template <int NT>
 __device__ __forceinline__ void block_emit_bitmap(const uint32_t* sel, int nw, int32_t* out, int k,
                                                   int* scratch) {
