@@ -1,7 +1,10 @@
 """Parity at the full sizes of the benchmarked workloads, in the launch
 configuration bench.py times (same entry points, shapes, workspaces and
 paths), checked against the oracle on sampled outputs it can compute one by
-one: sampled query rows (prefill) or sampled sequences (decode).
+one: sampled query rows (prefill) or sampled sequences (decode).  The MXFP8
+cases run bench.py --kv-format mxfp8's chain (pooling, encoding, MXFP8
+attention) against the oracle's pooling, encoding and attention over the
+decoded entries.
 
 The inputs are drawn on the GPU by the shared input module and copied to the
 host for the oracle, so both sides see the same numbers.  The oracle runs its
@@ -27,10 +30,12 @@ def sample_rows(w, fixed, n_random, seed):
     return np.array(sorted(rows), np.int64)
 
 
-def prefill_layer(w, rows):
+def prefill_layer(w, rows, kv_fmt="bf16"):
     """Full GPU chain of one prefill layer, then the oracle's chain for the
-    sampled query rows."""
-    say("full size", w.name, "rows", rows.tolist())
+    sampled query rows.  kv_fmt "mxfp8": the compressed entries are encoded
+    to MXFP8 after pooling and attention reads them so (bench.py
+    --kv-format mxfp8); the oracle encodes its own pooled entries."""
+    say("full size", w.name, kv_fmt, "rows", rows.tolist())
     raw = I.draw_raw(w, device=DEV)
     gck = csa.hca_compress(raw["k"], raw["gk"], w.m)
     gcv = csa.hca_compress(raw["v"], raw["gv"], w.m)
@@ -44,6 +49,15 @@ def prefill_layer(w, rows):
                          dtype=torch.uint8, device=DEV)
         gtk = csa.csa_index_topk(q_idx, gkc, gks, m=w.m, W=w.W, k=w.k, q_pos0=w.q_pos0, ws=ws)
         del q_idx, ws
+    if kv_fmt == "mxfp8":
+        (kc8, ks8), (vc8, vs8) = csa.csa_quantize_mxfp8(gck), csa.csa_quantize_mxfp8(gcv)
+        if w.kind == "csa":
+            go = csa.csa_attend_mxfp8(q, kc8, vc8, ks8, vs8, gtk, raw["k"], raw["v"], m=w.m,
+                                      W=w.W, q_pos0=w.q_pos0, raw_pos0=0)
+        else:
+            go = csa.hca_attend_mxfp8(q, kc8, vc8, ks8, vs8, raw["k"], raw["v"], m=w.m, W=w.W,
+                                      q_pos0=w.q_pos0, raw_pos0=0)
+    elif w.kind == "csa":
         go = csa.csa_attend(q, gck, gcv, gtk, raw["k"], raw["v"], m=w.m, W=w.W,
                             q_pos0=w.q_pos0, raw_pos0=0)
     else:
@@ -61,6 +75,9 @@ def prefill_layer(w, rows):
     err_c = max(maxerr(gck.cpu(), ck), maxerr(gcv.cpu(), cv))
     say("  compressed caches max err", err_c)
     assert err_c <= TOL[w.dtype]
+    if kv_fmt == "mxfp8":
+        ck, cv = oracle.dequant_mxfp8(*oracle.quant_mxfp8(ck)), oracle.dequant_mxfp8(
+            *oracle.quant_mxfp8(cv))
     q_pos = w.q_pos0 + rows
     qh = f64(I.draw_queries(w, device=DEV, rows=rows).cpu())
     if w.kind == "csa":
@@ -91,6 +108,12 @@ def test_csa_prefill_32k_full_size():
 def test_pair_prefill_128k_full_size(w):
     fixed = [0, 126, 127, 128, 255, 256, 2175, 2176, 8191, 8192, 65535, 65536, 131070, 131071]
     prefill_layer(w, sample_rows(w, fixed, 6, seed=102))
+
+
+@pytest.mark.parametrize("w", [I.PAIR_CSA_128K, I.PAIR_HCA_128K], ids=lambda w: w.name)
+def test_pair_prefill_128k_full_size_mxfp8(w):
+    fixed = [0, 127, 128, 2176, 65536, 131071]
+    prefill_layer(w, sample_rows(w, fixed, 4, seed=103), kv_fmt="mxfp8")
 
 
 def decode_caches_gpu(w, with_keys):
@@ -128,12 +151,17 @@ def decode_caches_oracle(w, b):
     return np.concatenate(ck)[None], np.concatenate(cv)[None], rk[None], rv[None]
 
 
-@pytest.mark.parametrize("name,seqs", [("hca_decode_1m", [0, 31]), ("csa_decode_1m", [9])])
-def test_decode_1m_full_size(name, seqs):
+@pytest.mark.parametrize("name,seqs,kv_fmt", [("hca_decode_1m", [0, 31], "bf16"),
+                                              ("csa_decode_1m", [9], "bf16"),
+                                              ("hca_decode_1m", [5], "mxfp8"),
+                                              ("csa_decode_1m", [14], "mxfp8")])
+def test_decode_1m_full_size(name, seqs, kv_fmt):
     w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
     t = w.q_pos0
-    say("full size", w.name, "sequences", seqs)
+    say("full size", w.name, kv_fmt, "sequences", seqs)
     ck, cv, rk, rv = decode_caches_gpu(w, w.kind == "csa")
+    if kv_fmt == "mxfp8":
+        mx = csa.csa_quantize_mxfp8(ck) + csa.csa_quantize_mxfp8(cv)   # kc, ks, vc, vs
     q = I.draw_queries(w, device=DEV)
     if w.kind == "csa":
         k_idx = I.draw_indexer_keys(w, device=DEV)
@@ -145,13 +173,21 @@ def test_decode_1m_full_size(name, seqs):
         aws = torch.empty(max(1, csa.csa_attend_workspace(1, w.B, 1, w.H, w.D, w.k, w.W)),
                           dtype=torch.uint8, device=DEV)
         gtk = csa.csa_index_topk(q_idx, gkc, gks, m=w.m, W=w.W, k=w.k, q_pos0=t, ws=iws)
-        go = csa.csa_attend(q, ck, cv, gtk, rk, rv, m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1,
-                            ws=aws)
+        if kv_fmt == "mxfp8":
+            go = csa.csa_attend_mxfp8(q, mx[0], mx[2], mx[1], mx[3], gtk, rk, rv, m=w.m, W=w.W,
+                                      q_pos0=t, raw_pos0=t - w.W + 1, ws=aws)
+        else:
+            go = csa.csa_attend(q, ck, cv, gtk, rk, rv, m=w.m, W=w.W, q_pos0=t,
+                                raw_pos0=t - w.W + 1, ws=aws)
     else:
         aws = torch.empty(max(1, csa.hca_attend_workspace(1, w.B, 1, w.H, w.D, w.Nc, w.m, w.W,
                                                           t)), dtype=torch.uint8, device=DEV)
-        go = csa.hca_attend(q, ck, cv, rk, rv, m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1,
-                            ws=aws)
+        if kv_fmt == "mxfp8":
+            go = csa.hca_attend_mxfp8(q, mx[0], mx[2], mx[1], mx[3], rk, rv, m=w.m, W=w.W,
+                                      q_pos0=t, raw_pos0=t - w.W + 1, ws=aws)
+        else:
+            go = csa.hca_attend(q, ck, cv, rk, rv, m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1,
+                                ws=aws)
     torch.cuda.synchronize()
     for b in seqs:
         ock, ocv, ork, orv = decode_caches_oracle(w, b)
@@ -166,6 +202,9 @@ def test_decode_1m_full_size(name, seqs):
             assert np.array_equal(gtk[b:b + 1].cpu().numpy(), tk)
         else:
             tk = None
+        if kv_fmt == "mxfp8":
+            ock = oracle.dequant_mxfp8(*oracle.quant_mxfp8(ock))
+            ocv = oracle.dequant_mxfp8(*oracle.quant_mxfp8(ocv))
         ref = oracle.attend(qh, ock, ocv, tk, ork, orv, t - w.W + 1, [t], w.m, w.W)
         err = maxerr(go[b:b + 1].cpu(), ref)
         say("  sequence", b, "output max err", err)
