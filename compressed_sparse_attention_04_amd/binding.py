@@ -49,6 +49,10 @@ _SIGS = {
     "hca_attend_workspace": ([ctypes.c_int] + [_i64] * 8 + [ctypes.POINTER(_sz)], ctypes.c_int),
     "hca_attend": ([ctypes.c_int] + [_i64] * 8 + [ctypes.c_float] + [_p] * 5 + [_i64, _i64]
                    + [_p, _p, _sz, _p], ctypes.c_int),
+    "csa_index_attend_workspace": ([ctypes.c_int] + [_i64] * 12 + [ctypes.POINTER(_sz)],
+                                   ctypes.c_int),
+    "csa_index_attend": ([ctypes.c_int] + [_i64] * 11 + [ctypes.c_float] + [_p] * 8 + [_i64, _i64]
+                         + [_p, _p, _i64, _p, _sz, _p, _p], ctypes.c_int),
     "csa_layer_schedule": ([_i64, _p], ctypes.c_int),
     "csa_stack_workspace": ([ctypes.c_int, _i64, _p] + [_i64] * 9 + [ctypes.POINTER(_sz)],
                             ctypes.c_int),
@@ -320,3 +324,42 @@ def csa_stack_attend(layers, *, W: int, k: int, q_pos0: int, raw_pos0: int, scal
     ws, wsb = _workspace(nbytes, q.device, ws)
     _call("csa_stack_attend", _dt(q), len(layers), ctypes.cast(arr, ctypes.c_void_p), B, Tq, H, D,
           HI, dI, W, k, q_pos0, scale, raw_pos0, raw_len, _ptr(ws), wsb, _stream(q, stream))
+
+
+_aux_streams = {}
+
+
+def csa_index_attend_workspace(dtype: int, B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0,
+                               n_chunks) -> int:
+    n = _sz(0)
+    _call("csa_index_attend_workspace", dtype, B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0,
+          n_chunks, ctypes.byref(n))
+    return n.value
+
+
+def csa_index_attend(q, q_idx, k_codes, k_scales, ck, cv, rk, rv, *, m: int, W: int, k: int,
+                     q_pos0: int, raw_pos0: int, n_chunks: int = 8, scale: float = 1.0,
+                     topk=None, out=None, ws=None, stream=None, aux_stream=None):
+    """csa_index_topk + csa_attend as one pipeline over n_chunks query slices
+    (selection on aux_stream, attention on stream).  Returns (topk, out)."""
+    B, Tq, H, D = q.shape
+    HI, dI = q_idx.shape[2], q_idx.shape[3]
+    Nc = ck.shape[1]
+    raw_len = rk.shape[1]
+    if aux_stream is None:
+        dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+        if dev not in _aux_streams:
+            _aux_streams[dev] = torch.cuda.Stream(device=dev)
+        aux_stream = _aux_streams[dev]
+    nbytes = csa_index_attend_workspace(_dt(q), B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0,
+                                        n_chunks)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    if topk is None:
+        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _call("csa_index_attend", _dt(q), B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0, scale, _ptr(q),
+          _ptr(q_idx), _ptr(k_codes), _ptr(k_scales), _ptr(ck), _ptr(cv), _ptr(rk), _ptr(rv),
+          raw_pos0, raw_len, _ptr(topk), _ptr(out), n_chunks, _ptr(ws), wsb, _stream(q, stream),
+          _stream(q, aux_stream))
+    return topk, out

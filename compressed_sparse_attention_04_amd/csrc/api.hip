@@ -327,6 +327,151 @@ csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
                          rk, rv, raw_pos0, raw_len, o, ws, ws_bytes, stream);
 }
 
+// ---- one CSA layer's selection and attention, pipelined over query slices ----
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct SliceWs {
+    size_t index, attend;   // bytes of the two regions (index first)
+};
+
+// The attention of every slice keeps the key-list splits of the whole call,
+// so each row is computed exactly as csa_attend computes it.
+static csa::AttendPlan slice_attend_plan(csa_dtype dt, int64_t B, int64_t Tq, int64_t rows,
+                                         int64_t H, int64_t D, int64_t k, int64_t W) {
+    csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, k + W);
+    p.ws_bytes = p.splits > 1 ? (size_t)(rows * p.splits * H) * (D * 2 + 8) : 0;
+    return p;
+}
+
+// query rows a .. b of one sequence form a slice; slices are ceil(Tq / n) rows
+static SliceWs slice_ws(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t HI,
+                        int64_t dI, int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                        int64_t n_chunks) {
+    SliceWs r{0, 0};
+    const int64_t per = (Tq + n_chunks - 1) / n_chunks;
+    for (int64_t a = 0; a < Tq; a += per) {
+        const int64_t rows = Tq - a < per ? Tq - a : per;
+        const size_t i = csa::plan_index(1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a)
+                             .ws_bytes;
+        const size_t t = slice_attend_plan(dt, B, Tq, rows, H, D, k, W).ws_bytes;
+        r.index = i > r.index ? i : r.index;
+        r.attend = t > r.attend ? t : r.attend;
+    }
+    return r;
+}
+
+static csa_status index_attend_args(const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
+                                    int64_t H, int64_t D, int64_t HI, int64_t dI, int64_t Nc,
+                                    int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                                    const void* q, const void* q_idx, const uint8_t* k_codes,
+                                    const uint8_t* k_scales, const void* ck, const void* cv,
+                                    const void* rk, const void* rv, int64_t raw_pos0,
+                                    int64_t raw_len, int32_t* topk, void* o, int64_t n_chunks) {
+    CHECK(n_chunks >= 1 && n_chunks <= 64, CSA_EINVAL, "%s: n_chunks must be in [1, 64]", fn);
+    // every check of the two steps over the whole range (workspaces apart)
+    void* fake_ws = (void*)(uintptr_t)256;
+    csa_status s = index_topk_do(false, fn, dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx,
+                                 k_codes, k_scales, topk, fake_ws, SIZE_MAX, nullptr);
+    if (s == CSA_OK)
+        s = csa_attend_do(false, fn, dt, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck, cv, topk,
+                          rk, rv, raw_pos0, raw_len, o, fake_ws, SIZE_MAX, nullptr);
+    return s;
+}
+
+csa_status csa_index_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                                      int64_t HI, int64_t dI, int64_t Nc, int64_t m, int64_t W,
+                                      int64_t k, int64_t q_pos0, int64_t n_chunks,
+                                      size_t* bytes) {
+    const char* fn = "csa_index_attend_workspace";
+    CHECK(bytes, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(n_chunks >= 1 && n_chunks <= 64, CSA_EINVAL, "%s: n_chunks must be in [1, 64]", fn);
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    if (csa_status s = index_args(fn, B, Tq, HI, dI, Nc, m, W, k, q_pos0)) return s;
+    if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
+    const SliceWs w = slice_ws(dt, B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0, n_chunks);
+    *bytes = align256(w.index) + w.attend;
+    return ok();
+}
+
+csa_status csa_index_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                            int64_t HI, int64_t dI, int64_t Nc, int64_t m, int64_t W, int64_t k,
+                            int64_t q_pos0, float scale, const void* q, const void* q_idx,
+                            const uint8_t* k_codes, const uint8_t* k_scales, const void* ck,
+                            const void* cv, const void* rk, const void* rv, int64_t raw_pos0,
+                            int64_t raw_len, int32_t* topk, void* o, int64_t n_chunks, void* ws,
+                            size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream) {
+    const char* fn = "csa_index_attend";
+    if (csa_status s = index_attend_args(fn, dt, B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0, scale,
+                                         q, q_idx, k_codes, k_scales, ck, cv, rk, rv, raw_pos0,
+                                         raw_len, topk, o, n_chunks))
+        return s;
+    const SliceWs w = slice_ws(dt, B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0, n_chunks);
+    const size_t need = align256(w.index) + w.attend;
+    CHECK(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))), CSA_EINVAL,
+          "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+    if (B == 0 || Tq == 0) return ok();
+    void* iws = ws;
+    void* aws = w.attend ? (void*)((char*)ws + align256(w.index)) : nullptr;
+    // events of the slices, kept for the life of the thread
+    // (made on the device current at the thread's first call there)
+    thread_local hipEvent_t ev[65];
+    thread_local int ev_dev = -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(CSA_EDEVICE, "%s: no device", fn);
+    if (dev != ev_dev) {
+        for (hipEvent_t& e : ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+                return fail(CSA_EDEVICE, "%s: hipEventCreate failed", fn);
+        ev_dev = dev;
+    }
+    const bool two = aux_stream != stream;
+    hipStream_t is = two ? aux_stream : stream;
+    if (two) {
+        // the selection stream starts after everything already queued on stream
+        if (hipEventRecord(ev[64], stream) != hipSuccess ||
+            hipStreamWaitEvent(is, ev[64], 0) != hipSuccess)
+            return fail(CSA_EDEVICE, "%s: stream ordering failed", fn);
+    }
+    const int64_t per = (Tq + n_chunks - 1) / n_chunks;
+    const int64_t esz = dt == CSA_F32 ? 4 : 2;
+    const char* qb = (const char*)q;
+    const char* qib = (const char*)q_idx;
+    char* ob = (char*)o;
+    for (int64_t b = 0; b < B; ++b) {
+        const char* ckb = (const char*)ck + b * Nc * D * esz;
+        const char* cvb = (const char*)cv + b * Nc * D * esz;
+        const char* rkb = (const char*)rk + b * raw_len * D * esz;
+        const char* rvb = (const char*)rv + b * raw_len * D * esz;
+        const uint8_t* kcb = k_codes + b * Nc * (dI / 2);
+        const uint8_t* ksb = k_scales + b * Nc * (dI / 32);
+        int c = 0;
+        for (int64_t a = 0; a < Tq; a += per, ++c) {
+            const int64_t rows = Tq - a < per ? Tq - a : per;
+            const int64_t r0 = b * Tq + a;
+            hipError_t e = csa::launch_index_topk(
+                (int)dt, csa::plan_index(1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a),
+                1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a, qib + r0 * HI * dI * esz,
+                kcb, ksb, topk + r0 * k, iws, is);
+            if (e == hipSuccess && two) e = hipEventRecord(ev[c], is);
+            if (e != hipSuccess) return launched(e, fn);
+        }
+        c = 0;
+        for (int64_t a = 0; a < Tq; a += per, ++c) {
+            const int64_t rows = Tq - a < per ? Tq - a : per;
+            const int64_t r0 = b * Tq + a;
+            hipError_t e = two ? hipStreamWaitEvent(stream, ev[c], 0) : hipSuccess;
+            if (e == hipSuccess)
+                e = csa::launch_attend((int)dt, slice_attend_plan(dt, B, Tq, rows, H, D, k, W), 1,
+                                       rows, H, D, Nc, m, W, k, q_pos0 + a, scale,
+                                       qb + r0 * H * D * esz, ckb, cvb, topk + r0 * k, rkb, rvb,
+                                       raw_pos0, raw_len, ob + r0 * H * D * esz, aws, stream);
+            if (e != hipSuccess) return launched(e, fn);
+        }
+    }
+    return ok();
+}
+
 // ---- a stack of layers ------------------------------------------------------
 
 csa_status csa_layer_schedule(int64_t n_layers, int32_t* kinds) {

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -271,6 +271,36 @@ csa_status hca_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t
                             const void *ck_scales, const void *cv_scales, const void *rk,
                             const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_index_attend -- csa_index_topk followed by csa_attend over the same
+ * query rows (jiwasawa.github.io post, CSA indexer and shared-KV MQA
+ * bullets), with bit-identical results (topk and o), scheduled as a
+ * pipeline: the query rows of each sequence are cut into n_chunks slices of
+ * ceil(Tq / n_chunks) rows; the selection of every slice runs on
+ * aux_stream, and the attention of slice c runs on stream once its
+ * selection is done, so one slice's attention overlaps the next slices'
+ * selection.  aux_stream first waits for the work already queued on
+ * stream, and stream has waited for all of aux_stream's work of this call
+ * when the call returns (use the results on stream).  aux_stream == stream
+ * (or n_chunks == 1) runs the two steps in order on stream.  Arguments,
+ * layouts and requirements are those of the two entry points; topk
+ * [B, Tq, k] is written; ws holds csa_index_attend_workspace bytes.  The
+ * library keeps 65 HIP events per host thread and device, made at the first
+ * call (a stream wait takes an event's state when it is queued, so later
+ * calls may record them again at once).
+ */
+csa_status csa_index_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                                      int64_t HI, int64_t dI, int64_t Nc, int64_t m, int64_t W,
+                                      int64_t k, int64_t q_pos0, int64_t n_chunks,
+                                      size_t *bytes);
+csa_status csa_index_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                            int64_t HI, int64_t dI, int64_t Nc, int64_t m, int64_t W, int64_t k,
+                            int64_t q_pos0, float scale, const void *q, const void *q_idx,
+                            const uint8_t *k_codes, const uint8_t *k_scales, const void *ck,
+                            const void *cv, const void *rk, const void *rv, int64_t raw_pos0,
+                            int64_t raw_len, int32_t *topk, void *o, int64_t n_chunks, void *ws,
+                            size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream);
 
 /*
  * A stack of attention layers (hazakura.dev note, CSA/HCA bullets: HCA in

@@ -35,14 +35,14 @@ def test_exports_every_declared_symbol(L):
     assert {"hca_compress", "csa_index_topk", "csa_attend", "hca_attend",
             "csa_quantize_mxfp4", "hca_append", "csa_quantize_mxfp8", "csa_attend_mxfp8",
             "hca_attend_mxfp8", "csa_layer_schedule", "csa_stack_workspace",
-            "csa_stack_attend"} <= set(names)
+            "csa_stack_attend", "csa_index_attend_workspace", "csa_index_attend"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGS), "binding and header disagree"
 
 
 def test_version(L):
-    assert L.csa_abi_version() == 4
+    assert L.csa_abi_version() == 5
 
 
 def err(L):
@@ -107,6 +107,28 @@ def test_mxfp8_rejects(L):
     st = L.csa_attend_mxfp8(1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, S, S, P, P, P,
                             1073, 127, P, None, 0, None)
     assert st == EINVAL and "raw rows" in err(L)
+
+
+def test_index_attend_rejects(L):
+    n = ctypes.c_size_t(0)
+    ws = lambda nch, Nc=600, k=512: L.csa_index_attend_workspace(1, 1, 100, 128, 128, 4, 64, Nc,
+                                                                  4, 128, k, 2000, nch,
+                                                                  ctypes.byref(n))
+    assert ws(0) == EINVAL and "n_chunks" in err(L)
+    assert ws(65) == EINVAL
+    assert ws(4, Nc=100) == EINVAL and "candidates" in err(L)
+    assert ws(4, k=4096) == EINVAL
+    assert ws(4) == 0
+
+    def call(nch=4, raw_pos0=0, topk=P, wsb=1 << 30):
+        return L.csa_index_attend(1, 1, 100, 128, 128, 4, 64, 600, 4, 128, 512, 2000, 1.0, P, P,
+                                  P, P, P, P, P, P, raw_pos0, 2100, topk, P, nch, P, wsb, None,
+                                  None)
+    assert call(nch=0) == EINVAL
+    assert call(topk=None) == EINVAL and "null" in err(L)
+    assert call(raw_pos0=1900) == EINVAL and "raw rows" in err(L)
+    assert n.value > 0                                    # 25-row slices split their keys
+    assert call(wsb=n.value - 1) == EINVAL and "workspace" in err(L)
 
 
 def test_layer_schedule():

@@ -1,0 +1,51 @@
+"""csa_index_attend (selection and attention pipelined over query slices on
+two streams) on the GPU: topk and output bit-identical to csa_index_topk
+followed by csa_attend, for one and several sequences, ragged slices,
+one-row slices and a single slice; one case also against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_sparse_attention_04_amd import binding as csa
+from compressed_sparse_attention_04_amd import inputs as I
+from tests.gpu_helpers import DEV, TOL, f64, maxerr, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,T,q0,Tq,k,n_chunks,with_oracle", [
+    (1, 6000, 2000, 600, 512, 8, True),
+    (1, 6000, 2000, 600, 512, 1, False),
+    (2, 9000, 7000, 333, 256, 5, False),       # ragged slices, two sequences
+    (3, 20000, 19997, 3, 512, 8, False),       # more slices than rows: one-row slices
+    (1, 140000, 139000, 40, 512, 4, False),    # long rows: chunked selection path
+])
+def test_index_attend_matches_two_calls(B, T, q0, Tq, k, n_chunks, with_oracle):
+    say("index_attend", B, T, q0, Tq, k, n_chunks)
+    w = I.Workload("t", "csa", seed=81, dtype="bf16", B=B, T=T, m=4, H=128, D=128, W=128, k=k,
+                   Tq=Tq, q_pos0=q0)
+    Nc = T // 4
+    q = I.draw_queries(w, device=DEV)
+    ck, cv = I.draw_cache(w, "ck", Nc, device=DEV), I.draw_cache(w, "cv", Nc, device=DEV)
+    rk, rv = I.draw_cache(w, "rk", T, device=DEV), I.draw_cache(w, "rv", T, device=DEV)
+    k_idx = I.draw_indexer_keys(w, device=DEV)
+    kc, ks = csa.csa_quantize_mxfp4(k_idx)
+    qi = I.draw_indexer_queries(w, device=DEV)
+    tk1 = csa.csa_index_topk(qi, kc, ks, m=4, W=128, k=k, q_pos0=q0)
+    o1 = csa.csa_attend(q, ck, cv, tk1, rk, rv, m=4, W=128, q_pos0=q0, raw_pos0=0)
+    tk2, o2 = csa.csa_index_attend(q, qi, kc, ks, ck, cv, rk, rv, m=4, W=128, k=k, q_pos0=q0,
+                                   raw_pos0=0, n_chunks=n_chunks)
+    torch.cuda.synchronize()
+    assert torch.equal(tk1, tk2)
+    assert torch.equal(o1, o2)
+    if with_oracle:
+        q_pos = np.arange(q0, q0 + Tq)
+        kc_o, ks_o = oracle.quant_mxfp4(f64(k_idx.cpu()))
+        ref_tk, exact = oracle.index_topk(f64(qi.cpu()), kc_o, ks_o, q_pos, 4, 128, k)
+        assert exact and np.array_equal(tk2.cpu().numpy(), ref_tk)
+        ref = oracle.attend(f64(q.cpu()), f64(ck.cpu()), f64(cv.cpu()), ref_tk, f64(rk.cpu()),
+                            f64(rv.cpu()), 0, q_pos, 4, 128)
+        err = maxerr(o2, ref)
+        say("  max err", err)
+        assert err <= TOL["bf16"]
