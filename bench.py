@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp4_TFLOPs": 10100.0}
+PIPE_SLICES = 8        # query slices of a pipelined CSA layer (selection | attention)
 DEFAULT = "pair_prefill_128k"
 
 # Kernel sources behind each stage: the HBM traffic recorded in
@@ -101,16 +102,19 @@ def attend_keys(q_pos, m, W, k):
 
 # --------------------------------------------------------------- workloads
 class Stage:
-    def __init__(self, name, fn, flops=0.0, bytes_=0.0, peak_key=None):
+    def __init__(self, name, fn, flops=0.0, bytes_=0.0, peak_key=None, fp4_flops=0.0):
         self.name, self.fn, self.flops, self.bytes, self.peak_key = name, fn, flops, bytes_, peak_key
+        self.fp4_flops = fp4_flops        # FP4 indexer flops of a stage that also runs bf16 MFMA
 
 
-def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16"):
+def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
     """CSA (and optionally HCA) prefill layers over one sequence.  shared_kv:
     one vector per entry and raw token serves as key and value (only K is
     compressed, and the same buffers are passed as K and V).  kv_fmt
     "mxfp8": the compressed entries are encoded to MXFP8 after pooling (a
-    timed stage) and attention reads them in that form."""
+    timed stage) and attention reads them in that form.  pipeline (bf16
+    entries): a CSA layer's selection and attention run as one
+    csa_index_attend call over 8 query slices on two streams."""
     import torch
     from compressed_sparse_attention_04_amd import binding as csa
     from compressed_sparse_attention_04_amd import inputs as I
@@ -164,6 +168,20 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16"):
                                     k_idx, codes=kc, scales=ks),
                                 bytes_=w.Nc * (w.dI * 2 + w.dI // 2 + w.dI // 32),
                                 peak_key="hbm_GBps"))
+            if pipeline and mx is None:
+                pws = torch.empty(max(1, csa.csa_index_attend_workspace(
+                    1, 1, w.Tq, H, D, w.HI, w.dI, w.Nc, m, W, w.k, w.q_pos0, PIPE_SLICES)),
+                    dtype=torch.uint8, device=dev)
+                stages.append(Stage(
+                    "csa_index_attend",
+                    lambda q=q, q_idx=q_idx, kc=kc, ks=ks, ck=ck, cv=cv, raw=raw, rv=rv,
+                    topk=topk, o=o, pws=pws, w=w:
+                    csa.csa_index_attend(q, q_idx, kc, ks, ck, cv, raw["k"], rv, m=w.m, W=w.W,
+                                         k=w.k, q_pos0=w.q_pos0, raw_pos0=0,
+                                         n_chunks=PIPE_SLICES, topk=topk, out=o, ws=pws),
+                    flops=4.0 * H * D * float(nkeys.sum()), bytes_=2.0 * w.Tq * H * D * 2,
+                    peak_key="bf16_TFLOPs", fp4_flops=2.0 * w.HI * w.dI * float(nc.sum())))
+                continue
             stages.append(Stage("index_topk",
                                 lambda q_idx=q_idx, kc=kc, ks=ks, topk=topk, iws=iws, w=w:
                                 csa.csa_index_topk(q_idx, kc, ks, m=w.m, W=w.W, k=w.k,
@@ -469,6 +487,10 @@ def main():
                     help="storage of the compressed entries: bf16 (default) or MXFP8 E4M3 "
                          "codes with a power-of-two scale per 32 values (the raw window "
                          "stays bf16)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="run a CSA prefill layer's selection and attention as one "
+                         "csa_index_attend call, pipelined over query slices on two streams "
+                         "(default: two stages in order)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -501,14 +523,15 @@ def main():
 
     if args.workload == "pair_prefill_128k":
         stages, tokens, notes = setup_prefill(dev, [I.PAIR_CSA_128K, I.PAIR_HCA_128K],
-                                              args.shared_kv, args.kv_format)
+                                              args.shared_kv, args.kv_format,
+                                              args.pipeline)
         wl = {"workload": "csa_hca_layer_pair_prefill", "seq_len": 131072, "batch": 1,
               "heads": 128, "kv_heads": 1, "head_dim": 128, "m_csa": 4, "m_hca": 128,
               "top_k": 512, "indexer": "4x64 MXFP4", "window": 128}
         metric, unit = "prefill tokens/s", "tokens/s"
     elif args.workload == "csa_prefill_32k":
         stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K], args.shared_kv,
-                                              args.kv_format)
+                                              args.kv_format, args.pipeline)
         wl = {"workload": "csa_prefill", "seq_len": 32768, "batch": 1, "heads": 128,
               "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
               "window": 128}
@@ -532,6 +555,9 @@ def main():
               "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
               "top_k": w.k if w.kind == "csa" else None, "window": w.W}
         metric, unit = "1M-ctx decode tokens/s/GPU", "tokens/s"
+    if not decode and args.pipeline and args.kv_format == "bf16":
+        wl["csa_schedule"] = (f"selection and attention pipelined over {PIPE_SLICES} query "
+                              "slices on two streams (csa_index_attend)")
     wl["kv"] = "one vector as key and value" if args.shared_kv else "separate K and V"
     wl["kv_format"] = ("compressed entries MXFP8 (E4M3), window bf16" if args.kv_format == "mxfp8"
                        else "bf16")
@@ -575,8 +601,15 @@ def main():
         roof = {"bound": "hbm", "achieved": d.bytes / sec / 1e9, "peak": PEAK["hbm_GBps"],
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": d.flops / sec / 1e12, "peak": PEAK[d.peak_key],
+        # a pipelined CSA layer runs FP4 indexer and bf16 attention MFMAs side by
+        # side: its FP4 flops count at the bf16/FP4 peak ratio, so achieved/peak
+        # is the sum over both of (flops / own peak) / time
+        eq = d.flops + d.fp4_flops * PEAK["bf16_TFLOPs"] / PEAK["fp4_TFLOPs"]
+        roof = {"bound": "mfma", "achieved": eq / sec / 1e12, "peak": PEAK[d.peak_key],
                 "unit": "TFLOP/s"}
+        if d.fp4_flops:
+            roof["convention"] = ("bf16-equivalent: attention bf16 flops + indexer FP4 flops x "
+                                  "2.5/10.1")
     roof["frac"] = roof["achieved"] / roof["peak"]
     # (counter passes exist for the default inputs only)
     roof["traffic"] = (None if args.shared_kv or args.kv_format != "bf16"
@@ -589,6 +622,8 @@ def main():
         e = {"ms": round(float(ms), 4)}
         if st.flops:
             e["TFLOP/s"] = round(st.flops / (ms / 1e3) / 1e12, 2)
+        if st.fp4_flops:
+            e["indexer FP4 TFLOP/s"] = round(st.fp4_flops / (ms / 1e3) / 1e12, 2)
         if st.bytes:
             e["GB/s"] = round(st.bytes / (ms / 1e3) / 1e9, 1)
         stage_info[st.name] = e
