@@ -123,13 +123,15 @@ def _stream(t: torch.Tensor, stream) -> int | None:
     return None
 
 
-def _workspace(nbytes: int, device, ws):
+def _workspace(ws, device, query):
+    """A workspace the caller passed is handed over whole (the library
+    checks its size); otherwise one of query() bytes is allocated."""
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    nbytes = query()
     if nbytes == 0:
         return None, 0
-    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
-        return ws, ws.numel() * ws.element_size()
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return ws, nbytes
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def hca_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out=None, stream=None):
@@ -182,8 +184,8 @@ def csa_index_topk(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.T
     -> topk [B,Tq,k] int32 (ascending, -1 padded)."""
     B, Tq, HI, dI = q_idx.shape
     Nc = k_codes.shape[1]
-    nbytes = csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0)
-    ws, wsb = _workspace(nbytes, q_idx.device, ws)
+    ws, wsb = _workspace(ws, q_idx.device,
+        lambda: csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0))
     if topk is None:
         topk = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
     _call("csa_index_topk", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
@@ -204,8 +206,7 @@ def csa_attend(q, ck, cv, topk, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0
     Nc = ck.shape[1]
     k = topk.shape[2]
     raw_len = rk.shape[1]
-    nbytes = csa_attend_workspace(_dt(q), B, Tq, H, D, k, W)
-    ws, wsb = _workspace(nbytes, q.device, ws)
+    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(_dt(q), B, Tq, H, D, k, W))
     if out is None:
         out = torch.empty_like(q)
     _call("csa_attend", _dt(q), B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
@@ -226,8 +227,8 @@ def hca_attend(q, ck, cv, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0: int,
     B, Tq, H, D = q.shape
     Nc = ck.shape[1]
     raw_len = rk.shape[1]
-    nbytes = hca_attend_workspace(_dt(q), B, Tq, H, D, Nc, m, W, q_pos0)
-    ws, wsb = _workspace(nbytes, q.device, ws)
+    ws, wsb = _workspace(ws, q.device,
+        lambda: hca_attend_workspace(_dt(q), B, Tq, H, D, Nc, m, W, q_pos0))
     if out is None:
         out = torch.empty_like(q)
     _call("hca_attend", _dt(q), B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck),
@@ -258,8 +259,7 @@ def csa_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, topk, rk, rv, *, m: int, W
     Nc = ck.shape[1]
     k = topk.shape[2]
     raw_len = rk.shape[1]
-    nbytes = csa_attend_workspace(CSA_BF16, B, Tq, H, D, k, W)
-    ws, wsb = _workspace(nbytes, q.device, ws)
+    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(CSA_BF16, B, Tq, H, D, k, W))
     if out is None:
         out = torch.empty_like(q)
     _call("csa_attend_mxfp8", B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
@@ -274,8 +274,8 @@ def hca_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, rk, rv, *, m: int, W: int,
     B, Tq, H, D = q.shape
     Nc = ck.shape[1]
     raw_len = rk.shape[1]
-    nbytes = hca_attend_workspace(CSA_BF16, B, Tq, H, D, Nc, m, W, q_pos0)
-    ws, wsb = _workspace(nbytes, q.device, ws)
+    ws, wsb = _workspace(ws, q.device,
+        lambda: hca_attend_workspace(CSA_BF16, B, Tq, H, D, Nc, m, W, q_pos0))
     if out is None:
         out = torch.empty_like(q)
     _call("hca_attend_mxfp8", B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck), _ptr(cv),
@@ -320,8 +320,8 @@ def csa_stack_attend(layers, *, W: int, k: int, q_pos0: int, raw_pos0: int, scal
     B, Tq, H, D = q.shape
     raw_len = layers[0]["rk"].shape[1]
     arr = _layer_array(layers)
-    nbytes = csa_stack_workspace(_dt(q), layers, B, Tq, H, D, HI, dI, W, k, q_pos0)
-    ws, wsb = _workspace(nbytes, q.device, ws)
+    ws, wsb = _workspace(ws, q.device,
+        lambda: csa_stack_workspace(_dt(q), layers, B, Tq, H, D, HI, dI, W, k, q_pos0))
     _call("csa_stack_attend", _dt(q), len(layers), ctypes.cast(arr, ctypes.c_void_p), B, Tq, H, D,
           HI, dI, W, k, q_pos0, scale, raw_pos0, raw_len, _ptr(ws), wsb, _stream(q, stream))
 
@@ -351,9 +351,9 @@ def csa_index_attend(q, q_idx, k_codes, k_scales, ck, cv, rk, rv, *, m: int, W: 
         if dev not in _aux_streams:
             _aux_streams[dev] = torch.cuda.Stream(device=dev)
         aux_stream = _aux_streams[dev]
-    nbytes = csa_index_attend_workspace(_dt(q), B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0,
-                                        n_chunks)
-    ws, wsb = _workspace(nbytes, q.device, ws)
+    ws, wsb = _workspace(ws, q.device,
+        lambda: csa_index_attend_workspace(_dt(q), B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0,
+                                        n_chunks))
     if topk is None:
         topk = torch.empty((B, Tq, k), dtype=torch.int32, device=q.device)
     if out is None:
