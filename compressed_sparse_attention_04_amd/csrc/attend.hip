@@ -691,12 +691,15 @@ k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
         // copies that tile tau and the conversion of tau + 1 need
         wait_vm_leaving(tau + 2 < tau1 && tau + 2 < ct ? percomp : 0);
         lds_barrier();
-        fill(tau + 1, stg1, nk_, nv_);
+        // a window tile's copies go out first; a compressed tile is converted
+        // after this tile's MFMA chain is issued, while it drains
+        if (tau + 1 >= ct) fill(tau + 1, stg1, nk_, nv_);
         stage(tau + 3, stg3);
         __builtin_amdgcn_sched_barrier(0);
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
         eng.tile((const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)(SHARED ? ck_ : cv_), nvalid,
                  scale_log2);
+        if (tau + 1 < ct) fill(tau + 1, stg1, nk_, nv_);
     };
 
     // prologue: stage tau0 .. tau0 + 2, then tile tau0's bf16 buffer
