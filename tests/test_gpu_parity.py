@@ -167,7 +167,7 @@ def test_index_unrepresentative_sample(T, q_pos0, Tq, shrink):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("copies", [600, 40])
+@pytest.mark.parametrize("copies", [600, 100, 40])
 def test_index_decode_clustered_range(copies):
     """Decode path: the keys around the k-th score all sit in one chunk of
     4096 candidates (copies of the row's best key, with 300 keys at twice
