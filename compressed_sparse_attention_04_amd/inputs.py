@@ -94,7 +94,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five problem shapes of this build (seeded, N(0,1) data):
+# The five problem shapes of the workloads (seeded, N(0,1) data):
 TINY_CSA = Workload("tiny_csa_f32", "csa", seed=0, dtype="f32", B=1, T=1024, m=4, H=8, D=64,
                     W=128, HI=2, dI=32, k=16, Tq=16, q_pos0=1008, gate="token")
 CSA_PREFILL_32K = Workload("csa_prefill_32k_bf16", "csa", seed=1, dtype="bf16", B=1, T=32768,

@@ -40,7 +40,7 @@
  *   - Errors: arguments are checked on the host before anything is
  *     enqueued.  A failed check returns CSA_EINVAL (bad value, null or
  *     misaligned pointer, too small workspace) or CSA_EUNSUPPORTED (a valid
- *     shape this build has no kernel for), writes nothing, and sets a
+ *     shape the library has no kernel for), writes nothing, and sets a
  *     thread-local message read by csa_last_error().  A launch error
  *     returns CSA_EDEVICE.  Base pointers must be 16-byte aligned.
  */
