@@ -42,7 +42,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version(L):
-    assert L.csa_abi_version() == 5
+    want = int(re.search(r"#define CSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.csa_abi_version() == want == 5
 
 
 def err(L):
