@@ -14,15 +14,16 @@ from tests.gpu_helpers import DEV, TOL, f64, maxerr, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("B,T,q0,Tq,k,n_chunks,with_oracle", [
-    (1, 6000, 2000, 600, 512, 8, True),
-    (1, 6000, 2000, 600, 512, 1, False),
-    (2, 9000, 7000, 333, 256, 5, False),       # ragged slices, two sequences
-    (3, 20000, 19997, 3, 512, 8, False),       # more slices than rows: one-row slices
-    (1, 140000, 139000, 40, 512, 4, False),    # long rows: chunked selection path
+@pytest.mark.parametrize("B,T,q0,Tq,k,n_chunks,with_oracle,same_stream", [
+    (1, 6000, 2000, 600, 512, 8, True, False),
+    (1, 6000, 2000, 600, 512, 1, False, False),
+    (2, 9000, 7000, 333, 256, 5, False, False),       # ragged slices, two sequences
+    (3, 20000, 19997, 3, 512, 8, False, False),       # more slices than rows
+    (1, 140000, 139000, 40, 512, 4, False, False),    # long rows: chunked selection path
+    (2, 9000, 7000, 333, 256, 5, False, True),        # auxiliary stream = the stream
 ])
-def test_index_attend_matches_two_calls(B, T, q0, Tq, k, n_chunks, with_oracle):
-    say("index_attend", B, T, q0, Tq, k, n_chunks)
+def test_index_attend_matches_two_calls(B, T, q0, Tq, k, n_chunks, with_oracle, same_stream):
+    say("index_attend", B, T, q0, Tq, k, n_chunks, same_stream)
     w = I.Workload("t", "csa", seed=81, dtype="bf16", B=B, T=T, m=4, H=128, D=128, W=128, k=k,
                    Tq=Tq, q_pos0=q0)
     Nc = T // 4
@@ -34,8 +35,9 @@ def test_index_attend_matches_two_calls(B, T, q0, Tq, k, n_chunks, with_oracle):
     qi = I.draw_indexer_queries(w, device=DEV)
     tk1 = csa.csa_index_topk(qi, kc, ks, m=4, W=128, k=k, q_pos0=q0)
     o1 = csa.csa_attend(q, ck, cv, tk1, rk, rv, m=4, W=128, q_pos0=q0, raw_pos0=0)
+    aux = torch.cuda.current_stream() if same_stream else None
     tk2, o2 = csa.csa_index_attend(q, qi, kc, ks, ck, cv, rk, rv, m=4, W=128, k=k, q_pos0=q0,
-                                   raw_pos0=0, n_chunks=n_chunks)
+                                   raw_pos0=0, n_chunks=n_chunks, aux_stream=aux)
     torch.cuda.synchronize()
     assert torch.equal(tk1, tk2)
     assert torch.equal(o1, o2)
