@@ -129,3 +129,62 @@ def test_decode_loop_with_append(kind):
         worst = max(worst, err)
         assert err <= TOL["bf16"], (t, err)
     say("  worst max err", worst)
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_decode_loop_mxfp8_entries(kind):
+    """The FP8 decode chain per token: append, encode each completed entry to
+    MXFP8 (csa_quantize_mxfp8 on its row), attend over the MXFP8 entries and
+    the bf16 window; against the oracle's own pooling, encoding and attention
+    over the decoded entries."""
+    m = 4 if kind == "csa" else 16
+    H, D, W, k, B = 128, 128, 128, 64, 2
+    T0, S = 1500, 20
+    w = I.Workload("t", "csa", seed=73, dtype="bf16", B=B, T=T0 + S, m=m, H=H, D=D, W=W, k=k,
+                   Tq=1, q_pos0=T0)
+    say("decode loop mxfp8", kind)
+    raw = {n: v.to(DEV) for n, v in I.draw_raw(w).items()}
+    nc_cap = (T0 + S) // m
+    st = new_state(w, D, D, 2 * W, nc_cap, False)
+    p0 = append_range(st, raw, w, 0, T0, 0, False)
+    kc8, ks8 = csa.csa_quantize_mxfp8(st["ck"])
+    vc8, vs8 = csa.csa_quantize_mxfp8(st["cv"])
+    ck_all = oracle.compress(f64(raw["k"].cpu()), f64(raw["gk"].cpu()), m)
+    cv_all = oracle.compress(f64(raw["v"].cpu()), f64(raw["gv"].cpu()), m)
+    ck_dq = oracle.dequant_mxfp8(*oracle.quant_mxfp8(ck_all))
+    cv_dq = oracle.dequant_mxfp8(*oracle.quant_mxfp8(cv_all))
+    rk_all, rv_all = f64(raw["k"].cpu()), f64(raw["v"].cpu())
+    wq = w.replace(Tq=S, q_pos0=T0)
+    q = I.draw_queries(wq, device=DEV)
+    if kind == "csa":
+        kc, ks = csa.csa_quantize_mxfp4(I.draw_indexer_keys(w.replace(T=T0 + S), device=DEV))
+        q_idx = I.draw_indexer_queries(wq, device=DEV)
+    worst = 0.0
+    for s in range(S):
+        t = T0 + s
+        p0 = append_range(st, raw, w, t, t + 1, p0, False)
+        if (t + 1) % m == 0:                          # entry (t + 1) / m - 1 completed
+            e = (t + 1) // m - 1
+            for b in range(B):
+                csa.csa_quantize_mxfp8(st["ck"][b, e:e + 1], codes=kc8[b, e:e + 1],
+                                       scales=ks8[b, e:e + 1])
+                csa.csa_quantize_mxfp8(st["cv"][b, e:e + 1], codes=vc8[b, e:e + 1],
+                                       scales=vs8[b, e:e + 1])
+        qt = q[:, s:s + 1].contiguous()
+        if kind == "csa":
+            tk = csa.csa_index_topk(q_idx[:, s:s + 1].contiguous(), kc, ks, m=m, W=W, k=k,
+                                    q_pos0=t)
+            o = csa.csa_attend_mxfp8(qt, kc8, vc8, ks8, vs8, tk, st["rk"], st["rv"], m=m, W=W,
+                                     q_pos0=t, raw_pos0=p0)
+            sel = tk.cpu().numpy()
+        else:
+            o = csa.hca_attend_mxfp8(qt, kc8, vc8, ks8, vs8, st["rk"], st["rv"], m=m, W=W,
+                                     q_pos0=t, raw_pos0=p0)
+            sel = None
+        torch.cuda.synchronize()
+        ref = oracle.attend(f64(qt.cpu()), ck_dq, cv_dq, sel, rk_all, rv_all, 0, np.array([t]),
+                            m, W)
+        err = maxerr(o, ref)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (t, err)
+    say("  worst max err", worst)
