@@ -13,6 +13,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _decode_inputs(kind, seed):
+    mx8 = kind.endswith("_mxfp8")
+    kind = kind.split("_")[0]
     m = 4 if kind == "csa" else 128
     T = m * 3000
     w = I.Workload("graph", kind, seed=seed, dtype="bf16", B=2, T=T, m=m, H=128, D=128, W=128,
@@ -37,29 +39,42 @@ def _decode_inputs(kind, seed):
                                                                w.W, t)),
                                dtype=torch.uint8, device=DEV)
     d["o"] = torch.empty_like(d["q"])
+    if mx8:                                       # MXFP8 compressed entries (encoded eagerly)
+        d["ck"], d["cks"] = csa.csa_quantize_mxfp8(d["ck"])
+        d["cv"], d["cvs"] = csa.csa_quantize_mxfp8(d["cv"])
     return w, d
 
 
 def _step(kind, w, d):
     t = w.q_pos0
-    if kind == "csa":
+    mx8 = kind.endswith("_mxfp8")
+    if kind.startswith("csa"):
         csa.csa_index_topk(d["q_idx"], d["kc"], d["ks"], m=w.m, W=w.W, k=w.k, q_pos0=t,
                            topk=d["topk"], ws=d["iws"])
-        csa.csa_attend(d["q"], d["ck"], d["cv"], d["topk"], d["rk"], d["rv"], m=w.m, W=w.W,
-                       q_pos0=t, raw_pos0=t - w.W + 1, out=d["o"], ws=d["aws"])
+        if mx8:
+            csa.csa_attend_mxfp8(d["q"], d["ck"], d["cv"], d["cks"], d["cvs"], d["topk"],
+                                 d["rk"], d["rv"], m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1,
+                                 out=d["o"], ws=d["aws"])
+        else:
+            csa.csa_attend(d["q"], d["ck"], d["cv"], d["topk"], d["rk"], d["rv"], m=w.m, W=w.W,
+                           q_pos0=t, raw_pos0=t - w.W + 1, out=d["o"], ws=d["aws"])
+    elif mx8:
+        csa.hca_attend_mxfp8(d["q"], d["ck"], d["cv"], d["cks"], d["cvs"], d["rk"], d["rv"],
+                             m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1, out=d["o"],
+                             ws=d["aws"])
     else:
         csa.hca_attend(d["q"], d["ck"], d["cv"], d["rk"], d["rv"], m=w.m, W=w.W, q_pos0=t,
                        raw_pos0=t - w.W + 1, out=d["o"], ws=d["aws"])
 
 
-@pytest.mark.parametrize("kind", ["csa", "hca"])
+@pytest.mark.parametrize("kind", ["csa", "hca", "csa_mxfp8", "hca_mxfp8"])
 def test_decode_step_graph_replay(kind):
     say("graph replay", kind)
     w, d = _decode_inputs(kind, seed=71)
     _step(kind, w, d)
     torch.cuda.synchronize()
     ref_o = d["o"].clone()
-    ref_tk = d["topk"].clone() if kind == "csa" else None
+    ref_tk = d["topk"].clone() if kind.startswith("csa") else None
     # other eager work between the replays: the same step on other inputs
     w2, d2 = _decode_inputs(kind, seed=72)
     g = torch.cuda.CUDAGraph()
@@ -67,13 +82,13 @@ def test_decode_step_graph_replay(kind):
         _step(kind, w, d)
     for r in range(3):
         d["o"].fill_(0)
-        if kind == "csa":
+        if kind.startswith("csa"):
             d["topk"].fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(d["o"], ref_o), f"replay {r}: attention output differs"
-        if kind == "csa":
+        if kind.startswith("csa"):
             assert torch.equal(d["topk"], ref_tk), f"replay {r}: kept set differs"
         _step(kind, w2, d2)
         torch.cuda.synchronize()
