@@ -5,24 +5,28 @@ CPU-oracle baseline, printed as one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 Workloads (synthetic, seeded, N(0,1); see compressed_sparse_attention_04_amd/inputs.py):
-  pair_prefill_128k  (default) one sequence of 131,072 tokens through a CSA
-                     layer (m=4, 4-head dim-64 MXFP4 indexer, top-512) and
-                     an HCA layer (m'=128), 128 query heads, one shared KV
-                     head, head_dim 128, 128-token window, bf16.  A step
-                     runs every stage of the path: gated compression of
-                     both layers' K and V, MXFP4 encoding of the indexer
-                     keys, indexer score + top-k, CSA attention, HCA
-                     attention.
+  all                (default) hca_decode_1m and csa_decode_1m, then
+                     pair_prefill_128k, in one process.  The line's top-level
+                     value is the prefill rate; "decode" holds one record per
+                     decode workload (rate, rooflines, CPU baseline).
+  pair_prefill_128k  one sequence of 131,072 tokens through a CSA layer (m=4,
+                     4-head dim-64 MXFP4 indexer, top-512) and an HCA layer
+                     (m'=128), 128 query heads, one shared KV head, head_dim
+                     128, 128-token window, bf16.  A step runs every stage of
+                     the path: gated compression of both layers' K and V,
+                     MXFP4 encoding of the indexer keys, indexer score +
+                     top-k, CSA attention, HCA attention.
   csa_prefill_32k    the CSA layer alone at 32,768 tokens.
   hca_decode_1m      32 sequences x 1,048,576 context tokens, m'=128: the
                      decode step (last-token query over all 8,191
                      candidates + window); caches precompressed, untimed.
   csa_decode_1m      16 sequences x 1,048,576 tokens, m=4: indexer over
                      262,112 candidates + top-512 + attention.
+  stack_decode_1m    the decode step of a 61-layer CSA/HCA attention stack.
 
 The timed region is exactly K steps bracketed by synchronisations; stage
 durations come from HIP events recorded on the launch stream.  Decode
-steps rotate over several copies of the caches (> 512 MB in total) so the
+steps rotate over several copies of the caches (> 600 MB in total) so the
 256 MB Infinity Cache cannot hold the working set between steps.
 """
 from __future__ import annotations
@@ -40,7 +44,6 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp4_TFLOPs": 10100.0}
 PIPE_SLICES = 8        # query slices of a pipelined CSA layer (selection | attention)
-DEFAULT = "pair_prefill_128k"
 
 # Kernel sources behind each stage: the HBM traffic recorded in
 # profiles/traffic.json for a stage is reported only while the digest of
@@ -386,97 +389,323 @@ def setup_stack_decode(dev, n_layers=61, B=16):
 
 
 # --------------------------------------------------------------- CPU baseline
-def cpu_baseline(name, budget_s=20.0, n_layers=61):
-    """Time the oracle, unchanged, on a bounded sample of the same workload."""
+def oracle_threads():
+    """Host threads for the oracle: OMP_NUM_THREADS when set, else every core
+    this process may run on."""
+    cores = len(os.sched_getaffinity(0))
+    return max(1, min(cores, int(os.environ.get("OMP_NUM_THREADS", cores))))
+
+
+def stratified_rows(w, n=128, seed=0):
+    """Query rows of a prefill layer for the oracle sample: the first 8, the
+    last 8, 16 around the point where the kept set saturates (n_cand = k; for
+    a dense layer, where the first compressed entry appears), rows at block
+    and window boundaries, and random rows up to n."""
+    T = w.Tq
+    rows = set(range(8)) | set(range(T - 8, T))
+    t = np.arange(T)
+    nc = n_cand(t, w.m, w.W)
+    sat = int(np.argmax(nc >= (w.k if w.kind == "csa" else 1)))
+    rows |= set(range(max(0, sat - 8), min(T, sat + 8)))
+    rows |= {r for r in (w.W - 2, w.W - 1, w.W, w.W + 1) if 0 <= r < T}
+    for c in (1, 2, 3, T // (2 * w.m), T // w.m - 1):          # block ends and starts
+        for r in (c * w.m - 1, c * w.m):
+            if 0 <= r < T:
+                rows.add(r)
+    rng = np.random.default_rng(seed)
+    while len(rows) < n:
+        rows.add(int(rng.integers(0, T)))
+    return np.array(sorted(rows)[:n] if len(rows) > n else sorted(rows), np.int64)
+
+
+def _cpu_prefill(layers, threads):
+    """Per-token oracle seconds of a prefill step: compression of 8,192
+    tokens of K and V per layer, plus index/attend of the stratified rows
+    (every 8th of them at one thread)."""
     import torch
 
     import oracle
     from compressed_sparse_attention_04_amd import inputs as I
-
-    oracle.build()
-    cores = len(os.sched_getaffinity(0))
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    f64 = lambda t: t.to(torch.float64).numpy()
-    rng = np.random.default_rng(0)
-
-    if name in ("pair_prefill_128k", "csa_prefill_32k"):
-        layers = [I.PAIR_CSA_128K, I.PAIR_HCA_128K] if name == "pair_prefill_128k" \
-            else [I.CSA_PREFILL_32K]
-        per_token = 0.0
-        desc = []
-        for w in layers:
-            nrows = 32
-            rows = np.sort(rng.choice(w.Tq, size=nrows, replace=False))
-            q_pos = w.q_pos0 + rows
-            span = min(w.T, 8192)
-            raw = I.draw_raw(w, t0=0, t1=w.T)
-            t0 = time.perf_counter()
-            oracle.compress(f64(raw["k"][:, :span]), f64(raw["gk"][:, :span]), w.m)
-            oracle.compress(f64(raw["v"][:, :span]), f64(raw["gv"][:, :span]), w.m)
-            t_comp = (time.perf_counter() - t0) / span
-            # the sampled rows need the full compressed cache (not timed)
-            ck = oracle.compress(f64(raw["k"]), f64(raw["gk"]), w.m)
-            cv = oracle.compress(f64(raw["v"]), f64(raw["gv"]), w.m)
-            q = f64(I.draw_queries(w, rows=rows))
-            t0 = time.perf_counter()
-            if w.kind == "csa":
-                kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(w)))
-                tk, _ = oracle.index_topk(f64(I.draw_indexer_queries(w, rows=rows)), kc, ks, q_pos,
-                                          w.m, w.W, w.k)
-            else:
-                tk = None
-            oracle.attend(q, ck, cv, tk, f64(raw["k"]), f64(raw["v"]), 0, q_pos, w.m, w.W)
-            t_rows = (time.perf_counter() - t0) / nrows
-            per_token += t_comp + t_rows
-            desc.append(f"{w.name}: compression of {span} tokens + index/attend of {nrows} "
-                        f"random query rows")
-        return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                "sample": "; ".join(desc) + " (per-token times summed over the layers)"}
-
-    def decode_seconds(w):
-        """The oracle's decode step of one sequence of workload w."""
-        ws = w.replace(B=1)
-        t = w.q_pos0
-        ck = f64(I.draw_cache(ws, "ck", w.Nc))
-        cv = f64(I.draw_cache(ws, "cv", w.Nc))
-        rk = f64(I.draw_cache(ws, "rk", w.W))
-        rv = f64(I.draw_cache(ws, "rv", w.W))
-        q = f64(I.draw_queries(ws))
+    f64 = lambda x: x.to(torch.float64).numpy()
+    per_token, desc = 0.0, []
+    for w in layers:
+        rows = stratified_rows(w)
+        if threads == 1:
+            rows = rows[::8]
+        q_pos = w.q_pos0 + rows
+        span = min(w.T, 8192)
+        raw = I.draw_raw(w, t0=0, t1=w.T)
+        t0 = time.perf_counter()
+        oracle.compress(f64(raw["k"][:, :span]), f64(raw["gk"][:, :span]), w.m)
+        oracle.compress(f64(raw["v"][:, :span]), f64(raw["gv"][:, :span]), w.m)
+        t_comp = (time.perf_counter() - t0) / span
+        # the sampled rows need the whole compressed cache (not timed)
+        ck = oracle.compress(f64(raw["k"]), f64(raw["gk"]), w.m)
+        cv = oracle.compress(f64(raw["v"]), f64(raw["gv"]), w.m)
+        q = f64(I.draw_queries(w, rows=rows))
+        tk = None
+        if w.kind == "csa":
+            kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(w)))
+            qi = f64(I.draw_indexer_queries(w, rows=rows))
         t0 = time.perf_counter()
         if w.kind == "csa":
-            kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(ws)))
-            t0 = time.perf_counter()
-            tk, _ = oracle.index_topk(f64(I.draw_indexer_queries(ws)), kc, ks, [t], w.m, w.W, w.k)
-        else:
-            tk = None
-        oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
-        return time.perf_counter() - t0
+            tk, _ = oracle.index_topk(qi, kc, ks, q_pos, w.m, w.W, w.k)
+        oracle.attend(q, ck, cv, tk, f64(raw["k"]), f64(raw["v"]), 0, q_pos, w.m, w.W)
+        per_token += t_comp + (time.perf_counter() - t0) / len(rows)
+        desc.append(f"{w.name}: compression of {span} tokens + index/attend of {len(rows)} "
+                    "stratified rows")
+    return per_token, "; ".join(desc)
 
+
+def _cpu_decode(w, S):
+    """Oracle seconds of the decode step of S sequences of workload w (every
+    candidate scored and selected; attention over the kept entries or all
+    candidates plus the window).  Cache rows that the step does not read are
+    left untouched (zero pages), the rows it reads are drawn."""
+    import torch
+
+    import oracle
+    from compressed_sparse_attention_04_amd import inputs as I
+    f64 = lambda x: x.to(torch.float64).numpy()
+    ws = w.replace(B=S)
+    t = w.q_pos0
+    q = f64(I.draw_queries(ws))
+    rk = f64(I.draw_cache(ws, "rk", w.W))
+    rv = f64(I.draw_cache(ws, "rv", w.W))
+    nc = int(n_cand([t], w.m, w.W)[0])
+    tk = None
+    el = 0.0
+    if w.kind == "csa":
+        kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(ws)))
+        qi = f64(I.draw_indexer_queries(ws))
+        t0 = time.perf_counter()
+        tk, _ = oracle.index_topk(qi, kc, ks, [t], w.m, w.W, w.k)
+        el += time.perf_counter() - t0
+        ck = np.zeros((S, w.Nc, w.D))
+        cv = np.zeros((S, w.Nc, w.D))
+        vals_k = f64(I.draw_cache(ws, "ck", w.k))
+        vals_v = f64(I.draw_cache(ws, "cv", w.k))
+        for b in range(S):
+            sel = tk[b, 0][tk[b, 0] >= 0]
+            ck[b, sel] = vals_k[b, :len(sel)]
+            cv[b, sel] = vals_v[b, :len(sel)]
+    else:
+        ck = f64(I.draw_cache(ws, "ck", nc))
+        cv = f64(I.draw_cache(ws, "cv", nc))
+    t0 = time.perf_counter()
+    oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
+    return el + time.perf_counter() - t0
+
+
+def cpu_baseline(name, n_layers=61):
+    """The oracle, unchanged, timed on a bounded sample of the same workload,
+    with every host thread and with one thread."""
+    import oracle
+    from compressed_sparse_attention_04_amd import inputs as I
+
+    oracle.build()
+    threads = oracle_threads()
+    res = {}
+    for th in sorted({threads, 1}, reverse=True):
+        oracle.set_threads(th)
+        if name in ("pair_prefill_128k", "csa_prefill_32k"):
+            layers = [I.PAIR_CSA_128K, I.PAIR_HCA_128K] if name == "pair_prefill_128k" \
+                else [I.CSA_PREFILL_32K]
+            sec, sample = _cpu_prefill(layers, th)
+            res[th] = (1.0 / sec, sample + " (per-token times summed over the layers)")
+        elif name == "stack_decode_1m":
+            from compressed_sparse_attention_04_amd import binding as csa
+            kinds = csa.csa_layer_schedule(n_layers)
+            ncsa = kinds.count(csa.CSA_LAYER_CSA)
+            S = min(th, I.CSA_DECODE_1M.B)
+            tc = _cpu_decode(I.CSA_DECODE_1M, S) / S
+            th_ = _cpu_decode(I.HCA_DECODE_1M, S) / S
+            res[th] = (1.0 / (ncsa * tc + (n_layers - ncsa) * th_),
+                       f"decode step of {S} sequences of one CSA and one HCA layer, per "
+                       f"sequence, scaled to {ncsa} CSA + {n_layers - ncsa} HCA layers")
+        else:
+            w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
+            S = min(th, w.B)
+            res[th] = (S / _cpu_decode(w, S),
+                       f"full decode step of {S} of the {w.B} sequences (every candidate "
+                       "scored and selected where the layer selects)")
+    oracle.set_threads(threads)
+    v, sample = res[threads]
+    out = {"value": v, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample}
+    if threads != 1:
+        v1, s1 = res[1]
+        out["single_thread"] = {"value": v1, "unit": "tokens/s", "cores": 1, "sample": s1}
+    return out
+
+
+# --------------------------------------------------------------- timing
+def time_stages(stages, steps, warmup):
+    """W untimed steps, then exactly `steps` timed steps bracketed by device
+    synchronisations; per-stage HIP events on the launch stream.  Returns
+    (ms per step from the host clock, mean ms per stage)."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for si, st in enumerate(stages):
+            st.fn()
+            if ev is not None:
+                ev[si].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        starts[s].record(stream)
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = np.zeros(len(stages))
+    for s in range(steps):
+        prev = starts[s]
+        for si in range(len(stages)):
+            stage_ms[si] += prev.elapsed_time(evs[s][si])
+            prev = evs[s][si]
+    return elapsed * 1e3 / steps, stage_ms / steps
+
+
+def kernel_roofline(stages, stage_ms, workload, traffic_ok):
+    """Roofline of the stage with the largest mean time (one entry point: its
+    kernels, and a decode attention's split combine, between two events)."""
+    dom = int(np.argmax(stage_ms))
+    d = stages[dom]
+    sec = stage_ms[dom] / 1e3
+    if d.peak_key == "hbm_GBps":
+        roof = {"bound": "hbm", "achieved": d.bytes / sec / 1e9, "peak": PEAK["hbm_GBps"],
+                "unit": "GB/s"}
+    else:
+        # a pipelined CSA layer runs FP4 indexer and bf16 attention MFMAs side by
+        # side: its FP4 flops count at the bf16/FP4 peak ratio
+        eq = d.flops + d.fp4_flops * PEAK["bf16_TFLOPs"] / PEAK["fp4_TFLOPs"]
+        roof = {"bound": "mfma", "achieved": eq / sec / 1e12, "peak": PEAK[d.peak_key],
+                "unit": "TFLOP/s"}
+        if d.fp4_flops:
+            roof["convention"] = ("bf16-equivalent: attention bf16 flops + indexer FP4 flops x "
+                                  "2.5/10.1")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(workload, d.name) if traffic_ok else None
+    roof["kernel"] = d.name
+    roof["ms_per_launch"] = float(stage_ms[dom])
+    roof["scope"] = "dominant stage (its kernels between two HIP events on the launch stream)"
+    return roof
+
+
+def stage_table(stages, stage_ms):
+    info = {}
+    for st, ms in zip(stages, stage_ms):
+        e = {"ms": round(float(ms), 4)}
+        if st.flops:
+            e["TFLOP/s"] = round(st.flops / (ms / 1e3) / 1e12, 2)
+        if st.fp4_flops:
+            e["indexer FP4 TFLOP/s"] = round(st.fp4_flops / (ms / 1e3) / 1e12, 2)
+        if st.bytes:
+            e["GB/s"] = round(st.bytes / (ms / 1e3) / 1e9, 1)
+        info[st.name] = e
+    return info
+
+
+def prefill_step_roofline(stages, ms_per_step):
+    """Whole-step MFMA fraction: the time every stage's MFMA work would take
+    at its dtype's dense peak (bf16 attention, FP4 indexer), over the
+    measured step time."""
+    ideal = 0.0
+    for st in stages:
+        if st.peak_key in ("bf16_TFLOPs", "fp4_TFLOPs"):
+            ideal += st.flops / (PEAK[st.peak_key] * 1e12)
+        ideal += st.fp4_flops / (PEAK["fp4_TFLOPs"] * 1e12)
+    return {"frac": ideal / (ms_per_step / 1e3), "ideal_ms": ideal * 1e3,
+            "scope": "whole step: sum of (flops / dense peak of their dtype) over the "
+                     "measured step time"}
+
+
+def run_prefill(dev, name, args, steps, warmup):
+    from compressed_sparse_attention_04_amd import inputs as I
+    if name == "pair_prefill_128k":
+        layers = [I.PAIR_CSA_128K, I.PAIR_HCA_128K]
+        wl = {"workload": "csa_hca_layer_pair_prefill", "seq_len": 131072, "batch": 1,
+              "heads": 128, "kv_heads": 1, "head_dim": 128, "m_csa": 4, "m_hca": 128,
+              "top_k": 512, "indexer": "4x64 MXFP4", "window": 128}
+    else:
+        layers = [I.CSA_PREFILL_32K]
+        wl = {"workload": "csa_prefill", "seq_len": 32768, "batch": 1, "heads": 128,
+              "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
+              "window": 128}
+    stages, tokens, notes = setup_prefill(dev, layers, args.shared_kv, args.kv_format,
+                                          args.pipeline)
+    if args.pipeline and args.kv_format == "bf16":
+        wl["csa_schedule"] = (f"selection and attention pipelined over {PIPE_SLICES} query "
+                              "slices on two streams (csa_index_attend)")
+    ms, stage_ms = time_stages(stages, steps, warmup)
+    traffic_ok = not args.shared_kv and args.kv_format == "bf16"
+    rec = {"metric": "prefill tokens/s", "value": round(tokens / (ms / 1e3), 1),
+           "unit": "tokens/s", "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+           "config": wl, "roofline": kernel_roofline(stages, stage_ms, name, traffic_ok)}
+    rec["roofline"]["step"] = prefill_step_roofline(stages, ms)
+    rec["stages"] = stage_table(stages, stage_ms)
+    rec.update(notes)
+    return rec
+
+
+def run_decode(dev, name, args, steps, warmup):
+    import torch
+    from compressed_sparse_attention_04_amd import inputs as I
     if name == "stack_decode_1m":
-        from compressed_sparse_attention_04_amd import binding as csa
-        kinds = csa.csa_layer_schedule(n_layers)
-        ncsa = kinds.count(csa.CSA_LAYER_CSA)
-        t_csa = decode_seconds(I.CSA_DECODE_1M)
-        t_hca = decode_seconds(I.HCA_DECODE_1M)
-        return {"value": 1.0 / (ncsa * t_csa + (n_layers - ncsa) * t_hca), "unit": "tokens/s",
-                "cores": threads, "kind": "oracle",
-                "sample": f"one sequence's decode step of one CSA and one HCA layer, scaled to "
-                          f"{ncsa} CSA + {n_layers - ncsa} HCA layers"}
-    w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
-    el = decode_seconds(w)
-    return {"value": 1.0 / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "decode step of 1 sequence (caches drawn at the workload's shapes)"}
+        stages, tokens, notes = setup_stack_decode(dev, args.layers)
+        wc = I.CSA_DECODE_1M
+        wl = {"workload": "attention_stack_decode_1m_ctx", "context": wc.T, "batch": tokens,
+              "layers": notes["layers"], "csa_layers": notes["csa_layers"],
+              "hca_layers": notes["hca_layers"], "heads": wc.H, "kv_heads": 1,
+              "head_dim": wc.D, "m_csa": 4, "m_hca": 128, "top_k": wc.k, "window": wc.W}
+        metric = "1M-ctx decode tokens/s/GPU (attention stack)"
+    else:
+        w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
+        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv,
+                                             kv_fmt=args.kv_format)
+        wl = {"workload": name.replace("_1m", "") + "_1m_ctx", "context": w.T,
+              "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
+              "top_k": w.k if w.kind == "csa" else None, "window": w.W}
+        metric = "1M-ctx decode tokens/s/GPU"
+    ms, stage_ms = time_stages(stages, steps, warmup)
+    traffic_ok = not args.shared_kv and args.kv_format == "bf16"
+    hbm = notes["step_bytes"] / (ms / 1e3) / 1e9
+    rec = {"metric": metric, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
+           "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "config": wl,
+           "roofline": kernel_roofline(stages, stage_ms, name, traffic_ok)}
+    rec["roofline"]["step"] = {"frac": hbm / PEAK["hbm_GBps"], "achieved_GBps": hbm,
+                               "scope": "whole step: algorithmic bytes over the measured "
+                                        "step time"}
+    rec["stages"] = stage_table(stages, stage_ms)
+    rec.update(notes)
+    del stages
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 # --------------------------------------------------------------- main
+WORKLOADS = ["all", "pair_prefill_128k", "csa_prefill_32k", "hca_decode_1m", "csa_decode_1m",
+             "stack_decode_1m"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps of the prefill workload (default 10); the decode "
+                         "workloads time max(steps, 100) steps")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default=DEFAULT,
-                    choices=["pair_prefill_128k", "csa_prefill_32k", "hca_decode_1m",
-                             "csa_decode_1m", "stack_decode_1m"])
+    ap.add_argument("--workload", default="all", choices=WORKLOADS,
+                    help="all (default): hca_decode_1m, csa_decode_1m and pair_prefill_128k "
+                         "in one process, one JSON line")
     ap.add_argument("--layers", type=int, default=61,
                     help="layers of the stack_decode_1m workload (default 61)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -495,6 +724,14 @@ def main():
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU mode (sequences or "
+              "query ranges would shard across GPUs); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "stack_decode_1m" and (args.kv_format != "bf16" or args.shared_kv):
+        print("stack_decode_1m runs bf16 caches with separate K and V", file=sys.stderr)
+        sys.exit(2)
     if args.calibrate_copy:
         import torch
         n = 256 << 20
@@ -506,139 +743,45 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
         return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU mode (sequences or "
-              "query ranges would shard across GPUs); run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
 
     import torch
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    from compressed_sparse_attention_04_amd import inputs as I
+    steps = args.steps if args.steps is not None else 10
+    warmup = args.warmup if args.warmup is not None else 2
+    dsteps, dwarm = max(steps, 100), max(warmup, 5)
+    cpu = not args.no_cpu_baseline
+    storage = {"kv": "one vector as key and value" if args.shared_kv else "separate K and V",
+               "kv_format": ("compressed entries MXFP8 (E4M3), window bf16"
+                             if args.kv_format == "mxfp8" else "bf16")}
 
-    decode = args.workload.endswith("decode_1m")
-    steps = args.steps if args.steps is not None else (50 if decode else 10)
-    warmup = args.warmup if args.warmup is not None else (5 if decode else 2)
-
-    if args.workload == "pair_prefill_128k":
-        stages, tokens, notes = setup_prefill(dev, [I.PAIR_CSA_128K, I.PAIR_HCA_128K],
-                                              args.shared_kv, args.kv_format,
-                                              args.pipeline)
-        wl = {"workload": "csa_hca_layer_pair_prefill", "seq_len": 131072, "batch": 1,
-              "heads": 128, "kv_heads": 1, "head_dim": 128, "m_csa": 4, "m_hca": 128,
-              "top_k": 512, "indexer": "4x64 MXFP4", "window": 128}
-        metric, unit = "prefill tokens/s", "tokens/s"
-    elif args.workload == "csa_prefill_32k":
-        stages, tokens, notes = setup_prefill(dev, [I.CSA_PREFILL_32K], args.shared_kv,
-                                              args.kv_format, args.pipeline)
-        wl = {"workload": "csa_prefill", "seq_len": 32768, "batch": 1, "heads": 128,
-              "kv_heads": 1, "head_dim": 128, "m": 4, "top_k": 512, "indexer": "4x64 MXFP4",
-              "window": 128}
-        metric, unit = "prefill tokens/s", "tokens/s"
-    elif args.workload == "stack_decode_1m":
-        if args.kv_format != "bf16" or args.shared_kv:
-            print("stack_decode_1m runs bf16 caches with separate K and V", file=sys.stderr)
-            sys.exit(2)
-        stages, tokens, notes = setup_stack_decode(dev, args.layers)
-        wc = I.CSA_DECODE_1M
-        wl = {"workload": "attention_stack_decode_1m_ctx", "context": wc.T, "batch": tokens,
-              "layers": notes["layers"], "csa_layers": notes["csa_layers"],
-              "hca_layers": notes["hca_layers"], "heads": wc.H, "kv_heads": 1,
-              "head_dim": wc.D, "m_csa": 4, "m_hca": 128, "top_k": wc.k, "window": wc.W}
-        metric, unit = "1M-ctx decode tokens/s/GPU (attention stack)", "tokens/s"
+    decode = {}
+    if args.workload == "all":
+        for name in ("hca_decode_1m", "csa_decode_1m"):
+            decode[name] = run_decode(dev, name, args, dsteps, dwarm)
+        rec = run_prefill(dev, "pair_prefill_128k", args, steps, warmup)
+        name = "pair_prefill_128k"
+    elif args.workload.endswith("decode_1m"):
+        name = args.workload
+        rec = run_decode(dev, name, args, dsteps, dwarm)
     else:
-        w = I.HCA_DECODE_1M if args.workload == "hca_decode_1m" else I.CSA_DECODE_1M
-        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv,
-                                             kv_fmt=args.kv_format)
-        wl = {"workload": args.workload.replace("_1m", "") + "_1m_ctx", "context": w.T,
-              "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
-              "top_k": w.k if w.kind == "csa" else None, "window": w.W}
-        metric, unit = "1M-ctx decode tokens/s/GPU", "tokens/s"
-    if not decode and args.pipeline and args.kv_format == "bf16":
-        wl["csa_schedule"] = (f"selection and attention pipelined over {PIPE_SLICES} query "
-                              "slices on two streams (csa_index_attend)")
-    wl["kv"] = "one vector as key and value" if args.shared_kv else "separate K and V"
-    wl["kv_format"] = ("compressed entries MXFP8 (E4M3), window bf16" if args.kv_format == "mxfp8"
-                       else "bf16")
-
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        for si, st in enumerate(stages):
-            st.fn()
-            if ev is not None:
-                ev[si].record(stream)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(steps)]
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        starts[s].record(stream)
-        step(evs[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    stage_ms = np.zeros(len(stages))
-    for s in range(steps):
-        prev = starts[s]
-        for si in range(len(stages)):
-            stage_ms[si] += prev.elapsed_time(evs[s][si])
-            prev = evs[s][si]
-    stage_ms /= steps
-    ms_per_step = elapsed * 1e3 / steps
-    value = tokens / (ms_per_step / 1e3)
-
-    dom = int(np.argmax(stage_ms))
-    d = stages[dom]
-    sec = stage_ms[dom] / 1e3
-    if d.peak_key == "hbm_GBps":
-        roof = {"bound": "hbm", "achieved": d.bytes / sec / 1e9, "peak": PEAK["hbm_GBps"],
-                "unit": "GB/s"}
+        name = args.workload
+        rec = run_prefill(dev, name, args, steps, warmup)
+    rec["config"].update(storage)
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline(name, n_layers=args.layers)
+        for dn, d in decode.items():
+            d["cpu_baseline"] = cpu_baseline(dn)
     else:
-        # a pipelined CSA layer runs FP4 indexer and bf16 attention MFMAs side by
-        # side: its FP4 flops count at the bf16/FP4 peak ratio, so achieved/peak
-        # is the sum over both of (flops / own peak) / time
-        eq = d.flops + d.fp4_flops * PEAK["bf16_TFLOPs"] / PEAK["fp4_TFLOPs"]
-        roof = {"bound": "mfma", "achieved": eq / sec / 1e12, "peak": PEAK[d.peak_key],
-                "unit": "TFLOP/s"}
-        if d.fp4_flops:
-            roof["convention"] = ("bf16-equivalent: attention bf16 flops + indexer FP4 flops x "
-                                  "2.5/10.1")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    # (counter passes exist for the default inputs only)
-    roof["traffic"] = (None if args.shared_kv or args.kv_format != "bf16"
-                       else recorded_traffic(args.workload, d.name))
-    roof["kernel"] = d.name
-    roof["ms_per_launch"] = stage_ms[dom]
-
-    stage_info = {}
-    for st, ms in zip(stages, stage_ms):
-        e = {"ms": round(float(ms), 4)}
-        if st.flops:
-            e["TFLOP/s"] = round(st.flops / (ms / 1e3) / 1e12, 2)
-        if st.fp4_flops:
-            e["indexer FP4 TFLOP/s"] = round(st.fp4_flops / (ms / 1e3) / 1e12, 2)
-        if st.bytes:
-            e["GB/s"] = round(st.bytes / (ms / 1e3) / 1e9, 1)
-        stage_info[st.name] = e
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload, n_layers=args.layers)
-
-    rec = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
-           "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded N(0,1))", "config": wl, "roofline": roof,
-           "cpu_baseline": cpu, "stages": stage_info}
-    rec.update({k: v for k, v in notes.items()})
-    print(json.dumps(rec), flush=True)
+        rec["cpu_baseline"] = None
+    out = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"),
+           "n_gpus": 1, "steps": rec.pop("steps"), "warmup": rec.pop("warmup"),
+           "ms_per_step": rec.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1))"}
+    out.update(rec)
+    if decode:
+        out["decode"] = decode
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

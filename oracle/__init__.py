@@ -226,3 +226,10 @@ def attend(q, ck, cv, topk, rk, rv, raw_pos0: int, q_pos, m: int, W: int,
                                _p(cv), None if tk is None else _p(tk), _p(rk), _p(rv),
                                raw_pos0, raw_len, _p(o)), "attend")
     return o
+
+
+def set_threads(n: int) -> None:
+    """Host threads that the oracle's parallel row loops use from now on (the
+    OpenMP runtime the oracle is linked against; no arithmetic changes)."""
+    lib()
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
