@@ -123,7 +123,20 @@ def _stream(t: torch.Tensor, stream) -> int | None:
     return None
 
 
-def _workspace(ws, device, query):
+def _keep(t, stream):
+    """A tensor this module allocated on the current stream but handed to
+    kernels on another stream: tell the caching allocator that the other
+    stream uses it, so its memory is not reused before that work is done."""
+    if t is None or stream is None or not t.is_cuda:
+        return t
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+        stream, device=t.device)
+    if s.cuda_stream != torch.cuda.current_stream(t.device).cuda_stream:
+        t.record_stream(s)
+    return t
+
+
+def _workspace(ws, device, query, stream=None):
     """A workspace the caller passed is handed over whole (the library
     checks its size); otherwise one of query() bytes is allocated."""
     if ws is not None:
@@ -131,14 +144,14 @@ def _workspace(ws, device, query):
     nbytes = query()
     if nbytes == 0:
         return None, 0
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    return _keep(torch.empty(nbytes, dtype=torch.uint8, device=device), stream), nbytes
 
 
 def hca_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out=None, stream=None):
     """Softmax-gated pooling: x [B,T,C], gate [B,T,1|C] -> [B, T//m, C]."""
     B, T, C = x.shape
     if out is None:
-        out = torch.empty((B, T // m, C), dtype=x.dtype, device=x.device)
+        out = _keep(torch.empty((B, T // m, C), dtype=x.dtype, device=x.device), stream)
     _call("hca_compress", _dt(x), B, T, C, m, _ptr(x), _ptr(gate), gate.shape[-1], _ptr(out),
           _stream(x, stream))
     return out
@@ -164,9 +177,11 @@ def csa_quantize_mxfp4(x: torch.Tensor, codes=None, scales=None, stream=None):
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
     if codes is None:
-        codes = torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8, device=x.device)
+        codes = _keep(torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8, device=x.device),
+                      stream)
     if scales is None:
-        scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+        scales = _keep(torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device),
+                       stream)
     _call("csa_quantize_mxfp4", _dt(x), rows, d, _ptr(x), _ptr(codes), _ptr(scales),
           _stream(x, stream))
     return codes, scales
@@ -185,9 +200,9 @@ def csa_index_topk(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.T
     B, Tq, HI, dI = q_idx.shape
     Nc = k_codes.shape[1]
     ws, wsb = _workspace(ws, q_idx.device,
-        lambda: csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0))
+        lambda: csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0), stream)
     if topk is None:
-        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+        topk = _keep(torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device), stream)
     _call("csa_index_topk", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
           _ptr(k_codes), _ptr(k_scales), _ptr(topk), _ptr(ws), wsb, _stream(q_idx, stream))
     return topk
@@ -206,9 +221,10 @@ def csa_attend(q, ck, cv, topk, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0
     Nc = ck.shape[1]
     k = topk.shape[2]
     raw_len = rk.shape[1]
-    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(_dt(q), B, Tq, H, D, k, W))
+    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(_dt(q), B, Tq, H, D, k, W),
+                          stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _keep(torch.empty_like(q), stream)
     _call("csa_attend", _dt(q), B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
           _ptr(cv), _ptr(topk), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws),
           wsb, _stream(q, stream))
@@ -228,9 +244,9 @@ def hca_attend(q, ck, cv, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0: int,
     Nc = ck.shape[1]
     raw_len = rk.shape[1]
     ws, wsb = _workspace(ws, q.device,
-        lambda: hca_attend_workspace(_dt(q), B, Tq, H, D, Nc, m, W, q_pos0))
+        lambda: hca_attend_workspace(_dt(q), B, Tq, H, D, Nc, m, W, q_pos0), stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _keep(torch.empty_like(q), stream)
     _call("hca_attend", _dt(q), B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck),
           _ptr(cv), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws), wsb,
           _stream(q, stream))
@@ -242,9 +258,10 @@ def csa_quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
     if codes is None:
-        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        codes = _keep(torch.empty(x.shape, dtype=torch.uint8, device=x.device), stream)
     if scales is None:
-        scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+        scales = _keep(torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device),
+                       stream)
     _call("csa_quantize_mxfp8", _dt(x), rows, d, _ptr(x), _ptr(codes), _ptr(scales),
           _stream(x, stream))
     return codes, scales
@@ -259,9 +276,10 @@ def csa_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, topk, rk, rv, *, m: int, W
     Nc = ck.shape[1]
     k = topk.shape[2]
     raw_len = rk.shape[1]
-    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(CSA_BF16, B, Tq, H, D, k, W))
+    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(CSA_BF16, B, Tq, H, D, k, W),
+                          stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _keep(torch.empty_like(q), stream)
     _call("csa_attend_mxfp8", B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
           _ptr(cv), _ptr(ck_scales), _ptr(cv_scales), _ptr(topk), _ptr(rk), _ptr(rv), raw_pos0,
           raw_len, _ptr(out), _ptr(ws), wsb, _stream(q, stream))
@@ -275,9 +293,9 @@ def hca_attend_mxfp8(q, ck, cv, ck_scales, cv_scales, rk, rv, *, m: int, W: int,
     Nc = ck.shape[1]
     raw_len = rk.shape[1]
     ws, wsb = _workspace(ws, q.device,
-        lambda: hca_attend_workspace(CSA_BF16, B, Tq, H, D, Nc, m, W, q_pos0))
+        lambda: hca_attend_workspace(CSA_BF16, B, Tq, H, D, Nc, m, W, q_pos0), stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _keep(torch.empty_like(q), stream)
     _call("hca_attend_mxfp8", B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck), _ptr(cv),
           _ptr(ck_scales), _ptr(cv_scales), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out),
           _ptr(ws), wsb, _stream(q, stream))
@@ -321,7 +339,7 @@ def csa_stack_attend(layers, *, W: int, k: int, q_pos0: int, raw_pos0: int, scal
     raw_len = layers[0]["rk"].shape[1]
     arr = _layer_array(layers)
     ws, wsb = _workspace(ws, q.device,
-        lambda: csa_stack_workspace(_dt(q), layers, B, Tq, H, D, HI, dI, W, k, q_pos0))
+        lambda: csa_stack_workspace(_dt(q), layers, B, Tq, H, D, HI, dI, W, k, q_pos0), stream)
     _call("csa_stack_attend", _dt(q), len(layers), ctypes.cast(arr, ctypes.c_void_p), B, Tq, H, D,
           HI, dI, W, k, q_pos0, scale, raw_pos0, raw_len, _ptr(ws), wsb, _stream(q, stream))
 
@@ -351,13 +369,17 @@ def csa_index_attend(q, q_idx, k_codes, k_scales, ck, cv, rk, rv, *, m: int, W: 
         if dev not in _aux_streams:
             _aux_streams[dev] = torch.cuda.Stream(device=dev)
         aux_stream = _aux_streams[dev]
+    own_ws = ws is None
     ws, wsb = _workspace(ws, q.device,
         lambda: csa_index_attend_workspace(_dt(q), B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0,
-                                        n_chunks))
+                                        n_chunks), stream)
+    if own_ws:
+        _keep(ws, aux_stream)            # the selection slices run on aux_stream
     if topk is None:
-        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=q.device)
+        topk = _keep(_keep(torch.empty((B, Tq, k), dtype=torch.int32, device=q.device), stream),
+                     aux_stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _keep(torch.empty_like(q), stream)
     _call("csa_index_attend", _dt(q), B, Tq, H, D, HI, dI, Nc, m, W, k, q_pos0, scale, _ptr(q),
           _ptr(q_idx), _ptr(k_codes), _ptr(k_scales), _ptr(ck), _ptr(cv), _ptr(rk), _ptr(rv),
           raw_pos0, raw_len, _ptr(topk), _ptr(out), n_chunks, _ptr(ws), wsb, _stream(q, stream),

@@ -361,6 +361,21 @@ static SliceWs slice_ws(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t 
     return r;
 }
 
+// The events of one pipelined call: created at its start, destroyed when it
+// returns (no event outlives the call).
+struct CallEvents {
+    hipEvent_t e[65];
+    int n = 0;
+    bool make(int count) {
+        for (; n < count; ++n)
+            if (hipEventCreateWithFlags(&e[n], hipEventDisableTiming) != hipSuccess) return false;
+        return true;
+    }
+    ~CallEvents() {
+        for (int i = 0; i < n; ++i) hipEventDestroy(e[i]);
+    }
+};
+
 static csa_status index_attend_args(const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
                                     int64_t H, int64_t D, int64_t HI, int64_t dI, int64_t Nc,
                                     int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
@@ -413,27 +428,23 @@ csa_status csa_index_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int6
     if (B == 0 || Tq == 0) return ok();
     void* iws = ws;
     void* aws = w.attend ? (void*)((char*)ws + align256(w.index)) : nullptr;
-    // events of the slices, kept for the life of the thread
-    // (made on the device current at the thread's first call there)
-    thread_local hipEvent_t ev[65];
-    thread_local int ev_dev = -1;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(CSA_EDEVICE, "%s: no device", fn);
-    if (dev != ev_dev) {
-        for (hipEvent_t& e : ev)
-            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-                return fail(CSA_EDEVICE, "%s: hipEventCreate failed", fn);
-        ev_dev = dev;
-    }
     const bool two = aux_stream != stream;
+    const int64_t per = (Tq + n_chunks - 1) / n_chunks;   // rows per slice
+    const int n_slices = (int)((Tq + per - 1) / per);
+    // events of this call (one per slice, one for the start), made here and
+    // destroyed on return: a destroyed event that is still pending is
+    // released by the runtime once it completes, and the waits already
+    // queued on it stand
+    CallEvents ev;
+    const int n_ev = two ? n_slices + 1 : 0;
+    if (!ev.make(n_ev)) return fail(CSA_EDEVICE, "%s: hipEventCreate failed", fn);
     hipStream_t is = two ? aux_stream : stream;
     if (two) {
         // the selection stream starts after everything already queued on stream
-        if (hipEventRecord(ev[64], stream) != hipSuccess ||
-            hipStreamWaitEvent(is, ev[64], 0) != hipSuccess)
+        if (hipEventRecord(ev.e[n_ev - 1], stream) != hipSuccess ||
+            hipStreamWaitEvent(is, ev.e[n_ev - 1], 0) != hipSuccess)
             return fail(CSA_EDEVICE, "%s: stream ordering failed", fn);
     }
-    const int64_t per = (Tq + n_chunks - 1) / n_chunks;
     const int64_t esz = dt == CSA_F32 ? 4 : 2;
     const char* qb = (const char*)q;
     const char* qib = (const char*)q_idx;
@@ -453,14 +464,14 @@ csa_status csa_index_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int6
                 (int)dt, csa::plan_index(1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a),
                 1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a, qib + r0 * HI * dI * esz,
                 kcb, ksb, topk + r0 * k, iws, is);
-            if (e == hipSuccess && two) e = hipEventRecord(ev[c], is);
+            if (e == hipSuccess && two) e = hipEventRecord(ev.e[c], is);
             if (e != hipSuccess) return launched(e, fn);
         }
         c = 0;
         for (int64_t a = 0; a < Tq; a += per, ++c) {
             const int64_t rows = Tq - a < per ? Tq - a : per;
             const int64_t r0 = b * Tq + a;
-            hipError_t e = two ? hipStreamWaitEvent(stream, ev[c], 0) : hipSuccess;
+            hipError_t e = two ? hipStreamWaitEvent(stream, ev.e[c], 0) : hipSuccess;
             if (e == hipSuccess)
                 e = csa::launch_attend((int)dt, slice_attend_plan(dt, B, Tq, rows, H, D, k, W), 1,
                                        rows, H, D, Nc, m, W, k, q_pos0 + a, scale,

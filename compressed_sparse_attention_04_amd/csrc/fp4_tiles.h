@@ -95,4 +95,18 @@ __device__ __forceinline__ uint32_t score_key(const f32x16& acc, int u) {
     return __float_as_uint(s);
 }
 
+// The order keys of every slot of a tile, formed by all lanes: each key
+// passes through an empty asm statement before any lane-dependent branch of
+// the caller, so the MFMA that produces the tile cannot be moved into a
+// branch that only some lanes take (an MFMA issued with part of EXEC off
+// does not give every lane its full result).
+template <int HI, int NU>
+__device__ __forceinline__ void tile_keys(const f32x16& acc, uint32_t (&key)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        key[u] = score_key<HI>(acc, u);
+        asm volatile("" : "+v"(key[u]));
+    }
+}
+
 }  // namespace csa

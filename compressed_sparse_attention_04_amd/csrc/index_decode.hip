@@ -3,135 +3,140 @@
 // (score every compressed entry, keep the top k); ai-papers.net, hybrid
 // attention section (the FP4 indexer scans the already 4x shorter sequence).
 //
-// The FP4 key stream dominates (34 bytes per candidate at dI = 64), so the
-// work is spread over many blocks that each read one chunk of keys once:
-//   k_dscore : scores of <= 8 query rows against one chunk (scaled FP4
-//              MFMA), written as fp32 to the workspace, plus the level-1
-//              threshold histogram of each row (LDS, then global atomics);
-//   k_dcollect: blocks over (chunk of 4096 stored scores, row) find the
-//              threshold range from the row's histogram, write the chunk's
-//              bitmap words of the surely kept keys (above the range) and
-//              put the keys inside the range in the chunk's own slots of the
-//              row's buffer (no global atomics: same-address device atomics
-//              from every chunk would serialise);
-//   k_dfinal : one block per row resolves the range exactly from the buffer
-//              (or, when the range holds too many keys, narrows it further
-//              by scanning the stored scores) and emits the kept indices in
-//              ascending order (score desc, index asc, as everywhere).
+// The FP4 key stream dominates (34 bytes per candidate at dI = 64), so it is
+// read once, by many blocks, and no score goes back to HBM:
+//   k_dscan : a block per (chunk of ch candidates, sequence) scores the
+//             chunk for every row of the sequence (scaled FP4 MFMA) into
+//             LDS, with each row's level-1 histogram.  Each row keeps a
+//             threshold-closed list: every key >= tau, where tau is 0 (the
+//             whole chunk fits the list's cap slots) or the upper edge of
+//             the level-1 bin at which the list would overflow.  The list
+//             (key, index) in ascending index order and (count, tau) go to
+//             the workspace.
+//   k_dmerge : a block per row selects the exact top k of the union U of
+//             the row's lists.  That is the row's top k whenever every chunk
+//             that left keys out has tau <= the k-th key of U: a key left
+//             out is then below k keys of U, so it is not among the top k.
+//             Otherwise (heavy ties, scores clustered in one chunk) the
+//             block finds the top k exactly over all candidates, rescoring
+//             the keys pass by pass (level-1 histogram, narrowed ranges,
+//             collection).
+// The order is the one used everywhere: score desc, index asc; the output
+// lists the kept indices in ascending order, -1 padded.
 #include "internal.h"
 #include "mxfp4.h"
+#include "select.h"
 #include "wave_select.h"
 #include "fp4_tiles.h"
 
 namespace csa {
 
-constexpr int DS_NT = 256;
-constexpr int DS_QT = 8;
-constexpr int DS_CH = 4096;            // candidates per scoring block
-constexpr int DL_NT = 1024;
-constexpr int DL_CAP = 1024;           // collected keys per row
-constexpr int DL_MAXW = 8192;          // bitmap words -> 262144 candidates
-constexpr int DC_CH_ = 4096;           // stored scores per collecting block
-constexpr int DC_NB = DL_MAXW * 32 / DC_CH_;   // collecting blocks per row (64)
-constexpr int DC_SLOTS = DL_CAP / DC_NB;       // buffer slots per collecting block (16)
+constexpr int DS_NT = 256;             // threads of a scanning block
+constexpr int DS_QT = 8;               // rows (queries x sequence) per sequence at most
+constexpr int DS_KEYS = 8192;          // LDS key words of a scanning block (all its rows)
+constexpr int DM_NT = 1024;            // threads of a merging block
+constexpr int DM_UCAP = 8192;          // union capacity (chunks x cap)
+constexpr int DM_MAXW = 8192;          // bitmap words of the exact path -> 262144 candidates
+constexpr int DM_CAP = 1024;           // collected keys of the exact path
+constexpr int DM_PASSES = 4;           // narrowing passes of the exact path (see below)
 
-// score rows are padded to whole 16-byte vectors
-__host__ __device__ __forceinline__ int64_t score_stride(int64_t nc) { return (nc + 3) & ~(int64_t)3; }
-
-__global__ void k_zero_u32(uint32_t* p, int64_t n) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
-
-// Workspace of the decode path (rows = B * Tq; u32 words, counts padded to
-// multiples of 4): hist [rows][1024] | cnt [rows][DC_NB] (keys in range per
-// collecting block) | thr [rows][4] | bitmap [rows][DL_MAXW] | buffer
-// [rows][DC_NB][DC_SLOTS] (key, index) | scores [rows][stride].  Only hist
-// starts at zero.
-struct DecodeWs {
-    uint32_t* hist;
-    uint32_t* cnt;
-    u32x4* thr;        // [rows] level-1 range: lo, hi, count above, count inside
-    uint32_t* bmp;
-    u32x2* cb;
-    uint32_t* scores;
+// Chunk geometry of a launch: ch candidates per chunk (at most 4096; the
+// rows' keys fill at most DS_KEYS words of LDS), nchunks chunks over the
+// longest row, cap list slots per (row, chunk): a power of two near four
+// times the expected share of the top k (k ch / ncand), at least 32, with
+// nchunks * cap <= DM_UCAP.
+struct DecodeGeom {
+    int ch, nchunks, cap, ept;
 };
 
-__host__ __device__ __forceinline__ int64_t pad4(int64_t n) { return (n + 3) & ~(int64_t)3; }
-
-__host__ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int64_t B, int64_t rows) {
-    DecodeWs w;
-    uint32_t* p = reinterpret_cast<uint32_t*>(ws);
-    w.hist = p;
-    p += rows * SEL_NB;
-    w.cnt = p;
-    p += rows * DC_NB;
-    w.thr = reinterpret_cast<u32x4*>(p);
-    p += rows * 4;
-    w.bmp = p;
-    p += rows * DL_MAXW;
-    w.cb = reinterpret_cast<u32x2*>(p);
-    p += rows * DL_CAP * 2;
-    w.scores = p;
-    return w;
+__host__ __device__ __forceinline__ DecodeGeom decode_geom(int64_t Tq, int64_t ncand, int k) {
+    DecodeGeom g;
+    g.ch = Tq <= 2 ? 4096 : Tq <= 4 ? 2048 : 1024;
+    g.nchunks = (int)((ncand + g.ch - 1) / g.ch);
+    const int64_t want = (4 * (int64_t)k * g.ch + ncand - 1) / (ncand > 0 ? ncand : 1);
+    int cap = 32;
+    while (cap < want) cap *= 2;
+    int lim = 1;                                     // largest power of two <= DM_UCAP / nchunks
+    while (2 * lim * (g.nchunks > 0 ? g.nchunks : 1) <= DM_UCAP) lim *= 2;
+    cap = cap < lim ? cap : lim;
+    g.cap = cap < g.ch ? cap : g.ch;
+    const int u = g.nchunks * g.cap;
+    g.ept = u <= 2 * DM_NT ? 2 : u <= 4 * DM_NT ? 4 : 8;
+    return g;
 }
 
-// Threshold range of a row at level 1 from its histogram (one wave).
-__device__ __forceinline__ void lvl1_threshold(const uint32_t* hist, int need, uint32_t* lo,
-                                               uint32_t* hi, int* above, int* in) {
-    int gt, cnt_in;
-    const int d = wave_hist_find(hist, need, &gt, &cnt_in);
-    lvl1_range(d, lo, hi);
-    *above = gt;
-    *in = cnt_in;
+// Workspace: lists [rows][nchunks][cap] (key, index) | meta [rows][nchunks]
+// (count, tau).  Nothing needs to start at any value.
+__host__ __device__ __forceinline__ u32x2* ws_lists(void* ws) {
+    return reinterpret_cast<u32x2*>(ws);
+}
+__host__ __device__ __forceinline__ u32x2* ws_meta(void* ws, int64_t rows, const DecodeGeom& g) {
+    return reinterpret_cast<u32x2*>(ws) + rows * g.nchunks * g.cap;
+}
+
+// MXFP4 A operand of the lane's (query, head) row of an MFMA: rows
+// (qi, h) = (row / HI, row % HI), 32-value block kb of its dI values
+// (dI = 32 leaves block 1 zero); query qi of the tile is row q0 + qi.
+template <typename T, int HI>
+__device__ __forceinline__ void encode_q(const T* q_idx, int64_t b, int64_t Tq, int64_t q0,
+                                         int qv, int dI, i32x8& aop, int& sa) {
+    const int lane = threadIdx.x % WAVE, row = lane & 31, kb = lane >> 5;
+    aop = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    sa = 127;
+    const int qi = row / HI, h = row % HI;
+    if (qi < qv && kb * 32 < dI) {
+        const T* src = q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + kb * 32);
+        float v[32];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float t8[8];
+            Elem<T>::load8(src + p * 8, t8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[p * 8 + i] = t8[i];
+        }
+        uint32_t pk[4], sb;
+        mxfp4_encode32(v, pk, sb);
+        aop[0] = (int)pk[0]; aop[1] = (int)pk[1]; aop[2] = (int)pk[2]; aop[3] = (int)pk[3];
+        sa = (int)sb;
+    }
 }
 
 template <typename T, int HI>
 __global__ void __launch_bounds__(DS_NT)
-k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
-         const uint8_t* __restrict__ ks, DecodeWs ws, int64_t Tq, int dI, int64_t Nc, int64_t m,
-         int64_t W, int k, int64_t q_pos0, int64_t ncap) {
-    extern __shared__ uint32_t hist_raw[];           // [Tq][SEL_NB]
-    uint32_t (*hist)[SEL_NB] = reinterpret_cast<uint32_t (*)[SEL_NB]>(hist_raw);
+k_dscan(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+        const uint8_t* __restrict__ ks, void* ws, int64_t Tq, int dI, int64_t Nc, int64_t m,
+        int64_t W, int64_t q_pos0, DecodeGeom g) {
+    extern __shared__ uint32_t smem[];               // keys [Tq][ch] | hist [Tq][SEL_NB]
     constexpr int NU = 16 / HI;
-    const int64_t c0 = (int64_t)blockIdx.x * DS_CH;
+    constexpr int NWV = DS_NT / WAVE;
+    const int ch = g.ch, cap = g.cap;
+    const int cx = blockIdx.x;
+    const int64_t c0 = (int64_t)cx * ch;
     const int64_t b = blockIdx.y;
     const int qv = (int)Tq;                          // Tq <= DS_QT on this path
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int row = lane & 31, kb = lane >> 5;
+    uint32_t* keys = smem;
+    uint32_t* hist = smem + qv * ch;
+    __shared__ uint32_t s_tau[DS_QT];
+    __shared__ int s_nv[DS_QT];
+    __shared__ int s_wcnt[DS_QT][NWV];
     const int64_t nc_max = n_candidates(q_pos0 + qv - 1, m, W);
-    const int nkeys = (int)min((int64_t)DS_CH, nc_max - c0);   // >= 1: grid covers nc_max
-    uint32_t* scores = ws.scores;
-    for (int i = tid; i < qv * SEL_NB; i += DS_NT) hist_raw[i] = 0u;
+    const int nkeys = (int)min((int64_t)ch, nc_max - c0);   // >= 1: the grid covers nc_max
+    for (int i = tid; i < qv * SEL_NB; i += DS_NT) hist[i] = 0u;
 
-    i32x8 aop = {0, 0, 0, 0, 0, 0, 0, 0};
-    int sa = 127;
-    {
-        const int qi = row / HI, h = row % HI;
-        if (qi < qv && kb * 32 < dI) {
-            const T* src = q_idx + (((b * Tq + qi) * HI + h) * dI + kb * 32);
-            float v[32];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float t8[8];
-                Elem<T>::load8(src + p * 8, t8);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[p * 8 + i] = t8[i];
-            }
-            uint32_t pk[4], sb;
-            mxfp4_encode32(v, pk, sb);
-            aop[0] = (int)pk[0]; aop[1] = (int)pk[1]; aop[2] = (int)pk[2]; aop[3] = (int)pk[3];
-            sa = (int)sb;
-        }
-    }
+    i32x8 aop;
+    int sa;
+    encode_q<T, HI>(q_idx, b, Tq, 0, qv, dI, aop, sa);
+    // lane slot u of a tile holds the scores of query qslot[u]
     const int kbq = kb * 4 / HI;
-    int qslot[NU];
-    int64_t ncq[NU];
+    int qslot[NU], nvq[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int g = (u * HI) / 4, i = (u * HI) % 4;
-        qslot[u] = (8 * g + i) / HI + kbq;
-        ncq[u] = qslot[u] < qv ? n_candidates(q_pos0 + qslot[u], m, W) : 0;
+        const int gg = (u * HI) / 4, i = (u * HI) % 4;
+        qslot[u] = (8 * gg + i) / HI + kbq;
+        const int64_t nq = qslot[u] < qv ? n_candidates(q_pos0 + qslot[u], m, W) - c0 : 0;
+        nvq[u] = (int)max((int64_t)0, min((int64_t)nkeys, nq));
     }
     __syncthreads();
 
@@ -141,256 +146,176 @@ k_dscore(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     stream_tiles<DS_NT, 4, true>(ts, (nkeys + 31) / 32, 1, aop, sa,
                                  [&](const f32x16& acc, int jt) {
         const int jj = jt + row;
-        const int64_t j = c0 + jj;
+        uint32_t key[NU];
+        tile_keys<HI>(acc, key);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int q = qslot[u];
             if (q >= qv || jj >= nkeys) continue;
-            const uint32_t key = score_key<HI>(acc, u);
-            scores[((b * Tq + q) * ncap) + j] = key;
-            if (j < ncq[u]) atomicAdd(&hist[q][lvl1_bin(key)], 1u);
+            keys[q * ch + jj] = key[u];
+            if (jj < nvq[u]) atomicAdd(&hist[q * SEL_NB + lvl1_bin(key[u])], 1u);
         }
     });
     __syncthreads();
-    for (int i = tid; i < qv * SEL_NB; i += DS_NT) {
-        const uint32_t c = hist_raw[i];
-        if (c) atomicAdd(&ws.hist[(b * Tq) * SEL_NB + i], c);
-    }
-}
 
-// Visit the nc stored keys of one row, 16-byte vectors, four in flight per
-// thread, calling fn(key, candidate index).
-template <typename F>
-__device__ __forceinline__ void scan_scores(const uint32_t* __restrict__ sc, int nc, F&& fn) {
-    const int nv = nc / 4;
-    const u32x4* v4 = reinterpret_cast<const u32x4*>(sc);
-    constexpr int U = 4;
-    for (int v0 = threadIdx.x; v0 < nv; v0 += DL_NT * U) {
-        u32x4 w[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * DL_NT;
-            w[u] = v < nv ? __builtin_nontemporal_load(v4 + v) : u32x4{0u, 0u, 0u, 0u};
+    u32x2* meta = ws_meta(ws, Tq * gridDim.y, g);
+    // per row: the list threshold (one wave per row)
+    for (int q = wave; q < qv; q += NWV) {
+        const int nv = (int)max((int64_t)0, min((int64_t)nkeys,
+                                                n_candidates(q_pos0 + q, m, W) - c0));
+        uint32_t tau = 0u;
+        int cnt = nv;
+        if (nv > cap) {
+            int gt, in;
+            const int d = wave_hist_find(hist + q * SEL_NB, cap + 1, &gt, &in);
+            uint32_t lo, hi;
+            lvl1_range(d, &lo, &hi);
+            tau = hi;                                // bins above d: gt <= cap keys
+            cnt = gt;
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * DL_NT;
-            if (v < nv) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) fn(w[u][e], 4 * v + e);
-            }
-        }
-    }
-    for (int j = 4 * nv + (int)threadIdx.x; j < nc; j += DL_NT) fn(sc[j], j);
-}
-
-constexpr int DC_NT = 256;
-constexpr int DC_CH = DC_CH_;
-
-__global__ void __launch_bounds__(DC_NT)
-k_dcollect(DecodeWs ws, int64_t Tq, int64_t m, int64_t W, int k, int64_t q_pos0,
-           int64_t stride) {
-    __shared__ uint32_t words[DC_CH / 32];
-    const int64_t c0 = (int64_t)blockIdx.x * DC_CH;
-    const int64_t q = blockIdx.y, b = blockIdx.z;
-    const int64_t rowi = b * Tq + q;
-    const int nc = (int)n_candidates(q_pos0 + q, m, W);
-    if (nc <= k || c0 >= nc) return;                 // the final kernel needs nothing here
-    const int tid = threadIdx.x;
-    const int n = (int)min((int64_t)DC_CH, (int64_t)nc - c0);
-    const uint32_t* sc = ws.scores + rowi * stride + c0;
-    const int nv = n / 4;
-    // this block's scores are in flight while wave 0 finds the range
-    constexpr int VPT = DC_CH / 4 / DC_NT;
-    u32x4 vals[VPT];
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-        const int v = tid + x * DC_NT;
-        vals[x] = v < nv ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sc) + v)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
-    __shared__ u32x4 s_thr;
-    if (tid < WAVE) {
-        uint32_t lo, hi;
-        int above, in;
-        lvl1_threshold(ws.hist + rowi * SEL_NB, k, &lo, &hi, &above, &in);
-        const u32x4 t = {lo, hi, (uint32_t)above, (uint32_t)in};
-        if (tid == 0) {
-            s_thr = t;
-            if (blockIdx.x == 0) ws.thr[rowi] = t;   // for the final kernel
-        }
-    }
-    __shared__ uint32_t s_cnt;
-    for (int w = tid; w < DC_CH / 32; w += DC_NT) words[w] = 0u;
-    if (tid == 0) s_cnt = 0u;
-    __syncthreads();
-    const uint32_t lo = s_thr[0], hi = s_thr[1];
-    const bool collect = s_thr[3] <= (uint32_t)DL_CAP;
-    uint32_t* cnt = &s_cnt;
-    u32x2* cb = ws.cb + rowi * DL_CAP + blockIdx.x * DC_SLOTS;
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-        const int v = tid + x * DC_NT;
-        if (v >= nv) break;
-        const u32x4 w = vals[x];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 4 * v + e;
-            const uint32_t key = w[e];
-            if (key >= hi) {
-                atomicOr(&words[j >> 5], 1u << (j & 31));
-            } else if (key >= lo && collect) {
-                const uint32_t pos = atomicAdd(cnt, 1u);
-                if (pos < (uint32_t)DC_SLOTS) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
-            }
-        }
-    }
-    for (int j = 4 * nv + tid; j < n; j += DC_NT) {
-        const uint32_t key = sc[j];
-        if (key >= hi) {
-            atomicOr(&words[j >> 5], 1u << (j & 31));
-        } else if (key >= lo && collect) {
-            const uint32_t pos = atomicAdd(cnt, 1u);
-            if (pos < (uint32_t)DC_SLOTS) cb[pos] = u32x2{key, (uint32_t)(c0 + j)};
+        if (lane == 0) {
+            s_tau[q] = tau;
+            s_nv[q] = nv;
+            meta[(b * Tq + q) * g.nchunks + cx] = u32x2{(uint32_t)cnt, tau};
         }
     }
     __syncthreads();
-    for (int w = tid; w < (n + 31) / 32; w += DC_NT) ws.bmp[rowi * DL_MAXW + c0 / 32 + w] = words[w];
-    // more than DC_SLOTS keys here reads as an overflow in the final kernel
-    if (tid == 0) ws.cnt[rowi * DC_NB + blockIdx.x] = s_cnt;
+    // per row: the keys >= tau in index order -> the list (each wave takes a
+    // contiguous quarter of the chunk; counts first, then positions)
+    const int span = ch / NWV;                       // a multiple of WAVE
+    const int j0 = wave * span;
+    for (int q = 0; q < qv; ++q) {
+        const uint32_t tau = s_tau[q];
+        const int j1 = min(j0 + span, s_nv[q]);
+        int c = 0;
+        for (int jb = j0; jb < j1; jb += WAVE) {
+            const int j = jb + lane;
+            const bool take = j < j1 && keys[q * ch + j] >= tau;
+            c += __popcll(__ballot(take));
+        }
+        if (lane == 0) s_wcnt[q][wave] = c;
+    }
+    __syncthreads();
+    u32x2* lists = ws_lists(ws);
+    for (int q = 0; q < qv; ++q) {
+        const uint32_t tau = s_tau[q];
+        const int j1 = min(j0 + span, s_nv[q]);
+        int pos = 0;
+        for (int w = 0; w < wave; ++w) pos += s_wcnt[q][w];
+        u32x2* dst = lists + ((b * Tq + q) * g.nchunks + cx) * (int64_t)cap;
+        for (int jb = j0; jb < j1; jb += WAVE) {
+            const int j = jb + lane;
+            const uint32_t key = j < j1 ? keys[q * ch + j] : 0u;
+            const bool take = j < j1 && key >= tau;
+            const uint64_t bal = __ballot(take);
+            if (take) dst[pos + __popcll(bal & ((1ull << lane) - 1ull))] =
+                u32x2{key, (uint32_t)(c0 + j)};
+            pos += __popcll(bal);
+        }
+    }
 }
 
-struct DselSmem {
-    uint32_t sel[DL_MAXW];
-    uint32_t eq[DL_MAXW];
+// ---- the exact path of a merging block -------------------------------------
+struct DmSmem {
+    SelectSmem sel_sm;
+    uint32_t cnt[DM_UCAP / 32];      // list counts per chunk (nchunks <= DM_UCAP / 32)
+    __attribute__((aligned(16))) uint32_t sel[DM_MAXW];
+    __attribute__((aligned(16))) uint32_t eq[DM_MAXW];
     uint32_t hist[SEL_NB];
-    u32x2 cb[DL_CAP];
-    uint32_t lo, hi;
-    int shift, above, in, mode, cnt, eqmode, need_eq;
-    int scratch[DL_NT / WAVE + 1];
-    int boff[DC_NB];                // first buffer position of each collecting block
+    u32x2 cb[DM_CAP];
+    uint32_t lo, hi, tau_need;
+    int above, in, ccnt, total, need_eq, unlisted;
+    int scratch[DM_NT / WAVE + 1];
 };
 
-__global__ void __launch_bounds__(DL_NT)
-k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t W, int k,
-         int64_t q_pos0, int64_t stride) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    DselSmem& S = *reinterpret_cast<DselSmem*>(smem_raw);
-    const int64_t q = blockIdx.x, b = blockIdx.y;
-    const int64_t rowi = b * Tq + q;
+// Exact top `need` of the row's nc candidates by rescoring the keys
+// (scan(fn) calls fn(key, j) once for every candidate j < nc, spread over the
+// block).  Level 1 fixes a range of 2^17 keys (2^30 for bin 0, < 2^32 for
+// bin 1023); each narrowing pass splits it into SEL_NB parts, so the widths
+// go <= 2^32 -> 2^22 -> 2^12 -> 2^2 -> 1 and DM_PASSES = 4 passes always
+// end with <= DM_CAP keys in range or a single key value.
+template <typename Scan>
+__device__ __forceinline__ void exact_select(Scan&& scan, int nc, int need, int32_t* out, int k,
+                                             DmSmem& S) {
+    static_assert(DM_MAXW == 8 * DM_NT, "merge-emit takes 8 words per thread");
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int nc = (int)n_candidates(q_pos0 + q, m, W);
     const int nw = (nc + 31) / 32;
-    const int need = min(nc, k);
-    const uint32_t* sc = ws.scores + rowi * stride;
-    int32_t* out = topk + rowi * k;
-
-    if (nc <= k) {                                  // every candidate is kept
-        for (int s2 = tid; s2 < k; s2 += DL_NT) out[s2] = s2 < nc ? s2 : -1;
-        return;
-    }
-    // every global read of this block is issued up front: the bitmap words of
-    // the keys above the range (8 per thread), one buffer slot and its
-    // block's count per thread, the threshold range
-    static_assert(DL_MAXW == 8 * DL_NT && DC_NB * DC_SLOTS == DL_NT, "one pass of loads");
-    const int nblk = (nc + DC_CH_ - 1) / DC_CH_;
-    const u32x4* bw = reinterpret_cast<const u32x4*>(ws.bmp + rowi * DL_MAXW) + 2 * tid;
-    const bool wlive = 8 * tid < nw;
-    const u32x4 w0 = wlive ? bw[0] : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 w1 = wlive ? bw[1] : u32x4{0u, 0u, 0u, 0u};
-    const int sblk = tid / DC_SLOTS, sidx = tid % DC_SLOTS;
-    const bool slive = sblk < nblk;
-    const uint32_t scnt = slive ? ws.cnt[rowi * DC_NB + sblk] : 0u;
-    // (read whether or not it holds a key, so it does not wait for the count)
-    const u32x2 slot = slive ? ws.cb[rowi * DL_CAP + tid] : u32x2{0u, 0u};
-    const uint32_t c = lane < nblk ? ws.cnt[rowi * DC_NB + lane] : 0u;   // (wave 0)
-    const u32x4 thr = ws.thr[rowi];
-    // (words past nw are never read: every bitmap pass stops at nw)
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        S.sel[8 * tid + x] = w0[x];
-        S.sel[8 * tid + 4 + x] = w1[x];
-        S.eq[8 * tid + x] = 0u;
-        S.eq[8 * tid + 4 + x] = 0u;
-    }
+    for (int i = tid; i < SEL_NB; i += DM_NT) S.hist[i] = 0u;
+    __syncthreads();
+    scan([&](uint32_t key, int j) { atomicAdd(&S.hist[lvl1_bin(key)], 1u); });
+    __syncthreads();
     if (wave == 0) {
-        // per collecting block: keys in range (more than DC_SLOTS: overflow)
-        const bool over = __ballot(c > (uint32_t)DC_SLOTS) != 0ull;
-        const int incl = wave_incl_scan((int)c);
-        const int total = __shfl(incl, WAVE - 1, WAVE);
-        S.boff[lane] = incl - (int)c;
+        int gt, in;
+        const int d = wave_hist_find(S.hist, need, &gt, &in);
+        uint32_t lo, hi;
+        lvl1_range(d, &lo, &hi);
         if (lane == 0) {
-            S.lo = thr[0];
-            S.hi = thr[1];
-            S.above = (int)thr[2];
-            S.in = (int)thr[3];
-            S.cnt = S.in <= DL_CAP && !over ? total : -1;
+            S.lo = lo;
+            S.hi = hi;
+            S.above = gt;
+            S.in = in;
         }
     }
     __syncthreads();
-    if (S.cnt >= 0) {
-        // the collecting blocks gathered the range's keys into their slots
-        if (slive && sidx < (int)scnt) S.cb[S.boff[sblk] + sidx] = slot;
-        __syncthreads();
-    } else {
-        // too many keys in the level-1 range: narrow it over the stored scores
 #pragma unroll 1
-        for (int it = 0; it < 6; ++it) {
-            const uint32_t lo = S.lo, hi = S.hi;
-            if (S.in <= DL_CAP || hi - lo == 1u) break;
-            const int sh = range_shift(lo, hi);
-            __syncthreads();
-            for (int i = tid; i < SEL_NB; i += DL_NT) S.hist[i] = 0u;
-            __syncthreads();
-            scan_scores(sc, nc, [&](uint32_t key, int j) {
-                if (key >= lo && key < hi) atomicAdd(&S.hist[(key - lo) >> sh], 1u);
-            });
-            __syncthreads();
-            if (wave == 0) {
-                int gt, in;
-                const int d = wave_hist_find(S.hist, need - S.above, &gt, &in);
-                if (lane == 0) {
-                    S.lo = lo + ((uint32_t)d << sh);
-                    uint64_t top = (uint64_t)lo + ((uint64_t)(d + 1) << sh);
-                    S.hi = top < (uint64_t)hi ? (uint32_t)top : hi;
-                    S.above += gt;
-                    S.in = in;
-                }
-            }
-            __syncthreads();
-        }
-        // collect the narrowed range (keys above it are kept for sure)
+    for (int it = 0; it < DM_PASSES; ++it) {
         const uint32_t lo = S.lo, hi = S.hi;
-        const bool eqmode = S.in > DL_CAP;         // single-valued range with many ties
-        if (tid == 0) S.cnt = 0;
+        if (S.in <= DM_CAP || hi - lo == 1u) break;
+        const int sh = range_shift(lo, hi);
         __syncthreads();
-        scan_scores(sc, nc, [&](uint32_t key, int j) {
-            if (key >= hi) {
-                atomicOr(&S.sel[j >> 5], 1u << (j & 31));
-            } else if (key >= lo) {
-                if (eqmode) {
-                    atomicOr(&S.eq[j >> 5], 1u << (j & 31));
-                } else {
-                    const int pos = atomicAdd(&S.cnt, 1);
-                    if (pos < DL_CAP) S.cb[pos] = u32x2{key, (uint32_t)j};
-                }
-            }
+        for (int i = tid; i < SEL_NB; i += DM_NT) S.hist[i] = 0u;
+        __syncthreads();
+        scan([&](uint32_t key, int j) {
+            if (key >= lo && key < hi) atomicAdd(&S.hist[(key - lo) >> sh], 1u);
         });
         __syncthreads();
-        if (eqmode && tid == 0) S.cnt = -1;
+        if (wave == 0) {
+            int gt, in;
+            const int d = wave_hist_find(S.hist, need - S.above, &gt, &in);
+            if (lane == 0) {
+                S.lo = lo + ((uint32_t)d << sh);
+                const uint64_t top = (uint64_t)lo + ((uint64_t)(d + 1) << sh);
+                S.hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+                S.above += gt;
+                S.in = in;
+            }
+        }
         __syncthreads();
     }
+    // collect: keys above the range are kept; keys inside go to the buffer,
+    // or, for a single-valued range with many ties, to the tie bitmap
+    const uint32_t lo = S.lo, hi = S.hi;
+    const bool eqmode = S.in > DM_CAP;
+    for (int w = tid; w < DM_MAXW; w += DM_NT) {
+        S.sel[w] = 0u;
+        S.eq[w] = 0u;
+    }
+    if (tid == 0) S.ccnt = 0;
+    __syncthreads();
+    scan([&](uint32_t key, int j) {
+        if (key >= hi) {
+            atomicOr(&S.sel[j >> 5], 1u << (j & 31));
+        } else if (key >= lo) {
+            if (eqmode) {
+                atomicOr(&S.eq[j >> 5], 1u << (j & 31));
+            } else {
+                const int pos = atomicAdd(&S.ccnt, 1);
+                if (pos < DM_CAP) S.cb[pos] = u32x2{key, (uint32_t)j};
+            }
+        }
+    });
+    __syncthreads();
     if (wave == 0) {
         const int need_in = need - S.above;
         int need_eq = need_in;
-        if (S.cnt >= 0) {
-            const int n = min(S.cnt, DL_CAP);
-            constexpr int EPT = DL_CAP / WAVE;
+        if (!eqmode) {
+            const int n = min(S.ccnt, DM_CAP);
+            constexpr int EPT = DM_CAP / WAVE;
             uint32_t key[EPT];
             bool valid[EPT];
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
-                const int p = e * WAVE + lane;          // lane-contiguous: no bank conflicts
+                const int p = e * WAVE + lane;
                 valid[e] = p < n;
                 key[e] = valid[e] ? S.cb[p][0] : 0u;
             }
@@ -408,27 +333,134 @@ k_dfinal(DecodeWs ws, int32_t* __restrict__ topk, int64_t Tq, int64_t m, int64_t
         if (lane == 0) S.need_eq = need_eq;
     }
     __syncthreads();
-    block_merge_emit8<DL_NT>(S.sel, S.eq, nw, S.need_eq, out, k, S.scratch);
+    block_merge_emit8<DM_NT>(S.sel, S.eq, nw, S.need_eq, out, k, S.scratch);
 }
 
-size_t dselect_smem_bytes() { return sizeof(DselSmem); }
-int decode_max_candidates() { return DL_MAXW * 32; }
+template <typename T, int HI, int EPT>
+__global__ void __launch_bounds__(DM_NT)
+k_dmerge(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+         const uint8_t* __restrict__ ks, void* ws, int32_t* __restrict__ topk, int64_t Tq,
+         int dI, int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0, DecodeGeom g) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    DmSmem& S = *reinterpret_cast<DmSmem*>(smem_raw);
+    const int64_t q = blockIdx.x, b = blockIdx.y;
+    const int64_t bq = b * Tq + q;
+    const int tid = threadIdx.x;
+    const int nc = (int)n_candidates(q_pos0 + q, m, W);
+    const int need = min(nc, k);
+    int32_t* out = topk + bq * k;
+    if (nc <= k) {                                  // every candidate is kept
+        for (int s = tid; s < k; s += DM_NT) out[s] = s < nc ? s : -1;
+        return;
+    }
+    const int cap = g.cap, ch = g.ch;
+    const int nchk = (nc + ch - 1) / ch;            // chunks holding this row's candidates
+    const u32x2* meta = ws_meta(ws, Tq * gridDim.y, g) + bq * g.nchunks;
+    const u32x2* lists = ws_lists(ws) + bq * g.nchunks * (int64_t)cap;
+    // the union, EPT list slots per thread in (chunk, slot) order, i.e. in
+    // ascending candidate index; keys + 1 (0: an empty slot)
+    u32x2 ent[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; e += 2) {
+        const int p = tid * EPT + e;
+        const u32x4 v = p < nchk * cap ? *reinterpret_cast<const u32x4*>(lists + p)
+                                       : u32x4{0u, 0u, 0u, 0u};
+        ent[e] = u32x2{v[0], v[1]};
+        ent[e + 1] = u32x2{v[2], v[3]};
+    }
+    if (tid == 0) {
+        S.tau_need = 0u;
+        S.total = 0;
+        S.unlisted = 0;
+    }
+    __syncthreads();
+    for (int c = tid; c < nchk; c += DM_NT) {
+        const u32x2 mt = meta[c];
+        S.cnt[c] = mt[0];
+        const int nv = min(ch, nc - c * ch);
+        atomicAdd(&S.total, (int)mt[0]);
+        if ((int)mt[0] < nv) {                       // the chunk left keys out
+            atomicMax(&S.tau_need, mt[1]);
+            S.unlisted = 1;
+        }
+    }
+    __syncthreads();
+    uint32_t key[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int p = tid * EPT + e;
+        const int c = p / cap, s = p - c * cap;
+        key[e] = c < nchk && s < (int)S.cnt[c] ? ent[e][0] + 1u : 0u;
+    }
+    bool exact_needed = S.total < need;
+    uint32_t thr = 0u;
+    int need_eq = 0;
+    if (!exact_needed) {
+        block_topk_threshold<DM_NT, EPT>(key, need, S.sel_sm, &thr, &need_eq);
+        // thr - 1 is the k-th key of the union; every left-out key is < tau
+        exact_needed = S.unlisted && thr - 1u < S.tau_need;
+    }
+    if (!exact_needed) {
+        int base, total;
+        const uint32_t flags = block_select_flags<DM_NT, EPT>(key, thr, need_eq, S.sel_sm,
+                                                             &base, &total);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (flags & (1u << e)) out[base++] = (int32_t)ent[e][1];
+        for (int s = total + tid; s < k; s += DM_NT) out[s] = -1;
+        return;
+    }
+    // exact path: rescore every candidate of the row, pass by pass
+    i32x8 aop;
+    int sa;
+    encode_q<T, HI>(q_idx, b, Tq, q, 1, dI, aop, sa);
+    const int lane = tid % WAVE, row = lane & 31, kb = lane >> 5;
+    const int kbytes = dI / 2, kscales = dI / 32;
+    const TileSrc ts{kc + b * Nc * kbytes, ks + b * Nc * kscales, kbytes, kscales, nc, row, kb};
+    auto scan = [&](auto&& fn) {
+        stream_tiles<DM_NT, 2>(ts, (nc + 31) / 32, 1, aop, sa, [&](const f32x16& acc, int jt) {
+            // the row's HI head scores sit in slots 0..HI-1 of lanes 0-31
+            const int j = jt + row;
+            uint32_t key[1];
+            tile_keys<HI>(acc, key);
+            if (kb == 0 && j < nc) fn(key[0], j);
+        });
+    };
+    __syncthreads();
+    exact_select(scan, nc, need, out, k, S);
+}
+
+int decode_max_candidates() { return DM_MAXW * 32; }
 int decode_max_rows() { return DS_QT; }
 
-size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap) {
+size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap, int k) {
+    const DecodeGeom g = decode_geom(Tq, ncap, k);
     const int64_t rows = B * Tq;
-    const int64_t words = rows * SEL_NB + rows * DC_NB + rows * 4 + rows * DL_MAXW +
-                          rows * DL_CAP * 2 + rows * score_stride(ncap);
-    return (size_t)words * sizeof(uint32_t);
+    return (size_t)(rows * g.nchunks * g.cap + rows * g.nchunks) * sizeof(u32x2);
 }
 
 template <typename T, int HI>
-static void launch_dscore(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W, int k,
-                          int64_t q_pos0, const void* q_idx, const uint8_t* kc, const uint8_t* ks,
-                          const DecodeWs& w, int64_t ncand, int64_t stride, hipStream_t st) {
-    dim3 grid((unsigned)((ncand + DS_CH - 1) / DS_CH), (unsigned)B);
-    hipLaunchKernelGGL((k_dscore<T, HI>), grid, dim3(DS_NT), Tq * SEL_NB * sizeof(uint32_t), st,
-                       (const T*)q_idx, kc, ks, w, Tq, dI, Nc, m, W, k, q_pos0, stride);
+static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W,
+                            int k, int64_t q_pos0, const void* q_idx, const uint8_t* kc,
+                            const uint8_t* ks, int32_t* topk, void* ws, const DecodeGeom& g,
+                            hipStream_t st) {
+    const size_t lds_scan = (size_t)Tq * (g.ch + SEL_NB) * sizeof(uint32_t);
+    hipLaunchKernelGGL((k_dscan<T, HI>), dim3((unsigned)g.nchunks, (unsigned)B), dim3(DS_NT),
+                       lds_scan, st, (const T*)q_idx, kc, ks, ws, Tq, dI, Nc, m, W, q_pos0, g);
+    const size_t lds = sizeof(DmSmem);
+#define CSA_DM_CASE(E)                                                                       \
+    do {                                                                                     \
+        auto kern = k_dmerge<T, HI, E>;                                                      \
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                            (int)lds);                                                       \
+        hipLaunchKernelGGL(kern, dim3((unsigned)Tq, (unsigned)B), dim3(DM_NT), lds, st,      \
+                           (const T*)q_idx, kc, ks, ws, topk, Tq, dI, Nc, m, W, k, q_pos0,   \
+                           g);                                                               \
+    } while (0)
+    if (g.ept == 2) CSA_DM_CASE(2);
+    else if (g.ept == 4) CSA_DM_CASE(4);
+    else CSA_DM_CASE(8);
+#undef CSA_DM_CASE
 }
 
 hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
@@ -437,34 +469,19 @@ hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, in
                                hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
     const int64_t ncand = n_candidates(q_pos0 + Tq - 1, m, W);
-    const int64_t stride = score_stride(ncand);
-    const int64_t rows = B * Tq;
-    DecodeWs w = decode_ws(ws, B, rows);
-    if (ncand > 0) {
-        // histograms start at zero
-        const int64_t nz = rows * SEL_NB;
-        hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st,
-                           w.hist, nz);
+    const DecodeGeom g = decode_geom(Tq, ncand, k);
 #define CSA_DS_CASE(TT, HH) \
-    launch_dscore<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, w, ncand, stride, st)
-        if (dt == 0) {
-            if (HI == 1) CSA_DS_CASE(float, 1);
-            else if (HI == 2) CSA_DS_CASE(float, 2);
-            else CSA_DS_CASE(float, 4);
-        } else {
-            if (HI == 1) CSA_DS_CASE(uint16_t, 1);
-            else if (HI == 2) CSA_DS_CASE(uint16_t, 2);
-            else CSA_DS_CASE(uint16_t, 4);
-        }
-#undef CSA_DS_CASE
-        hipLaunchKernelGGL(k_dcollect, dim3((unsigned)((ncand + DC_CH - 1) / DC_CH), (unsigned)Tq,
-                                             (unsigned)B),
-                           dim3(DC_NT), 0, st, w, Tq, m, W, k, q_pos0, stride);
+    launch_decode_t<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk, ws, g, st)
+    if (dt == 0) {
+        if (HI == 1) CSA_DS_CASE(float, 1);
+        else if (HI == 2) CSA_DS_CASE(float, 2);
+        else CSA_DS_CASE(float, 4);
+    } else {
+        if (HI == 1) CSA_DS_CASE(uint16_t, 1);
+        else if (HI == 2) CSA_DS_CASE(uint16_t, 2);
+        else CSA_DS_CASE(uint16_t, 4);
     }
-    const size_t lds = sizeof(DselSmem);
-    hipFuncSetAttribute((const void*)k_dfinal, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k_dfinal, dim3((unsigned)Tq, (unsigned)B), dim3(DL_NT), lds, st, w, topk, Tq,
-                       m, W, k, q_pos0, stride);
+#undef CSA_DS_CASE
     return hipGetLastError();
 }
 

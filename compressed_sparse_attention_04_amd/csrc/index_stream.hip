@@ -172,10 +172,12 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         stream_tiles<ST_NT, st_unr<HI>()>(ts, (ntiles + ST_SAMPLE - 1) / ST_SAMPLE, ST_SAMPLE, aop, sa,
                      [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
+            uint32_t key[NU];
+            tile_keys<HI>(acc, key);
 #pragma unroll
             for (int u = 0; u < NU; ++u)
                 if (act[u] && j < ncq[u])
-                    atomicAdd(&S.hist[qslot[u]][lvl1_bin(score_key<HI>(acc, u))], 1u);
+                    atomicAdd(&S.hist[qslot[u]][lvl1_bin(key[u])], 1u);
         });
         __syncthreads();
         // 2. key range of the k-th key, per sampled row (wave q)
@@ -222,10 +224,12 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         for (int u = 0; u < NU; ++u) wc0[u] = wc1[u] = 0;
         stream_tiles<ST_NT, st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
+            uint32_t keys[NU];
+            tile_keys<HI>(acc, keys);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const bool ok = act[u] && j < ncq[u];
-                const uint32_t key = score_key<HI>(acc, u);
+                const uint32_t key = keys[u];
                 const bool above = ok && key >= hi[u];
                 const bool in = ok && !above && key >= lo[u];
                 const int q = qslot[u] < ST_QT ? qslot[u] : 0;
@@ -329,10 +333,12 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
 
         stream_tiles<ST_NT, st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
+            uint32_t keys[NU];
+            tile_keys<HI>(acc, keys);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (md[u] == M_DONE || j >= ncq[u]) continue;
-                const uint32_t key = score_key<HI>(acc, u);
+                const uint32_t key = keys[u];
                 const int q = qslot[u];
                 if (md[u] == M_HIST1) {
                     atomicAdd(&S.hist[q][lvl1_bin(key)], 1u);

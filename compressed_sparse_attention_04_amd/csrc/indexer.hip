@@ -200,7 +200,7 @@ k_topk_merge(const u32x2* __restrict__ part, int32_t* __restrict__ topk, int64_t
 int stream_max_candidates();
 int decode_max_candidates();
 int decode_max_rows();
-size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap);
+size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap, int k);
 hipError_t launch_index_stream(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
                                int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
                                const uint8_t* kc, const uint8_t* ks, int32_t* topk,
@@ -220,7 +220,7 @@ IndexPlan plan_index(int64_t B, int64_t Tq, int HI, int dI, int64_t Nc, int64_t 
     p.n_chunks = maxc > 0 ? (maxc + p.ch - 1) / p.ch : 1;
     if (Tq <= decode_max_rows() && maxc > 4096 && maxc <= decode_max_candidates()) {
         p.path = IDX_DECODE;
-        p.ws_bytes = decode_ws_bytes(B, Tq, maxc);
+        p.ws_bytes = decode_ws_bytes(B, Tq, maxc, k);
     } else if (maxc <= stream_max_candidates()) {
         p.path = IDX_STREAM;
         p.ws_bytes = 0;

@@ -145,6 +145,33 @@ __device__ __forceinline__ void block_topk_threshold(const uint32_t (&key)[EPT],
     *need_out = remaining;
 }
 
+// Selection flags for a known threshold: key > T, or key == T among the
+// first need keys equal to T in position order.  Returns the thread's flags
+// as a bitmask and its output offset; *total = number selected.
+template <int NT, int EPT>
+__device__ __forceinline__ uint32_t block_select_flags(const uint32_t (&key)[EPT], uint32_t T,
+                                                       int need, SelectSmem& sm, int* out_base,
+                                                       int* total) {
+    int neq = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) neq += key[e] == T;
+    int tot_eq;
+    int eq_rank = block_excl_scan<NT>(neq, sm, &tot_eq);
+    uint32_t flags = 0;
+    int nsel = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        bool s = key[e] > T;
+        if (key[e] == T) {
+            s = eq_rank < need;
+            eq_rank++;
+        }
+        if (s) { flags |= 1u << e; nsel++; }
+    }
+    *out_base = block_excl_scan<NT>(nsel, sm, total);
+    return flags;
+}
+
 // Full selection: returns the selected flags as a bitmask per thread and
 // the thread's output offset; *total = number selected (= kk).
 template <int NT, int EPT>
@@ -164,24 +191,7 @@ __device__ __forceinline__ uint32_t block_topk_select(const uint32_t (&key)[EPT]
     } else {
         block_topk_threshold<NT, EPT>(key, k, sm, &T, &need);
     }
-    int neq = 0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) neq += key[e] == T;
-    int tot_eq;
-    int eq_rank = block_excl_scan<NT>(neq, sm, &tot_eq);
-    uint32_t flags = 0;
-    int nsel = 0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        bool s = key[e] > T;
-        if (key[e] == T) {
-            s = eq_rank < need;
-            eq_rank++;
-        }
-        if (s) { flags |= 1u << e; nsel++; }
-    }
-    *out_base = block_excl_scan<NT>(nsel, sm, total);
-    return flags;
+    return block_select_flags<NT, EPT>(key, T, need, sm, out_base, total);
 }
 
 }  // namespace csa

@@ -198,6 +198,23 @@ def test_index_decode_clustered_range(copies):
     assert set(range(20000, 20300)) <= set(g[0, 0].tolist())
 
 
+@pytest.mark.parametrize("dtype,HI,dI,T,Tq,B,k", [
+    ("f32", 2, 64, 4 * 60000, 2, 2, 512),
+    ("bf16", 1, 32, 4 * 100000, 5, 1, 256),
+    ("bf16", 4, 32, 4 * 262144, 8, 1, 512),      # 256 chunks of 1024, 32 list slots each
+    ("bf16", 4, 64, 4 * 262144, 1, 1, 2048),     # 64 chunks, 128 list slots, k = 2048
+    ("bf16", 2, 64, 4 * 9000, 4, 3, 64),
+])
+def test_index_decode_shapes(dtype, HI, dI, T, Tq, B, k):
+    """Decode path (<= 8 rows, > 4096 candidates) at every indexer head count,
+    both indexer dims, fp32 and bf16 queries, 1 to 8 rows, and chunk
+    geometries from 4096 to 1024 candidates: chunk lists merged exactly."""
+    say("index decode shapes", dtype, HI, dI, T, Tq, B, k)
+    w = I.Workload("t", "csa", seed=27, dtype=dtype, B=B, T=T, m=4, H=128, D=128, HI=HI, dI=dI,
+                   k=k)
+    index_case(w, T - Tq, Tq)
+
+
 def test_index_one_head_small_k():
     say("index HI=1")
     w = I.Workload("t", "csa", seed=24, dtype="f32", B=2, T=6000, m=4, H=8, D=64, HI=1, dI=64,
