@@ -24,30 +24,47 @@ struct TileSrc {
 // operand), so the compiler can count them: the current batch is waited
 // for while the next one stays in flight.  STREAM: keys read once (decode)
 // bypass the caches' normal retention.
+// Offsets from the tile source's base are 32-bit: a source holds at most
+// 262,144 candidates of at most 32 code bytes.
 template <int UNR, bool STREAM>
 __device__ __forceinline__ void load_batch(const TileSrc& ts, int v0, int stride,
                                            u32x4 (&kw)[UNR], int (&ksv)[UNR]) {
-    const int koff = min(ts.kb * 16, ts.kbytes - 16);
-    const int soff = min(ts.kb, ts.kscales - 1);
+    const uint32_t koff = (uint32_t)min(ts.kb * 16, ts.kbytes - 16);
+    const uint32_t soff = (uint32_t)min(ts.kb, ts.kscales - 1);
 #pragma unroll
     for (int x = 0; x < UNR; ++x) {
-        const int j = min((v0 + x) * stride * 32 + ts.row, ts.nc_max - 1);
-        const u32x4* src = reinterpret_cast<const u32x4*>(ts.kcb + (int64_t)j * ts.kbytes + koff);
+        const uint32_t j = (uint32_t)min((v0 + x) * stride * 32 + ts.row, ts.nc_max - 1);
+        const u32x4* src =
+            reinterpret_cast<const u32x4*>(ts.kcb + (j * (uint32_t)ts.kbytes + koff));
         kw[x] = STREAM ? __builtin_nontemporal_load(src) : *src;
-        const int sc = ts.ksb[(int64_t)j * ts.kscales + soff];
+        const int sc = ts.ksb[j * (uint32_t)ts.kscales + soff];
         ksv[x] = ts.kb < ts.kscales ? sc : 127;
     }
 }
 
 // f(acc, j0): MFMA scores of the tile whose first key is j0 (this lane's
-// key is j0 + row for its S rows; see the callers)
+// key is j0 + row for its S rows; see the callers).  kwA / ksA hold the
+// wave's first batch, already requested by load_first (so a kernel can put
+// the first key loads in flight before its own set-up work).
+template <int NT, int UNR>
+__device__ __forceinline__ int first_batch(int nv) {
+    return (int)(threadIdx.x / WAVE) * UNR < nv;
+}
+template <int NT, int UNR, bool STREAM>
+__device__ __forceinline__ void load_first(const TileSrc& ts, int nv, int stride,
+                                           u32x4 (&kwA)[UNR], int (&ksA)[UNR]) {
+    if (first_batch<NT, UNR>(nv))
+        load_batch<UNR, STREAM>(ts, (int)(threadIdx.x / WAVE) * UNR, stride, kwA, ksA);
+}
+
 template <int NT, int UNR, bool STREAM = false, typename F>
-__device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stride,
-                                             const i32x8& aop, int sa, F&& f) {
+__device__ __forceinline__ void stream_tiles_from(const TileSrc& ts, int nv, int stride,
+                                                  const i32x8& aop, int sa, u32x4 (&kwA)[UNR],
+                                                  int (&ksA)[UNR], F&& f) {
     constexpr int NWV = NT / WAVE;
     const int wave = threadIdx.x / WAVE;
-    u32x4 kwA[UNR], kwB[UNR];
-    int ksA[UNR], ksB[UNR];
+    u32x4 kwB[UNR];
+    int ksB[UNR];
     auto mfma = [&](const u32x4& kw, int ksv) {
         const i32x8 bop = {(int)kw[0], (int)kw[1], (int)kw[2], (int)kw[3], 0, 0, 0, 0};
         const f32x16 zero = {};
@@ -70,7 +87,6 @@ __device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stri
     };
     int v0 = wave * UNR;
     if (v0 >= nv) return;
-    load_batch<UNR, STREAM>(ts, v0, stride, kwA, ksA);
     while (true) {
         load_batch<UNR, STREAM>(ts, v0 + NWV * UNR, stride, kwB, ksB);
         run(kwA, ksA, v0);
@@ -81,6 +97,15 @@ __device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stri
         v0 += NWV * UNR;
         if (v0 >= nv) break;
     }
+}
+
+template <int NT, int UNR, bool STREAM = false, typename F>
+__device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stride,
+                                             const i32x8& aop, int sa, F&& f) {
+    u32x4 kwA[UNR];
+    int ksA[UNR];
+    load_first<NT, UNR, STREAM>(ts, nv, stride, kwA, ksA);
+    stream_tiles_from<NT, UNR, STREAM>(ts, nv, stride, aop, sa, kwA, ksA, f);
 }
 
 // ReLU head sum of slot u of an MFMA tile as an order key.  ReLU is the
@@ -100,13 +125,30 @@ __device__ __forceinline__ uint32_t score_key(const f32x16& acc, int u) {
 // the caller, so the MFMA that produces the tile cannot be moved into a
 // branch that only some lanes take (an MFMA issued with part of EXEC off
 // does not give every lane its full result).
+// Only the first nlive slots (wave-uniform) are formed; the others read 0.
 template <int HI, int NU>
-__device__ __forceinline__ void tile_keys(const f32x16& acc, uint32_t (&key)[NU]) {
+__device__ __forceinline__ void tile_keys(const f32x16& acc, uint32_t (&key)[NU],
+                                          int nlive = NU) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        key[u] = score_key<HI>(acc, u);
-        asm volatile("" : "+v"(key[u]));
+        key[u] = 0u;
+        if (u < nlive) {
+            key[u] = score_key<HI>(acc, u);
+            asm volatile("" : "+v"(key[u]));
+        }
     }
+}
+
+// Slots of a tile that hold a query of the first qv (query qi of A row
+// (qi, h) = (row / HI, row % HI) sits in slot u of the lanes with
+// 8 (u HI / 4) + (u HI) % 4 + 4 kb = HI qi + h, h < HI).
+template <int HI>
+__host__ __device__ __forceinline__ int live_slots(int qv) {
+    constexpr int NU = 16 / HI;
+    int n = 0;
+    for (int u = 0; u < NU; ++u)
+        if ((8 * ((u * HI) / 4) + (u * HI) % 4) / HI < qv) n = u + 1;
+    return n;
 }
 
 }  // namespace csa

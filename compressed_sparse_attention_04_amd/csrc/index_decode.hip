@@ -32,9 +32,10 @@
 namespace csa {
 
 constexpr int DS_NT = 256;             // threads of a scanning block
+constexpr int DS_UNR = 4;              // key tiles per load batch of a scanning wave
 constexpr int DS_QT = 8;               // rows (queries x sequence) per sequence at most
 constexpr int DS_KEYS = 8192;          // LDS key words of a scanning block (all its rows)
-constexpr int DM_NT = 1024;            // threads of a merging block
+constexpr int DM_NT = 256;             // threads of a merging block
 constexpr int DM_UCAP = 8192;          // union capacity (chunks x cap)
 constexpr int DM_MAXW = 8192;          // bitmap words of the exact path -> 262144 candidates
 constexpr int DM_CAP = 1024;           // collected keys of the exact path
@@ -53,7 +54,7 @@ __host__ __device__ __forceinline__ DecodeGeom decode_geom(int64_t Tq, int64_t n
     DecodeGeom g;
     g.ch = Tq <= 2 ? 4096 : Tq <= 4 ? 2048 : 1024;
     g.nchunks = (int)((ncand + g.ch - 1) / g.ch);
-    const int64_t want = (4 * (int64_t)k * g.ch + ncand - 1) / (ncand > 0 ? ncand : 1);
+    const int64_t want = 4 * (int64_t)k * g.ch / (ncand > 0 ? ncand : 1);
     int cap = 32;
     while (cap < want) cap *= 2;
     int lim = 1;                                     // largest power of two <= DM_UCAP / nchunks
@@ -61,7 +62,7 @@ __host__ __device__ __forceinline__ DecodeGeom decode_geom(int64_t Tq, int64_t n
     cap = cap < lim ? cap : lim;
     g.cap = cap < g.ch ? cap : g.ch;
     const int u = g.nchunks * g.cap;
-    g.ept = u <= 2 * DM_NT ? 2 : u <= 4 * DM_NT ? 4 : 8;
+    g.ept = u <= 8 * DM_NT ? 8 : u <= 16 * DM_NT ? 16 : 32;
     return g;
 }
 
@@ -123,12 +124,22 @@ k_dscan(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     __shared__ int s_wcnt[DS_QT][NWV];
     const int64_t nc_max = n_candidates(q_pos0 + qv - 1, m, W);
     const int nkeys = (int)min((int64_t)ch, nc_max - c0);   // >= 1: the grid covers nc_max
+    // the first key batch of every wave is in flight during the set-up below
+    const int kbytes = dI / 2, kscales = dI / 32;
+    const TileSrc ts{kc + (b * Nc + c0) * kbytes, ks + (b * Nc + c0) * kscales, kbytes, kscales,
+                     nkeys, row, kb};
+    const int ntiles = (nkeys + 31) / 32;
+    u32x4 kwA[DS_UNR];
+    int ksA[DS_UNR];
+    load_first<DS_NT, DS_UNR, true>(ts, ntiles, 1, kwA, ksA);
     for (int i = tid; i < qv * SEL_NB; i += DS_NT) hist[i] = 0u;
 
     i32x8 aop;
     int sa;
     encode_q<T, HI>(q_idx, b, Tq, 0, qv, dI, aop, sa);
-    // lane slot u of a tile holds the scores of query qslot[u]
+    // lane slot u of a tile holds the scores of query qslot[u]; slots from
+    // nlive on hold no query of this launch
+    const int nlive = live_slots<HI>(qv);
     const int kbq = kb * 4 / HI;
     int qslot[NU], nvq[NU];
 #pragma unroll
@@ -140,18 +151,15 @@ k_dscan(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     }
     __syncthreads();
 
-    const int kbytes = dI / 2, kscales = dI / 32;
-    const TileSrc ts{kc + (b * Nc + c0) * kbytes, ks + (b * Nc + c0) * kscales, kbytes, kscales,
-                     nkeys, row, kb};
-    stream_tiles<DS_NT, 4, true>(ts, (nkeys + 31) / 32, 1, aop, sa,
-                                 [&](const f32x16& acc, int jt) {
+    stream_tiles_from<DS_NT, DS_UNR, true>(ts, ntiles, 1, aop, sa, kwA, ksA,
+                                           [&](const f32x16& acc, int jt) {
         const int jj = jt + row;
         uint32_t key[NU];
-        tile_keys<HI>(acc, key);
+        tile_keys<HI>(acc, key, nlive);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int q = qslot[u];
-            if (q >= qv || jj >= nkeys) continue;
+            if (u >= nlive || q >= qv || jj >= nkeys) continue;
             keys[q * ch + jj] = key[u];
             if (jj < nvq[u]) atomicAdd(&hist[q * SEL_NB + lvl1_bin(key[u])], 1u);
         }
@@ -223,7 +231,7 @@ struct DmSmem {
     __attribute__((aligned(16))) uint32_t eq[DM_MAXW];
     uint32_t hist[SEL_NB];
     u32x2 cb[DM_CAP];
-    uint32_t lo, hi, tau_need;
+    uint32_t lo, hi, tau_need, tau_thr;
     int above, in, ccnt, total, need_eq, unlisted;
     int scratch[DM_NT / WAVE + 1];
 };
@@ -237,7 +245,7 @@ struct DmSmem {
 template <typename Scan>
 __device__ __forceinline__ void exact_select(Scan&& scan, int nc, int need, int32_t* out, int k,
                                              DmSmem& S) {
-    static_assert(DM_MAXW == 8 * DM_NT, "merge-emit takes 8 words per thread");
+    static_assert(DM_MAXW % (8 * DM_NT) == 0, "merge-emit takes whole segments of 8 words per thread");
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int nw = (nc + 31) / 32;
     for (int i = tid; i < SEL_NB; i += DM_NT) S.hist[i] = 0u;
@@ -392,23 +400,79 @@ k_dmerge(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         const int c = p / cap, s = p - c * cap;
         key[e] = c < nchk && s < (int)S.cnt[c] ? ent[e][0] + 1u : 0u;
     }
+    // The k-th key of the union: its level-1 bin d from a histogram of the
+    // union, then the keys of bin d (few, as a rule) resolved exactly by one
+    // wave; a bin with more keys than the buffer takes the block-wide radix
+    // search.  The selection is key > thr, or key == thr among the first
+    // need_eq such keys in union order (= ascending candidate index).
     bool exact_needed = S.total < need;
-    uint32_t thr = 0u;
-    int need_eq = 0;
     if (!exact_needed) {
-        block_topk_threshold<DM_NT, EPT>(key, need, S.sel_sm, &thr, &need_eq);
-        // thr - 1 is the k-th key of the union; every left-out key is < tau
-        exact_needed = S.unlisted && thr - 1u < S.tau_need;
-    }
-    if (!exact_needed) {
-        int base, total;
-        const uint32_t flags = block_select_flags<DM_NT, EPT>(key, thr, need_eq, S.sel_sm,
-                                                             &base, &total);
+        for (int i = tid; i < SEL_NB; i += DM_NT) S.hist[i] = 0u;
+        if (tid == 0) S.ccnt = 0;
+        __syncthreads();
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
-            if (flags & (1u << e)) out[base++] = (int32_t)ent[e][1];
-        for (int s = total + tid; s < k; s += DM_NT) out[s] = -1;
-        return;
+            if (key[e]) atomicAdd(&S.hist[lvl1_bin(key[e] - 1u)], 1u);
+        __syncthreads();
+        if (tid < WAVE) {
+            int gt, in;
+            const int d = wave_hist_find(S.hist, need, &gt, &in);
+            uint32_t lo, hi;
+            lvl1_range(d, &lo, &hi);
+            if (tid == 0) {
+                S.lo = lo;
+                S.hi = hi;
+                S.above = gt;
+                S.in = in;
+            }
+        }
+        __syncthreads();
+        uint32_t thr1;                               // threshold in key + 1 form
+        int need_eq;
+        if (S.in <= DM_CAP) {
+            const uint32_t lo = S.lo, hi = S.hi;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const uint32_t v = key[e] - 1u;
+                if (key[e] && v >= lo && v < hi) S.cb[atomicAdd(&S.ccnt, 1)] = u32x2{v, 0u};
+            }
+            __syncthreads();
+            if (tid < WAVE) {
+                constexpr int CE = DM_CAP / WAVE;
+                uint32_t ck[CE];
+                bool valid[CE];
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    const int p = e * WAVE + tid;
+                    valid[e] = p < S.in;
+                    ck[e] = valid[e] ? S.cb[p][0] : 0u;
+                }
+                uint32_t t;
+                int ne;
+                wave_radix_threshold<CE>(ck, valid, need - S.above, S.sel, &t, &ne);
+                if (tid == 0) {
+                    S.tau_thr = t;
+                    S.need_eq = ne;
+                }
+            }
+            __syncthreads();
+            thr1 = S.tau_thr + 1u;
+            need_eq = S.need_eq;
+        } else {
+            block_topk_threshold<DM_NT, EPT>(key, need, S.sel_sm, &thr1, &need_eq);
+        }
+        // thr1 - 1 is the k-th key of the union; every left-out key is < tau
+        exact_needed = S.unlisted && thr1 - 1u < S.tau_need;
+        if (!exact_needed) {
+            int base, total;
+            const uint32_t flags = block_select_flags<DM_NT, EPT>(key, thr1, need_eq, S.sel_sm,
+                                                                 &base, &total);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (flags & (1u << e)) out[base++] = (int32_t)ent[e][1];
+            for (int s = total + tid; s < k; s += DM_NT) out[s] = -1;
+            return;
+        }
     }
     // exact path: rescore every candidate of the row, pass by pass
     i32x8 aop;
@@ -457,9 +521,9 @@ static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m
                            (const T*)q_idx, kc, ks, ws, topk, Tq, dI, Nc, m, W, k, q_pos0,   \
                            g);                                                               \
     } while (0)
-    if (g.ept == 2) CSA_DM_CASE(2);
-    else if (g.ept == 4) CSA_DM_CASE(4);
-    else CSA_DM_CASE(8);
+    if (g.ept == 8) CSA_DM_CASE(8);
+    else if (g.ept == 16) CSA_DM_CASE(16);
+    else CSA_DM_CASE(32);
 #undef CSA_DM_CASE
 }
 

@@ -171,11 +171,17 @@ def ws_index(L, *a):
 
 
 def test_index_workspace_and_rejects(L):
-    # decode rows over 262,112 candidates, per row: histogram (1024 words),
-    # in-range counts of the 64 collecting blocks, threshold (4 words), bitmap
-    # (8192 words), buffer of 64 x 16 (key, index) pairs, every candidate's score
+    # decode rows over 262,112 candidates, per row: 64 chunks of 4096, each
+    # with a list of 32 (key, index) pairs (4 x 512 x 4096 / 262112 rounded up
+    # to a power of two) and one (count, threshold) pair; no score array
     st, n = ws_index(L, 16, 1, 4, 64, 262144, 4, 128, 512, (1 << 20) - 1)
-    assert st == 0 and n == 16 * (1024 + 64 + 4 + 8192 + 2048 + 262112) * 4
+    assert st == 0 and n == 16 * 64 * (32 + 1) * 8
+    # k = 2048: 128 pairs per chunk
+    st, n = ws_index(L, 16, 1, 4, 64, 262144, 4, 128, 2048, (1 << 20) - 1)
+    assert st == 0 and n == 16 * 64 * (128 + 1) * 8
+    # 8 rows: chunks of 1024 (256 of them), 32 pairs each
+    st, n = ws_index(L, 2, 8, 4, 64, 262144, 4, 128, 512, (1 << 20) - 8)
+    assert st == 0 and n == 16 * 256 * (32 + 1) * 8
     # the streaming path (<= 32768 candidates) needs no workspace
     st, n = ws_index(L, 1, 16, 2, 32, 256, 4, 128, 16, 1008)
     assert st == 0 and n == 0
