@@ -43,6 +43,7 @@ _SIGS = {
                    ctypes.POINTER(_i64)] + [_p] * 4 + [_i64, _p], ctypes.c_int),
     "csa_index_topk_workspace": ([_i64] * 9 + [ctypes.POINTER(_sz)], ctypes.c_int),
     "csa_index_topk": ([ctypes.c_int] + [_i64] * 9 + [_p] * 5 + [_sz, _p], ctypes.c_int),
+    "csa_index_topk_noalloc": ([ctypes.c_int] + [_i64] * 9 + [_p] * 4 + [_p], ctypes.c_int),
     "csa_attend_workspace": ([ctypes.c_int] + [_i64] * 6 + [ctypes.POINTER(_sz)], ctypes.c_int),
     "csa_attend": ([ctypes.c_int] + [_i64] * 9 + [ctypes.c_float] + [_p] * 6 + [_i64, _i64]
                    + [_p, _p, _sz, _p], ctypes.c_int),
@@ -205,6 +206,19 @@ def csa_index_topk(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.T
         topk = _keep(torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device), stream)
     _call("csa_index_topk", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
           _ptr(k_codes), _ptr(k_scales), _ptr(topk), _ptr(ws), wsb, _stream(q_idx, stream))
+    return topk
+
+
+def csa_index_topk_noalloc(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                           *, m: int, W: int, k: int, q_pos0: int, topk=None, stream=None):
+    """csa_index_topk with the library's static scratch instead of a workspace
+    (the call allocates nothing when topk is given)."""
+    B, Tq, HI, dI = q_idx.shape
+    Nc = k_codes.shape[1]
+    if topk is None:
+        topk = _keep(torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device), stream)
+    _call("csa_index_topk_noalloc", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
+          _ptr(k_codes), _ptr(k_scales), _ptr(topk), _stream(q_idx, stream))
     return topk
 
 

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "csa.h"
 #include "common.h"
@@ -207,6 +208,59 @@ csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64
                           int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
     return index_topk_do(true, "csa_index_topk", dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx,
                          k_codes, k_scales, topk, ws, ws_bytes, stream);
+}
+
+// ---- selection without a workspace argument ---------------------------------
+// The static scratch array of csa_index_topk_noalloc.  In host code its name
+// is only a stand-in: kernels receive the per-device address that
+// hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];          // per device, looked up once
+}  // namespace
+
+static csa_status scratch_ptr(const char* fn, void** p) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(CSA_EDEVICE, "%s: no current device", fn);
+    CHECK(dev >= 0 && dev < MAX_DEVICES, CSA_EUNSUPPORTED, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* q = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !q)
+            return fail(CSA_EDEVICE, "%s: scratch address lookup failed: %s", fn,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = q;
+    }
+    *p = g_scratch_ptr[dev];
+    return CSA_OK;
+}
+
+csa_status csa_index_topk_noalloc(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                                  int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                                  const void* q_idx, const uint8_t* k_codes,
+                                  const uint8_t* k_scales, int32_t* topk,
+                                  hipStream_t stream) {
+    const char* fn = "csa_index_topk_noalloc";
+    // every check of csa_index_topk first (no device call), then the size
+    void* fake_ws = (void*)(uintptr_t)256;
+    if (csa_status s = index_topk_do(false, fn, dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx,
+                                     k_codes, k_scales, topk, fake_ws, SIZE_MAX, stream))
+        return s;
+    const size_t need =
+        csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0).ws_bytes;
+    CHECK(need <= CSA_NOALLOC_SCRATCH_BYTES, CSA_EUNSUPPORTED,
+          "%s: the selection needs %zu bytes of scratch, the static array holds %zu "
+          "(use csa_index_topk with a workspace)",
+          fn, need, (size_t)CSA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0)
+        if (csa_status s = scratch_ptr(fn, &ws)) return s;
+    return index_topk_do(true, fn, dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, k_codes,
+                         k_scales, topk, ws, need, stream);
 }
 
 static csa_status attend_shape(const char* fn, csa_dtype dt, int64_t B, int64_t Tq, int64_t H,

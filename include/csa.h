@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -176,6 +176,29 @@ csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64
                           const void *q_idx, const uint8_t *k_codes,
                           const uint8_t *k_scales, int32_t *topk, void *ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_index_topk_noalloc -- csa_index_topk without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The selection
+ * state lives in a static device array of CSA_NOALLOC_SCRATCH_BYTES bytes
+ * per GPU, held by the library until the process ends; its address is
+ * looked up once per device at the first call there.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and give undefined results.  Nothing in the array
+ * needs to start at any value.  Same arguments, layouts and results as
+ * csa_index_topk; the call allocates and frees nothing.
+ * Errors: CSA_EUNSUPPORTED when the selection needs more scratch than the
+ * array holds (csa_index_topk_workspace(...) > CSA_NOALLOC_SCRATCH_BYTES,
+ * e.g. many query rows over more than 32,768 candidates; decode rows and
+ * prefill rows over at most 32,768 candidates fit); otherwise as
+ * csa_index_topk.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+csa_status csa_index_topk_noalloc(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
+                                  int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
+                                  const void *q_idx, const uint8_t *k_codes,
+                                  const uint8_t *k_scales, int32_t *topk, hipStream_t stream);
 
 /*
  * csa_attend -- shared-KV multi-query attention over the kept compressed

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version(L):
     want = int(re.search(r"#define CSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.csa_abi_version() == want == 5
+    assert L.csa_abi_version() == want == 6
 
 
 def err(L):
@@ -225,3 +225,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(binding.CsaError):
         binding.lib()
+
+
+def test_index_noalloc_rejects_before_the_device(L):
+    """csa_index_topk_noalloc checks its arguments and the scratch size before
+    any device call: a selection needing more than the static array (140,000
+    query rows, up to 34,968 candidates: chunk lists of 2.6 GB) is refused."""
+    f = L.csa_index_topk_noalloc
+    assert f(1, 1, 140000, 4, 64, 35000, 4, 128, 512, 0, P, P, P, P, None) == EUNSUP
+    assert "scratch" in err(L)
+    assert f(1, 1, 16, 3, 64, 8192, 4, 128, 512, 0, P, P, P, P, None) == EUNSUP   # HI
+    assert f(1, 1, 16, 4, 64, 8192, 4, 128, 0, 0, P, P, P, P, None) == EINVAL     # k
+    assert f(1, 1, 16, 4, 64, 8192, 4, 128, 512, 0, None, P, P, P, None) == EINVAL
+    assert "null" in err(L)
+    assert f(1, 1, 1, 4, 64, 100, 4, 128, 512, 1 << 20, P, P, P, P, None) == EINVAL  # Nc
