@@ -39,7 +39,6 @@ constexpr int DM_NT = 256;             // threads of a merging block
 constexpr int DM_UCAP = 8192;          // union capacity (chunks x cap)
 constexpr int DM_MAXW = 8192;          // bitmap words of the exact path -> 262144 candidates
 constexpr int DM_CAP = 1024;           // collected keys of the exact path
-constexpr int DM_PASSES = 4;           // narrowing passes of the exact path (see below)
 
 // Chunk geometry of a launch: ch candidates per chunk (at most 4096; the
 // rows' keys fill at most DS_KEYS words of LDS), nchunks chunks over the
@@ -239,9 +238,9 @@ struct DmSmem {
 // Exact top `need` of the row's nc candidates by rescoring the keys
 // (scan(fn) calls fn(key, j) once for every candidate j < nc, spread over the
 // block).  Level 1 fixes a range of 2^17 keys (2^30 for bin 0, < 2^32 for
-// bin 1023); each narrowing pass splits it into SEL_NB parts, so the widths
-// go <= 2^32 -> 2^22 -> 2^12 -> 2^2 -> 1 and DM_PASSES = 4 passes always
-// end with <= DM_CAP keys in range or a single key value.
+// bin 1023); each narrowing pass splits it into SEL_NB parts, so
+// NARROW_PASSES passes always end with <= DM_CAP keys in range or a single
+// key value.
 template <typename Scan>
 __device__ __forceinline__ void exact_select(Scan&& scan, int nc, int need, int32_t* out, int k,
                                              DmSmem& S) {
@@ -266,7 +265,7 @@ __device__ __forceinline__ void exact_select(Scan&& scan, int nc, int need, int3
     }
     __syncthreads();
 #pragma unroll 1
-    for (int it = 0; it < DM_PASSES; ++it) {
+    for (int it = 0; it < NARROW_PASSES; ++it) {
         const uint32_t lo = S.lo, hi = S.hi;
         if (S.in <= DM_CAP || hi - lo == 1u) break;
         const int sh = range_shift(lo, hi);

@@ -306,9 +306,11 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         __syncthreads();
     }
 
-    // ================= exact multi-pass search for the remaining rows
+    // ================= exact multi-pass search for the remaining rows: every
+    // row still searching starts at level 1 here, so EXACT_PASSES passes
+    // (level 1, the narrowing passes, the collection) finish every row
 #pragma unroll 1
-    for (int pass = 0; pass < 8; ++pass) {
+    for (int pass = 0; pass < EXACT_PASSES; ++pass) {
         // per-slot state of this pass (registers)
         int md[NU], sh[NU];
         uint32_t lo[NU], hi[NU];

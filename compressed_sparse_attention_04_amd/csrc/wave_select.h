@@ -20,13 +20,13 @@ constexpr int SEL_NB = 1024;                       // histogram bins per level
 constexpr uint32_t L1_BASE = 121u << 23;           // fp32 bits of 2^-6
 constexpr uint32_t KEY_END = 0xFFFFFFFFu;          // exclusive top of key space
 
-__device__ __forceinline__ int lvl1_bin(uint32_t key) {
+__host__ __device__ __forceinline__ int lvl1_bin(uint32_t key) {
     if (key < L1_BASE) return 0;
     uint32_t d = ((key - L1_BASE) >> 17) + 1u;
     return d > 1023u ? 1023 : (int)d;
 }
 
-__device__ __forceinline__ void lvl1_range(int d, uint32_t* lo, uint32_t* hi) {
+__host__ __device__ __forceinline__ void lvl1_range(int d, uint32_t* lo, uint32_t* hi) {
     if (d == 0) {
         *lo = 0u;
         *hi = L1_BASE;
@@ -37,11 +37,29 @@ __device__ __forceinline__ void lvl1_range(int d, uint32_t* lo, uint32_t* hi) {
 }
 
 // shift that splits [lo, hi) into at most SEL_NB sub-ranges
-__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
-    uint32_t span = hi - lo - 1u;                  // >= 1 when refining
-    int bits = 32 - __clz(span);
+__host__ __device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t span = hi - lo - 1u;            // >= 1 when refining
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
     return bits > 10 ? bits - 10 : 0;
 }
+
+// Passes of the exact search.  A level-1 range is less than 2^32 keys wide;
+// a narrowing pass over a range whose span needs b bits leaves a sub-range
+// at most 2^max(b - 10, 0) wide, so widths go 2^32 -> 2^22 -> 2^12 -> 2^2
+// -> 1 and NARROW_PASSES narrowing passes always end with a single key
+// value (or fewer keys in range than the collection buffer holds, earlier).
+// The search is then level 1, the narrowing passes and one collection pass.
+__host__ __device__ constexpr int narrowing_passes_bound() {
+    int bits = 32, n = 0;
+    while (bits > 0) {
+        bits = bits > 10 ? bits - 10 : 0;
+        ++n;
+    }
+    return n;
+}
+constexpr int NARROW_PASSES = narrowing_passes_bound();
+constexpr int EXACT_PASSES = 1 + NARROW_PASSES + 1;
+static_assert(NARROW_PASSES == 4 && EXACT_PASSES == 6, "32-bit keys, 1024-bin passes");
 
 // Wave-wide search of a SEL_NB-bin histogram (lane l owns bins 16l..16l+15):
 // the largest bin d with count(bins > d) < need <= count(bins >= d).
