@@ -24,6 +24,18 @@ _sz = ctypes.c_size_t
 CSA_LAYER_CSA, CSA_LAYER_HCA = 0, 1
 
 
+class CsaIn(ctypes.Structure):
+    """csa_in: a strided view (base, element strides between sequences and rows)."""
+    _fields_ = [("p", ctypes.c_void_p), ("seq_stride", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64)]
+
+
+class CsaOut(ctypes.Structure):
+    """csa_out: a strided output view."""
+    _fields_ = [("p", ctypes.c_void_p), ("seq_stride", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64)]
+
+
 class LayerDesc(ctypes.Structure):
     """csa_layer_desc: one layer of a stack (kind, m, Nc and device pointers)."""
     _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
@@ -37,19 +49,22 @@ class LayerDesc(ctypes.Structure):
 _SIGS = {
     "csa_abi_version": ([], ctypes.c_int),
     "csa_last_error": ([], ctypes.c_char_p),
-    "hca_compress": ([ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p], ctypes.c_int),
-    "csa_quantize_mxfp4": ([ctypes.c_int, _i64, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "hca_compress": ([ctypes.c_int, _i64, _i64, _i64, _i64, CsaIn, CsaIn, _i64, CsaOut, _p],
+                     ctypes.c_int),
+    "csa_quantize_mxfp4": ([ctypes.c_int, _i64, _i64, CsaIn, _p, _p, _p], ctypes.c_int),
     "hca_append": ([ctypes.c_int] + [_i64] * 5 + [_p] * 4 + [_i64, _p, _p, _i64,
                    ctypes.POINTER(_i64)] + [_p] * 4 + [_i64, _p], ctypes.c_int),
     "csa_index_topk_workspace": ([_i64] * 9 + [ctypes.POINTER(_sz)], ctypes.c_int),
-    "csa_index_topk": ([ctypes.c_int] + [_i64] * 9 + [_p] * 5 + [_sz, _p], ctypes.c_int),
-    "csa_index_topk_noalloc": ([ctypes.c_int] + [_i64] * 9 + [_p] * 4 + [_p], ctypes.c_int),
+    "csa_index_topk": ([ctypes.c_int] + [_i64] * 9 + [CsaIn] + [_p] * 4 + [_sz, _p],
+                       ctypes.c_int),
+    "csa_index_topk_noalloc": ([ctypes.c_int] + [_i64] * 9 + [CsaIn] + [_p] * 3 + [_p],
+                               ctypes.c_int),
     "csa_attend_workspace": ([ctypes.c_int] + [_i64] * 6 + [ctypes.POINTER(_sz)], ctypes.c_int),
-    "csa_attend": ([ctypes.c_int] + [_i64] * 9 + [ctypes.c_float] + [_p] * 6 + [_i64, _i64]
-                   + [_p, _p, _sz, _p], ctypes.c_int),
+    "csa_attend": ([ctypes.c_int] + [_i64] * 9 + [ctypes.c_float] + [CsaIn] * 3 + [_p]
+                   + [CsaIn] * 2 + [_i64, _i64, CsaOut, _p, _sz, _p], ctypes.c_int),
     "hca_attend_workspace": ([ctypes.c_int] + [_i64] * 8 + [ctypes.POINTER(_sz)], ctypes.c_int),
-    "hca_attend": ([ctypes.c_int] + [_i64] * 8 + [ctypes.c_float] + [_p] * 5 + [_i64, _i64]
-                   + [_p, _p, _sz, _p], ctypes.c_int),
+    "hca_attend": ([ctypes.c_int] + [_i64] * 8 + [ctypes.c_float] + [CsaIn] * 5 + [_i64, _i64]
+                   + [CsaOut, _p, _sz, _p], ctypes.c_int),
     "csa_index_attend_workspace": ([ctypes.c_int] + [_i64] * 12 + [ctypes.POINTER(_sz)],
                                    ctypes.c_int),
     "csa_index_attend": ([ctypes.c_int] + [_i64] * 11 + [ctypes.c_float] + [_p] * 8 + [_i64, _i64]
@@ -112,8 +127,31 @@ def _ptr(t) -> int | None:
     if t is None:
         return None
     if not t.is_contiguous():
-        raise ValueError("libcsa takes dense row-major tensors")
+        raise ValueError("this libcsa entry point takes dense row-major tensors")
     return t.data_ptr()
+
+
+def _rows(t: torch.Tensor, nrow: int):
+    """Element strides (between sequences, between rows) of a tensor
+    [B, rows, *row] whose last nrow dims form contiguous rows."""
+    expect = 1
+    for d in range(t.dim() - 1, t.dim() - 1 - nrow, -1):
+        if t.shape[d] != 1 and t.stride(d) != expect:
+            raise ValueError("libcsa views need each row contiguous")
+        expect *= t.shape[d]
+    return t.stride(0), t.stride(1)
+
+
+def _in(t: torch.Tensor, nrow: int = 1) -> CsaIn:
+    """A [B, rows, *row] tensor (rows contiguous, any sequence and row
+    strides) as a csa_in view."""
+    ss, rs = _rows(t, nrow)
+    return CsaIn(t.data_ptr(), ss, rs)
+
+
+def _out(t: torch.Tensor, nrow: int = 1) -> CsaOut:
+    ss, rs = _rows(t, nrow)
+    return CsaOut(t.data_ptr(), ss, rs)
 
 
 def _stream(t: torch.Tensor, stream) -> int | None:
@@ -149,11 +187,12 @@ def _workspace(ws, device, query, stream=None):
 
 
 def hca_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out=None, stream=None):
-    """Softmax-gated pooling: x [B,T,C], gate [B,T,1|C] -> [B, T//m, C]."""
+    """Softmax-gated pooling: x [B,T,C], gate [B,T,1|C] -> [B, T//m, C] (any
+    views whose rows are contiguous)."""
     B, T, C = x.shape
     if out is None:
         out = _keep(torch.empty((B, T // m, C), dtype=x.dtype, device=x.device), stream)
-    _call("hca_compress", _dt(x), B, T, C, m, _ptr(x), _ptr(gate), gate.shape[-1], _ptr(out),
+    _call("hca_compress", _dt(x), B, T, C, m, _in(x), _in(gate), gate.shape[-1], _out(out),
           _stream(x, stream))
     return out
 
@@ -183,8 +222,11 @@ def csa_quantize_mxfp4(x: torch.Tensor, codes=None, scales=None, stream=None):
     if scales is None:
         scales = _keep(torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device),
                        stream)
-    _call("csa_quantize_mxfp4", _dt(x), rows, d, _ptr(x), _ptr(codes), _ptr(scales),
-          _stream(x, stream))
+    x2 = x.view(rows, d)                  # evenly spaced rows (no copy), else an error
+    if d and x2.stride(1) != 1:
+        raise ValueError("libcsa views need each row contiguous")
+    _call("csa_quantize_mxfp4", _dt(x), rows, d, CsaIn(x.data_ptr(), 0, x2.stride(0)),
+          _ptr(codes), _ptr(scales), _stream(x, stream))
     return codes, scales
 
 
@@ -204,7 +246,7 @@ def csa_index_topk(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.T
         lambda: csa_index_topk_workspace(B, Tq, HI, dI, Nc, m, W, k, q_pos0), stream)
     if topk is None:
         topk = _keep(torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device), stream)
-    _call("csa_index_topk", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
+    _call("csa_index_topk", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _in(q_idx, 2),
           _ptr(k_codes), _ptr(k_scales), _ptr(topk), _ptr(ws), wsb, _stream(q_idx, stream))
     return topk
 
@@ -217,8 +259,8 @@ def csa_index_topk_noalloc(q_idx: torch.Tensor, k_codes: torch.Tensor, k_scales:
     Nc = k_codes.shape[1]
     if topk is None:
         topk = _keep(torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device), stream)
-    _call("csa_index_topk_noalloc", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0, _ptr(q_idx),
-          _ptr(k_codes), _ptr(k_scales), _ptr(topk), _stream(q_idx, stream))
+    _call("csa_index_topk_noalloc", _dt(q_idx), B, Tq, HI, dI, Nc, m, W, k, q_pos0,
+          _in(q_idx, 2), _ptr(k_codes), _ptr(k_scales), _ptr(topk), _stream(q_idx, stream))
     return topk
 
 
@@ -239,8 +281,8 @@ def csa_attend(q, ck, cv, topk, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0
                           stream)
     if out is None:
         out = _keep(torch.empty_like(q), stream)
-    _call("csa_attend", _dt(q), B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
-          _ptr(cv), _ptr(topk), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws),
+    _call("csa_attend", _dt(q), B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _in(q, 2), _in(ck),
+          _in(cv), _ptr(topk), _in(rk), _in(rv), raw_pos0, raw_len, _out(out, 2), _ptr(ws),
           wsb, _stream(q, stream))
     return out
 
@@ -261,8 +303,8 @@ def hca_attend(q, ck, cv, rk, rv, *, m: int, W: int, q_pos0: int, raw_pos0: int,
         lambda: hca_attend_workspace(_dt(q), B, Tq, H, D, Nc, m, W, q_pos0), stream)
     if out is None:
         out = _keep(torch.empty_like(q), stream)
-    _call("hca_attend", _dt(q), B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck),
-          _ptr(cv), _ptr(rk), _ptr(rv), raw_pos0, raw_len, _ptr(out), _ptr(ws), wsb,
+    _call("hca_attend", _dt(q), B, Tq, H, D, Nc, m, W, q_pos0, scale, _in(q, 2), _in(ck),
+          _in(cv), _in(rk), _in(rv), raw_pos0, raw_len, _out(out, 2), _ptr(ws), wsb,
           _stream(q, stream))
     return out
 

@@ -69,6 +69,38 @@ csa_status check_positions(const char* fn, int64_t Tq, int64_t Nc, int64_t m, in
     return CSA_OK;
 }
 
+// A strided view as the kernels take it (element strides)
+csa::RowStrides strides(const csa_in& v) { return {v.seq_stride, v.row_stride}; }
+csa::RowStrides strides(const csa_out& v) { return {v.seq_stride, v.row_stride}; }
+
+// A dense [B][rows][row_elems] tensor as a view
+csa_in dense_in(const void* p, int64_t rows, int64_t row_elems) {
+    return csa_in{p, rows * row_elems, row_elems};
+}
+csa_out dense_out(void* p, int64_t rows, int64_t row_elems) {
+    return csa_out{p, rows * row_elems, row_elems};
+}
+
+// A view of B sequences of `rows` rows of `row_elems` contiguous elements of
+// esize bytes: non-negative strides, rows that do not overlap, and (align)
+// base and strides on 16-byte boundaries; an output's sequences must not
+// overlap either.
+csa_status check_view(const char* fn, const char* name, const void* p, int64_t ss, int64_t rs,
+                      int64_t B, int64_t rows, int64_t row_elems, int64_t esize, bool out,
+                      bool align = true) {
+    CHECK(p, CSA_EINVAL, "%s: null pointer (%s)", fn, name);
+    CHECK(ss >= 0 && rs >= 0, CSA_EINVAL, "%s: %s: strides must be >= 0", fn, name);
+    CHECK(rows <= 1 || rs >= row_elems, CSA_EINVAL,
+          "%s: %s: row stride %lld is below the row length %lld", fn, name, (long long)rs,
+          (long long)row_elems);
+    CHECK(!align || (((uintptr_t)p & 15u) == 0 && (ss * esize) % 16 == 0 && (rs * esize) % 16 == 0),
+          CSA_EINVAL, "%s: %s: base and strides must be 16-byte aligned", fn, name);
+    if (out && B > 1 && rows > 0)
+        CHECK(ss >= (rows - 1) * rs + row_elems, CSA_EINVAL,
+              "%s: %s: sequence stride %lld makes sequences overlap", fn, name, (long long)ss);
+    return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,9 +109,8 @@ int csa_abi_version(void) { return CSA_ABI_VERSION; }
 
 const char* csa_last_error(void) { return g_err; }
 
-csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m,
-                        const void* x, const void* gate, int64_t gate_channels, void* out,
-                        hipStream_t stream) {
+csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m, csa_in x,
+                        csa_in gate, int64_t gate_channels, csa_out out, hipStream_t stream) {
     const char* fn = "hca_compress";
     if (csa_status s = check_dtype(dt, fn)) return s;
     CHECK(B >= 1 && B < 65536 * 1024LL, CSA_EINVAL, "%s: B out of range", fn);
@@ -89,13 +120,21 @@ csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m
           "%s: C must be a multiple of 8 in [8, 1024] (got %lld)", fn, (long long)C);
     CHECK(gate_channels == 1 || gate_channels == C, CSA_EINVAL,
           "%s: gate_channels must be 1 or C", fn);
-    CHECK(x && gate && out, CSA_EINVAL, "%s: null pointer", fn);
-    CHECK(aligned16(x) && aligned16(out) && (gate_channels == 1 || aligned16(gate)), CSA_EINVAL,
-          "%s: x, out (and a per-channel gate) must be 16-byte aligned", fn);
+    const int64_t esz = dt == CSA_F32 ? 4 : 2;
+    if (csa_status s = check_view(fn, "x", x.p, x.seq_stride, x.row_stride, B, T, C, esz, false))
+        return s;
+    if (csa_status s = check_view(fn, "gate", gate.p, gate.seq_stride, gate.row_stride, B, T,
+                                  gate_channels, esz, false, gate_channels != 1))
+        return s;
+    if (csa_status s = check_view(fn, "out", out.p, out.seq_stride, out.row_stride, B, T / m, C,
+                                  esz, true))
+        return s;
     const int64_t blocks = (m <= 16) ? (B * (T / m) * (C / 8) + 255) / 256 : B * (T / m);
     CHECK(blocks < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "%s: problem too large", fn);
-    return launched(csa::launch_compress((int)dt, x, gate, out, B, T, (int)C, (int)m,
-                                         (int)gate_channels, stream), fn);
+    return launched(csa::launch_compress((int)dt, x.p, strides(x), gate.p, strides(gate), out.p,
+                                         strides(out), B, T, (int)C, (int)m, (int)gate_channels,
+                                         stream),
+                    fn);
 }
 
 csa_status hca_append(csa_dtype dt, int64_t B, int64_t C, int64_t m, int64_t W, int64_t t,
@@ -140,18 +179,22 @@ csa_status hca_append(csa_dtype dt, int64_t B, int64_t C, int64_t m, int64_t W, 
     return st;
 }
 
-csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, const void* x,
-                              uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, csa_in x, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
     const char* fn = "csa_quantize_mxfp4";
     if (csa_status s = check_dtype(dt, fn)) return s;
     CHECK(rows >= 0, CSA_EINVAL, "%s: rows must be >= 0", fn);
     CHECK(d >= 32 && d % 32 == 0, CSA_EINVAL, "%s: d must be a positive multiple of 32", fn);
-    CHECK(x && codes && scales, CSA_EINVAL, "%s: null pointer", fn);
-    CHECK(aligned16(x) && aligned16(codes), CSA_EINVAL, "%s: x and codes must be 16-byte aligned",
-          fn);
+    const int64_t esz = dt == CSA_F32 ? 4 : 2;
+    if (csa_status s = check_view(fn, "x", x.p, 0, x.row_stride, 1, rows, d, esz, false))
+        return s;
+    CHECK(codes && scales, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(codes), CSA_EINVAL, "%s: codes must be 16-byte aligned", fn);
     CHECK((rows * (d / 32) + 255) / 256 < ((int64_t)1 << 31), CSA_EUNSUPPORTED,
           "%s: problem too large", fn);
-    return launched(csa::launch_quant_mxfp4((int)dt, x, codes, scales, rows, (int)d, stream), fn);
+    return launched(csa::launch_quant_mxfp4((int)dt, x.p, x.row_stride, codes, scales, rows,
+                                            (int)d, stream),
+                    fn);
 }
 
 static csa_status index_args(const char* fn, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
@@ -185,26 +228,30 @@ csa_status csa_index_topk_workspace(int64_t B, int64_t Tq, int64_t HI, int64_t d
 // run == false: every check of the entry point, no launch
 static csa_status index_topk_do(bool run, const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
                                 int64_t HI, int64_t dI, int64_t Nc, int64_t m, int64_t W,
-                                int64_t k, int64_t q_pos0, const void* q_idx,
+                                int64_t k, int64_t q_pos0, csa_in q_idx,
                                 const uint8_t* k_codes, const uint8_t* k_scales, int32_t* topk,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
     if (csa_status s = check_dtype(dt, fn)) return s;
     if (csa_status s = index_args(fn, B, Tq, HI, dI, Nc, m, W, k, q_pos0)) return s;
-    CHECK(q_idx && k_codes && k_scales && topk, CSA_EINVAL, "%s: null pointer", fn);
-    CHECK(aligned16(q_idx) && aligned16(k_codes), CSA_EINVAL,
-          "%s: q_idx and k_codes must be 16-byte aligned", fn);
+    const int64_t esz = dt == CSA_F32 ? 4 : 2;
+    if (csa_status s = check_view(fn, "q_idx", q_idx.p, q_idx.seq_stride, q_idx.row_stride, B,
+                                  Tq, HI * dI, esz, false))
+        return s;
+    CHECK(k_codes && k_scales && topk, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(k_codes), CSA_EINVAL, "%s: k_codes must be 16-byte aligned", fn);
     csa::IndexPlan p = csa::plan_index(B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0);
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
     if (!run) return CSA_OK;
     return launched(csa::launch_index_topk((int)dt, p, B, Tq, (int)HI, (int)dI, Nc, m, W, (int)k,
-                                           q_pos0, q_idx, k_codes, k_scales, topk, ws, stream),
+                                           q_pos0, q_idx.p, strides(q_idx), k_codes, k_scales,
+                                           topk, ws, stream),
                     fn);
 }
 
 csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
                           int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
-                          const void* q_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                          csa_in q_idx, const uint8_t* k_codes, const uint8_t* k_scales,
                           int32_t* topk, void* ws, size_t ws_bytes, hipStream_t stream) {
     return index_topk_do(true, "csa_index_topk", dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx,
                          k_codes, k_scales, topk, ws, ws_bytes, stream);
@@ -241,7 +288,7 @@ static csa_status scratch_ptr(const char* fn, void** p) {
 
 csa_status csa_index_topk_noalloc(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
                                   int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
-                                  const void* q_idx, const uint8_t* k_codes,
+                                  csa_in q_idx, const uint8_t* k_codes,
                                   const uint8_t* k_scales, int32_t* topk,
                                   hipStream_t stream) {
     const char* fn = "csa_index_topk_noalloc";
@@ -280,8 +327,8 @@ static csa_status attend_shape(const char* fn, csa_dtype dt, int64_t B, int64_t 
     return CSA_OK;
 }
 
-// The bf16 attention kernel addresses rows with 32-bit byte offsets and
-// key-list positions with 32-bit ints.
+// The bf16 attention kernel addresses key and value rows with 32-bit byte
+// offsets from their sequence's base and key-list positions with 32-bit ints.
 static csa_status attend_ranges(const char* fn, int64_t Nc, int64_t D, int64_t raw_len, int64_t k,
                                 int64_t W, int64_t q_pos0, int64_t Tq, int64_t m) {
     const int64_t lim = ((int64_t)1 << 31) - 1;
@@ -290,6 +337,38 @@ static csa_status attend_ranges(const char* fn, int64_t Nc, int64_t D, int64_t r
     const int64_t keys = (Tq > 0 ? csa::n_candidates(q_pos0 + Tq - 1, m, W) : 0) + k + W;
     CHECK(keys <= lim, CSA_EUNSUPPORTED, "%s: key list too long", fn);
     return CSA_OK;
+}
+
+// The views of one attention call: q / o rows are query tokens of [H][D]
+// contiguous elements, ck / cv rows compressed entries and rk / rv rows raw
+// tokens of D contiguous elements; a sequence's key and value rows must lie
+// within 2 GiB of its first row.
+static csa_status attend_views(const char* fn, csa_dtype dt, int64_t B, int64_t Tq, int64_t H,
+                               int64_t D, int64_t Nc, int64_t raw_len, const csa_in& q,
+                               const csa_in& ck, const csa_in& cv, const csa_in& rk,
+                               const csa_in& rv, const csa_out& o) {
+    const int64_t esz = dt == CSA_F32 ? 4 : 2;
+    if (csa_status s = check_view(fn, "q", q.p, q.seq_stride, q.row_stride, B, Tq, H * D, esz,
+                                  false))
+        return s;
+    const csa_in* kv[4] = {&ck, &cv, &rk, &rv};
+    const char* names[4] = {"ck", "cv", "rk", "rv"};
+    for (int i = 0; i < 4; ++i) {
+        const int64_t rows = i < 2 ? Nc : raw_len;
+        if (csa_status s = check_view(fn, names[i], kv[i]->p, kv[i]->seq_stride,
+                                      kv[i]->row_stride, B, rows, D, esz, false))
+            return s;
+        CHECK(rows == 0 || (rows - 1) * kv[i]->row_stride * esz + D * esz <= ((int64_t)1 << 31) - 1,
+              CSA_EUNSUPPORTED, "%s: %s: a sequence's rows span more than 2 GiB", fn, names[i]);
+    }
+    return check_view(fn, "o", o.p, o.seq_stride, o.row_stride, B, Tq, H * D, esz, true);
+}
+
+static csa::AttendIO attend_io(const csa_in& q, const csa_in& ck, const csa_in& cv,
+                               const csa_in& rk, const csa_in& rv, const csa_out& o) {
+    return csa::AttendIO{q.p,          ck.p,          cv.p,          rk.p,        rv.p,
+                         o.p,          strides(q),    strides(ck),   strides(cv), strides(rk),
+                         strides(rv),  strides(o)};
 }
 
 csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
@@ -304,33 +383,33 @@ csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, 
 
 static csa_status csa_attend_do(bool run, const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
                                 int64_t H, int64_t D, int64_t Nc, int64_t m, int64_t W,
-                                int64_t k, int64_t q_pos0, float scale, const void* q,
-                                const void* ck, const void* cv, const int32_t* topk,
-                                const void* rk, const void* rv, int64_t raw_pos0,
-                                int64_t raw_len, void* o, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+                                int64_t k, int64_t q_pos0, float scale, csa_in q, csa_in ck,
+                                csa_in cv, const int32_t* topk, csa_in rk, csa_in rv,
+                                int64_t raw_pos0, int64_t raw_len, csa_out o, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
     if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
     CHECK(k >= 1 && k <= 2048, CSA_EINVAL, "%s: k must be in [1, 2048]", fn);
     CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
+    CHECK(topk, CSA_EINVAL, "%s: null pointer", fn);
+    if (csa_status s = attend_views(fn, dt, B, Tq, H, D, Nc, raw_len, q, ck, cv, rk, rv, o))
+        return s;
     if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
-    CHECK(q && ck && cv && topk && rk && rv && o, CSA_EINVAL, "%s: null pointer", fn);
-    CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
-              aligned16(o), CSA_EINVAL, "%s: tensors must be 16-byte aligned", fn);
     if (csa_status s = attend_ranges(fn, Nc, D, raw_len, k, W, q_pos0, Tq, m)) return s;
     csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, k + W);
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
     if (!run) return CSA_OK;
-    return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck,
-                                       cv, topk, rk, rv, raw_pos0, raw_len, o, ws, stream),
+    return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, k, q_pos0, scale,
+                                       attend_io(q, ck, cv, rk, rv, o), topk, raw_pos0, raw_len,
+                                       ws, stream),
                     fn);
 }
 
 csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
-                      int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
-                      const void* q, const void* ck, const void* cv, const int32_t* topk,
-                      const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
-                      void* o, void* ws, size_t ws_bytes, hipStream_t stream) {
+                      int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale, csa_in q,
+                      csa_in ck, csa_in cv, const int32_t* topk, csa_in rk, csa_in rv,
+                      int64_t raw_pos0, int64_t raw_len, csa_out o, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
     return csa_attend_do(true, "csa_attend", dt, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck,
                          cv, topk, rk, rv, raw_pos0, raw_len, o, ws, ws_bytes, stream);
 }
@@ -352,31 +431,29 @@ csa_status hca_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, 
 
 static csa_status hca_attend_do(bool run, const char* fn, csa_dtype dt, int64_t B, int64_t Tq,
                                 int64_t H, int64_t D, int64_t Nc, int64_t m, int64_t W,
-                                int64_t q_pos0, float scale, const void* q, const void* ck,
-                                const void* cv, const void* rk, const void* rv,
-                                int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+                                int64_t q_pos0, float scale, csa_in q, csa_in ck, csa_in cv,
+                                csa_in rk, csa_in rv, int64_t raw_pos0, int64_t raw_len,
+                                csa_out o, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (csa_status s = attend_shape(fn, dt, B, Tq, H, D)) return s;
     CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
+    if (csa_status s = attend_views(fn, dt, B, Tq, H, D, Nc, raw_len, q, ck, cv, rk, rv, o))
+        return s;
     if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
-    CHECK(q && ck && cv && rk && rv && o, CSA_EINVAL, "%s: null pointer", fn);
-    CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
-              aligned16(o), CSA_EINVAL, "%s: tensors must be 16-byte aligned", fn);
     if (csa_status s = attend_ranges(fn, Nc, D, raw_len, 0, W, q_pos0, Tq, m)) return s;
     csa::AttendPlan p = csa::plan_attend((int)dt, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0));
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
     if (!run) return CSA_OK;
-    return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, 0, q_pos0, scale, q, ck,
-                                       cv, nullptr, rk, rv, raw_pos0, raw_len, o, ws, stream),
+    return launched(csa::launch_attend((int)dt, p, B, Tq, H, D, Nc, m, W, 0, q_pos0, scale,
+                                       attend_io(q, ck, cv, rk, rv, o), nullptr, raw_pos0,
+                                       raw_len, ws, stream),
                     fn);
 }
 
 csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
-                      int64_t m, int64_t W, int64_t q_pos0, float scale, const void* q,
-                      const void* ck, const void* cv, const void* rk, const void* rv,
-                      int64_t raw_pos0, int64_t raw_len, void* o, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
+                      int64_t m, int64_t W, int64_t q_pos0, float scale, csa_in q, csa_in ck,
+                      csa_in cv, csa_in rk, csa_in rv, int64_t raw_pos0, int64_t raw_len,
+                      csa_out o, void* ws, size_t ws_bytes, hipStream_t stream) {
     return hca_attend_do(true, "hca_attend", dt, B, Tq, H, D, Nc, m, W, q_pos0, scale, q, ck, cv,
                          rk, rv, raw_pos0, raw_len, o, ws, ws_bytes, stream);
 }
@@ -440,11 +517,14 @@ static csa_status index_attend_args(const char* fn, csa_dtype dt, int64_t B, int
     CHECK(n_chunks >= 1 && n_chunks <= 64, CSA_EINVAL, "%s: n_chunks must be in [1, 64]", fn);
     // every check of the two steps over the whole range (workspaces apart)
     void* fake_ws = (void*)(uintptr_t)256;
-    csa_status s = index_topk_do(false, fn, dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx,
-                                 k_codes, k_scales, topk, fake_ws, SIZE_MAX, nullptr);
+    csa_status s = index_topk_do(false, fn, dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0,
+                                 dense_in(q_idx, Tq, HI * dI), k_codes, k_scales, topk, fake_ws,
+                                 SIZE_MAX, nullptr);
     if (s == CSA_OK)
-        s = csa_attend_do(false, fn, dt, B, Tq, H, D, Nc, m, W, k, q_pos0, scale, q, ck, cv, topk,
-                          rk, rv, raw_pos0, raw_len, o, fake_ws, SIZE_MAX, nullptr);
+        s = csa_attend_do(false, fn, dt, B, Tq, H, D, Nc, m, W, k, q_pos0, scale,
+                          dense_in(q, Tq, H * D), dense_in(ck, Nc, D), dense_in(cv, Nc, D), topk,
+                          dense_in(rk, raw_len, D), dense_in(rv, raw_len, D), raw_pos0, raw_len,
+                          dense_out(o, Tq, H * D), fake_ws, SIZE_MAX, nullptr);
     return s;
 }
 
@@ -517,7 +597,7 @@ csa_status csa_index_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int6
             hipError_t e = csa::launch_index_topk(
                 (int)dt, csa::plan_index(1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a),
                 1, rows, (int)HI, (int)dI, Nc, m, W, (int)k, q_pos0 + a, qib + r0 * HI * dI * esz,
-                kcb, ksb, topk + r0 * k, iws, is);
+                csa::RowStrides{Tq * HI * dI, HI * dI}, kcb, ksb, topk + r0 * k, iws, is);
             if (e == hipSuccess && two) e = hipEventRecord(ev.e[c], is);
             if (e != hipSuccess) return launched(e, fn);
         }
@@ -527,10 +607,14 @@ csa_status csa_index_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int6
             const int64_t r0 = b * Tq + a;
             hipError_t e = two ? hipStreamWaitEvent(stream, ev.e[c], 0) : hipSuccess;
             if (e == hipSuccess)
-                e = csa::launch_attend((int)dt, slice_attend_plan(dt, B, Tq, rows, H, D, k, W), 1,
-                                       rows, H, D, Nc, m, W, k, q_pos0 + a, scale,
-                                       qb + r0 * H * D * esz, ckb, cvb, topk + r0 * k, rkb, rvb,
-                                       raw_pos0, raw_len, ob + r0 * H * D * esz, aws, stream);
+                e = csa::launch_attend(
+                    (int)dt, slice_attend_plan(dt, B, Tq, rows, H, D, k, W), 1, rows, H, D, Nc, m,
+                    W, k, q_pos0 + a, scale,
+                    attend_io(dense_in(qb + r0 * H * D * esz, Tq, H * D), dense_in(ckb, Nc, D),
+                              dense_in(cvb, Nc, D), dense_in(rkb, raw_len, D),
+                              dense_in(rvb, raw_len, D),
+                              dense_out(ob + r0 * H * D * esz, Tq, H * D)),
+                    topk + r0 * k, raw_pos0, raw_len, aws, stream);
             if (e != hipSuccess) return launched(e, fn);
         }
     }
@@ -606,14 +690,20 @@ static csa_status stack_layer(bool run, const char* fn, int64_t l, csa_dtype dt,
     csa_status s;
     if (L.kind == CSA_LAYER_CSA) {
         s = index_topk_do(run, "csa_index_topk", dt, B, Tq, HI, dI, L.Nc, L.m, W, k, q_pos0,
-                          L.q_idx, L.k_codes, L.k_scales, L.topk, ws, ws_bytes, stream);
+                          dense_in(L.q_idx, Tq, HI * dI), L.k_codes, L.k_scales, L.topk, ws,
+                          ws_bytes, stream);
         if (s == CSA_OK)
             s = csa_attend_do(run, "csa_attend", dt, B, Tq, H, D, L.Nc, L.m, W, k, q_pos0, scale,
-                              L.q, L.ck, L.cv, L.topk, L.rk, L.rv, raw_pos0, raw_len, L.o, ws,
-                              ws_bytes, stream);
+                              dense_in(L.q, Tq, H * D), dense_in(L.ck, L.Nc, D),
+                              dense_in(L.cv, L.Nc, D), L.topk, dense_in(L.rk, raw_len, D),
+                              dense_in(L.rv, raw_len, D), raw_pos0, raw_len,
+                              dense_out(L.o, Tq, H * D), ws, ws_bytes, stream);
     } else {
-        s = hca_attend_do(run, "hca_attend", dt, B, Tq, H, D, L.Nc, L.m, W, q_pos0, scale, L.q,
-                          L.ck, L.cv, L.rk, L.rv, raw_pos0, raw_len, L.o, ws, ws_bytes, stream);
+        s = hca_attend_do(run, "hca_attend", dt, B, Tq, H, D, L.Nc, L.m, W, q_pos0, scale,
+                          dense_in(L.q, Tq, H * D), dense_in(L.ck, L.Nc, D),
+                          dense_in(L.cv, L.Nc, D), dense_in(L.rk, raw_len, D),
+                          dense_in(L.rv, raw_len, D), raw_pos0, raw_len,
+                          dense_out(L.o, Tq, H * D), ws, ws_bytes, stream);
     }
     if (s != CSA_OK) {
         char inner[512];
@@ -686,10 +776,13 @@ csa_status csa_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t
     csa::AttendPlan p = csa::plan_attend(1, B, Tq, H, D, k + W);
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
-    return launched(csa::launch_attend_mx8(p, B, Tq, H, Nc, m, W, k, q_pos0, scale, q,
-                                           (const uint8_t*)ck, (const uint8_t*)cv,
-                                           (const uint8_t*)ck_scales, (const uint8_t*)cv_scales,
-                                           topk, rk, rv, raw_pos0, raw_len, o, ws, stream),
+    return launched(csa::launch_attend_mx8(
+                        p, B, Tq, H, Nc, m, W, k, q_pos0, scale,
+                        attend_io(dense_in(q, Tq, H * D), dense_in(ck, Nc, D),
+                                  dense_in(cv, Nc, D), dense_in(rk, raw_len, D),
+                                  dense_in(rv, raw_len, D), dense_out(o, Tq, H * D)),
+                        (const uint8_t*)ck_scales, (const uint8_t*)cv_scales, topk, raw_pos0,
+                        raw_len, ws, stream),
                     fn);
 }
 
@@ -707,10 +800,13 @@ csa_status hca_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t
     csa::AttendPlan p = csa::plan_attend(1, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0));
     CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
           "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
-    return launched(csa::launch_attend_mx8(p, B, Tq, H, Nc, m, W, 0, q_pos0, scale, q,
-                                           (const uint8_t*)ck, (const uint8_t*)cv,
-                                           (const uint8_t*)ck_scales, (const uint8_t*)cv_scales,
-                                           nullptr, rk, rv, raw_pos0, raw_len, o, ws, stream),
+    return launched(csa::launch_attend_mx8(
+                        p, B, Tq, H, Nc, m, W, 0, q_pos0, scale,
+                        attend_io(dense_in(q, Tq, H * D), dense_in(ck, Nc, D),
+                                  dense_in(cv, Nc, D), dense_in(rk, raw_len, D),
+                                  dense_in(rv, raw_len, D), dense_out(o, Tq, H * D)),
+                        (const uint8_t*)ck_scales, (const uint8_t*)cv_scales, nullptr, raw_pos0,
+                        raw_len, ws, stream),
                     fn);
 }
 

@@ -101,19 +101,27 @@ __device__ __forceinline__ int slot_of(int r, int c) { return c ^ row_swz<D>(r);
 // All offsets fit 32 bits (validated on the host).
 // SHARED: one vector serves as key and value (the same rows passed as K and
 // V), so only the K rows are copied and the V operands are read from them.
+// Rows of one sequence's four K/V sources: base addresses and row strides in
+// bytes (a source's rows lie within 2 GiB of its base; checked on the host).
+struct KvRows {
+    const char *ck, *cv, *rk, *rv;
+    uint32_t ck_rb, cv_rb, rk_rb, rv_rb;
+};
+
 template <int NW, int D, bool SHARED>
 __device__ __forceinline__ void issue_tile(int wave, int tau, int ct, int nval, int nwin,
                                            int raw_first,
                                            bool sparse, const CSA_LDS int32_t* ssel,
-                                           const char* ckb, const char* cvb, const char* rkb,
-                                           const char* rvb, CSA_LDS uint8_t* sk,
+                                           const KvRows& kv, CSA_LDS uint8_t* sk,
                                            CSA_LDS uint8_t* sv) {
     using G = TileGeom<D>;
     const int lane = threadIdx.x % 64;
     const bool comp = tau < ct;
     const int base = comp ? ATT_KT * tau : ATT_KT * (tau - ct);
-    const char* kb = comp ? ckb : rkb;
-    const char* vb = comp ? cvb : rvb;
+    const char* kb = comp ? kv.ck : kv.rk;
+    const char* vb = comp ? kv.cv : kv.rv;
+    const uint32_t krb = comp ? kv.ck_rb : kv.rk_rb;
+    const uint32_t vrb = comp ? kv.cv_rb : kv.rv_rb;
 #pragma unroll
     for (int ins = wave; ins < G::NINS; ins += NW) {
         const int r = ins * G::RPI + lane / G::CH;
@@ -121,15 +129,25 @@ __device__ __forceinline__ void issue_tile(int wave, int tau, int ct, int nval, 
         int row;
         if (comp) row = sparse ? ssel[base + r] : min(base + r, nval - 1);
         else row = raw_first + min(base + r, nwin - 1);
-        const uint32_t off = (uint32_t)row * (uint32_t)G::ROWB + (uint32_t)cb;
-        __builtin_amdgcn_global_load_lds(kb + off, (CSA_LDS void*)(sk + ins * G::RPI * G::ROWB),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kb + ((uint32_t)row * krb + (uint32_t)cb),
+                                         (CSA_LDS void*)(sk + ins * G::RPI * G::ROWB), 16, 0, 0);
         if constexpr (!SHARED)
-            __builtin_amdgcn_global_load_lds(vb + off,
+            __builtin_amdgcn_global_load_lds(vb + ((uint32_t)row * vrb + (uint32_t)cb),
                                              (CSA_LDS void*)(sv + ins * G::RPI * G::ROWB), 16, 0,
                                              0);
     }
 }
+
+// Pointers and strides of one attention call (element strides; Q and O rows
+// are query tokens holding [H][D], K/V rows are entries or raw tokens)
+template <typename TQ, typename TKV>
+struct AttnArgs {
+    const TQ* q;
+    const TKV *ck, *cv;
+    const TQ *rk, *rv;
+    TQ* o;
+    RowStrides qs, cks, cvs, rks, rvs, os;
+};
 
 // Maximum / sum of a value over lanes l and l ^ 32 (a VALU lane swap, so it
 // does not queue behind LDS reads)
@@ -351,12 +369,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int NW, int D, class E, bool SHARED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
-              const uint16_t* __restrict__ cv, const int32_t* __restrict__ topk,
-              const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
-              uint16_t* __restrict__ o, float* __restrict__ part, int64_t Tq, int64_t Nc,
-              int64_t m, int64_t W, int k, int64_t q_pos0, float scale_log2, int64_t raw_pos0,
-              int64_t raw_len, int splits) {
+k_attend_bf16(AttnArgs<uint16_t, uint16_t> A, const int32_t* __restrict__ topk,
+              float* __restrict__ part, int64_t Tq, int64_t Nc, int64_t m, int64_t W, int k,
+              int64_t q_pos0, float scale_log2, int64_t raw_pos0, int64_t raw_len, int splits) {
     using G = TileGeom<D>;
     constexpr int NT = NW * 64;
     constexpr int H = NW * E::HPW;
@@ -419,19 +434,20 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
     const int tau0 = split * tps;
     const int tau1 = min(ntile, tau0 + tps);
 
-    const char* ckb = reinterpret_cast<const char*>(ck + b * Nc * D);
-    const char* cvb = reinterpret_cast<const char*>(cv + b * Nc * D);
-    const char* rkb = reinterpret_cast<const char*>(rk + b * raw_len * D);
-    const char* rvb = reinterpret_cast<const char*>(rv + b * raw_len * D);
+    const KvRows kv{reinterpret_cast<const char*>(A.ck + b * A.cks.ss),
+                    reinterpret_cast<const char*>(A.cv + b * A.cvs.ss),
+                    reinterpret_cast<const char*>(A.rk + b * A.rks.ss),
+                    reinterpret_cast<const char*>(A.rv + b * A.rvs.ss),
+                    (uint32_t)(A.cks.rs * 2), (uint32_t)(A.cvs.rs * 2), (uint32_t)(A.rks.rs * 2),
+                    (uint32_t)(A.rvs.rs * 2)};
 
     E eng;
-    eng.init(q + ((b * Tq + i) * H + wave * E::HPW) * D);
+    eng.init(A.q + b * A.qs.ss + i * A.qs.rs + wave * E::HPW * D);
 
     auto issue = [&](int tau, uint8_t* sk, uint8_t* sv) {
         if (tau < tau1)
-            issue_tile<NW, D, SHARED>(wave, tau, ct, nval, nwin, raw_first, sparse, ssel, ckb, cvb,
-                                      rkb, rvb,
-                              (CSA_LDS uint8_t*)sk, (CSA_LDS uint8_t*)sv);
+            issue_tile<NW, D, SHARED>(wave, tau, ct, nval, nwin, raw_first, sparse, ssel, kv,
+                                      (CSA_LDS uint8_t*)sk, (CSA_LDS uint8_t*)sv);
     };
     // one tile: wait for its copies, barrier (the stage written next is then
     // free on every wave), issue the copies three tiles ahead, compute
@@ -460,7 +476,8 @@ k_attend_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ ck,
         step(tau + 3, sK3, sV3, sK2, sV2);
     }
     if (splits == 1) {
-        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, nullptr, scale_log2);
+        eng.store(A.o + b * A.os.ss + i * A.os.rs + wave * E::HPW * D, nullptr, nullptr,
+                  scale_log2);
     } else {
         const int64_t rec = ((b * Tq + i) * splits + split) * H + wave * E::HPW;
         const int64_t nrec = (int64_t)gridDim.x * gridDim.y * gridDim.z * H;
@@ -587,13 +604,10 @@ __device__ __forceinline__ void mx8_convert(const CSA_LDS uint8_t* stg, CSA_LDS 
 
 template <int NW, class E, bool SHARED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
-             const uint8_t* __restrict__ cv, const uint8_t* __restrict__ cks,
+k_attend_mx8(AttnArgs<uint16_t, uint8_t> A, const uint8_t* __restrict__ cks,
              const uint8_t* __restrict__ cvs, const int32_t* __restrict__ topk,
-             const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
-             uint16_t* __restrict__ o, float* __restrict__ part, int64_t Tq, int64_t Nc,
-             int64_t m, int64_t W, int k, int64_t q_pos0, float scale_log2, int64_t raw_pos0,
-             int64_t raw_len, int splits) {
+             float* __restrict__ part, int64_t Tq, int64_t Nc, int64_t m, int64_t W, int k,
+             int64_t q_pos0, float scale_log2, int64_t raw_pos0, int64_t raw_len, int splits) {
     constexpr int D = 128;
     using G = TileGeom<D>;
     using M = Mx8Geom;
@@ -654,16 +668,17 @@ k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
     const int tau0 = split * tps;
     const int tau1 = min(ntile, tau0 + tps);
 
-    const uint8_t* ckb = ck + b * Nc * D;
-    const uint8_t* cvb = cv + b * Nc * D;
+    const uint8_t* ckb = A.ck + b * Nc * D;
+    const uint8_t* cvb = A.cv + b * Nc * D;
     const uint8_t* ksb = cks + b * Nc * (D / 32);
     const uint8_t* vsb = cvs + b * Nc * (D / 32);
-    const char* rkb = reinterpret_cast<const char*>(rk + b * raw_len * D);
-    const char* rvb = reinterpret_cast<const char*>(rv + b * raw_len * D);
+    const KvRows kv{nullptr, nullptr, reinterpret_cast<const char*>(A.rk + b * A.rks.ss),
+                    reinterpret_cast<const char*>(A.rv + b * A.rvs.ss), 0u, 0u,
+                    (uint32_t)(A.rks.rs * 2), (uint32_t)(A.rvs.rs * 2)};
     const int percomp = mx8_comp_copies<NW, SHARED>(wave);
 
     E eng;
-    eng.init(q + ((b * Tq + i) * H + wave * E::HPW) * D);
+    eng.init(A.q + b * A.qs.ss + i * A.qs.rs + wave * E::HPW * D);
 
     // staging copies of compressed tile tau (nothing for other tiles)
     auto stage = [&](int tau, uint8_t* stg) {
@@ -678,9 +693,8 @@ k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
             mx8_convert<NW, SHARED>((const CSA_LDS uint8_t*)stg, (CSA_LDS uint8_t*)bk,
                                     (CSA_LDS uint8_t*)bv);
         else
-            issue_tile<NW, D, SHARED>(wave, tau, ct, nval, nwin, raw_first, false, ssel, nullptr,
-                                      nullptr, rkb, rvb, (CSA_LDS uint8_t*)bk,
-                                      (CSA_LDS uint8_t*)bv);
+            issue_tile<NW, D, SHARED>(wave, tau, ct, nval, nwin, raw_first, false, ssel, kv,
+                                      (CSA_LDS uint8_t*)bk, (CSA_LDS uint8_t*)bv);
     };
     // one step: wait, barrier (stage tau's bf16 tile complete everywhere; the
     // other bf16 buffer and staging slot of tau - 1 free), fill tile tau + 1,
@@ -722,7 +736,8 @@ k_attend_mx8(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ck,
         step(tau + 3, sS0, sS2, sK1, sV1, sK0, sV0);
     }
     if (splits == 1) {
-        eng.store(o + ((b * Tq + i) * H + wave * E::HPW) * D, nullptr, nullptr, scale_log2);
+        eng.store(A.o + b * A.os.ss + i * A.os.rs + wave * E::HPW * D, nullptr, nullptr,
+                  scale_log2);
     } else {
         const int64_t rec = ((b * Tq + i) * splits + split) * H + wave * E::HPW;
         const int64_t nrec = (int64_t)gridDim.x * gridDim.y * gridDim.z * H;
@@ -742,7 +757,7 @@ constexpr int CMB_MAXS = 64;
 template <typename TO>
 __global__ void __launch_bounds__(256)
 k_attend_combine(const uint16_t* __restrict__ po, const float* __restrict__ pml,
-                 TO* __restrict__ o, int64_t Tq, int H, int D, int splits) {
+                 TO* __restrict__ o, RowStrides os, int64_t Tq, int H, int D, int splits) {
     __shared__ float sw[8][CMB_MAXS];
     const int64_t i = blockIdx.x, b = blockIdx.y;
     const int per_head = D / 4;                     // 32 or 16: a power of two <= 32
@@ -800,7 +815,7 @@ k_attend_combine(const uint16_t* __restrict__ po, const float* __restrict__ pml,
             a[3] += bf16_bits_to_f32(v[u][1] >> 16) * w;
         }
     }
-    TO* op = o + ((b * Tq + i) * H + h) * (int64_t)D + d0;
+    TO* op = o + b * os.ss + i * os.rs + h * (int64_t)D + d0;
     if constexpr (sizeof(TO) == 2) {
         u32x2 w;
         w[0] = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
@@ -815,11 +830,9 @@ k_attend_combine(const uint16_t* __restrict__ po, const float* __restrict__ pml,
 // fp32 kernel: one wave per (query, head) at a time, keys in sequence, the
 // D dims spread over the lanes; fp32 arithmetic with accurate expf.
 __global__ void __launch_bounds__(256)
-k_attend_f32(const float* __restrict__ q, const float* __restrict__ ck,
-             const float* __restrict__ cv, const int32_t* __restrict__ topk,
-             const float* __restrict__ rk, const float* __restrict__ rv, float* __restrict__ o,
-             int64_t Tq, int H, int D, int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0,
-             float scale, int64_t raw_pos0, int64_t raw_len) {
+k_attend_f32(AttnArgs<float, float> A, const int32_t* __restrict__ topk, int64_t Tq, int H,
+             int D, int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0, float scale,
+             int64_t raw_pos0, int64_t raw_len) {
     const int64_t i = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
     const int64_t t = q_pos0 + i;
@@ -829,7 +842,7 @@ k_attend_f32(const float* __restrict__ q, const float* __restrict__ ck,
     const int32_t* sel = sparse ? topk + (b * Tq + i) * k : nullptr;
     constexpr int DPL = 4;                 // dims per lane (D <= 256)
     for (int h = wave; h < H; h += blockDim.x / 64) {
-        const float* qh = q + ((b * Tq + i) * H + h) * (int64_t)D;
+        const float* qh = A.q + b * A.qs.ss + i * A.qs.rs + h * (int64_t)D;
         float qv[DPL], acc[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
@@ -841,10 +854,10 @@ k_attend_f32(const float* __restrict__ q, const float* __restrict__ ck,
         for (int64_t s = 0; s < L.len; ++s) {
             int64_t row = list_row(L, s, sel, nc_t, raw_pos0);
             if (row == -1) continue;
-            const float* kr = row >= 0 ? ck + (b * Nc + row) * (int64_t)D
-                                       : rk + (b * raw_len + (-row - 2)) * (int64_t)D;
-            const float* vr = row >= 0 ? cv + (b * Nc + row) * (int64_t)D
-                                       : rv + (b * raw_len + (-row - 2)) * (int64_t)D;
+            const float* kr = row >= 0 ? A.ck + b * A.cks.ss + row * A.cks.rs
+                                       : A.rk + b * A.rks.ss + (-row - 2) * A.rks.rs;
+            const float* vr = row >= 0 ? A.cv + b * A.cvs.ss + row * A.cvs.rs
+                                       : A.rv + b * A.rvs.ss + (-row - 2) * A.rvs.rs;
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) {
@@ -864,7 +877,7 @@ k_attend_f32(const float* __restrict__ q, const float* __restrict__ ck,
             }
             mx = nm;
         }
-        float* oh = o + ((b * Tq + i) * H + h) * (int64_t)D;
+        float* oh = A.o + b * A.os.ss + i * A.os.rs + h * (int64_t)D;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
             const int d = lane + 64 * e;
@@ -894,45 +907,50 @@ AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int6
 // NW waves per block, E::HPW heads per wave
 template <int D, int NW, class E>
 static void launch_bf16(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, int64_t m,
-                        int64_t W, int k, int64_t q_pos0, float scale, const void* q,
-                        const void* ck, const void* cv, const int32_t* topk, const void* rk,
-                        const void* rv, int64_t raw_pos0, int64_t raw_len, void* o, void* ws,
+                        int64_t W, int k, int64_t q_pos0, float scale, const AttendIO& io,
+                        const int32_t* topk, int64_t raw_pos0, int64_t raw_len, void* ws,
                         hipStream_t st) {
     const float scale_log2 = scale * 1.4426950408889634f;
+    const AttnArgs<uint16_t, uint16_t> A{
+        (const uint16_t*)io.q,  (const uint16_t*)io.ck, (const uint16_t*)io.cv,
+        (const uint16_t*)io.rk, (const uint16_t*)io.rv, (uint16_t*)io.o,
+        io.qs, io.cks, io.cvs, io.rks, io.rvs, io.os};
     // the same rows passed as keys and values: copy them once
-    const bool shared = ck == cv && rk == rv;
+    const bool shared = io.ck == io.cv && io.rk == io.rv && io.cks.ss == io.cvs.ss &&
+                        io.cks.rs == io.cvs.rs && io.rks.ss == io.rvs.ss && io.rks.rs == io.rvs.rs;
     auto kern = shared ? k_attend_bf16<NW, D, E, true> : k_attend_bf16<NW, D, E, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64),
-                       0, st, (const uint16_t*)q, (const uint16_t*)ck, (const uint16_t*)cv, topk,
-                       (const uint16_t*)rk, (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq,
-                       Nc, m, W, k, q_pos0, scale_log2, raw_pos0, raw_len, p.splits);
+                       0, st, A, topk, (float*)ws, Tq, Nc, m, W, k, q_pos0, scale_log2, raw_pos0,
+                       raw_len, p.splits);
     if (p.splits > 1) {
         const int H = NW * E::HPW;
         const uint16_t* po = (const uint16_t*)ws;
         const float* pml = (const float*)(po + B * Tq * p.splits * H * D);
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,
                            dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
-                           st, po, pml, (uint16_t*)o, Tq, H, D, p.splits);
+                           st, po, pml, (uint16_t*)io.o, io.os, Tq, H, D, p.splits);
     }
 }
 
 hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int64_t H,
                          int64_t D, int64_t Nc, int64_t m, int64_t W, int64_t k,
-                         int64_t q_pos0, float scale, const void* q, const void* ck,
-                         const void* cv, const int32_t* topk, const void* rk, const void* rv,
-                         int64_t raw_pos0, int64_t raw_len, void* o, void* ws, hipStream_t st) {
+                         int64_t q_pos0, float scale, const AttendIO& io, const int32_t* topk,
+                         int64_t raw_pos0, int64_t raw_len, void* ws, hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
     if (dt == 0) {
-        hipLaunchKernelGGL(k_attend_f32, dim3((unsigned)Tq, (unsigned)B), dim3(256), 0, st,
-                           (const float*)q, (const float*)ck, (const float*)cv, topk,
-                           (const float*)rk, (const float*)rv, (float*)o, Tq, (int)H, (int)D,
-                           Nc, m, W, (int)k, q_pos0, scale, raw_pos0, raw_len);
+        const AttnArgs<float, float> A{(const float*)io.q,  (const float*)io.ck,
+                                       (const float*)io.cv, (const float*)io.rk,
+                                       (const float*)io.rv, (float*)io.o,
+                                       io.qs, io.cks, io.cvs, io.rks, io.rvs, io.os};
+        hipLaunchKernelGGL(k_attend_f32, dim3((unsigned)Tq, (unsigned)B), dim3(256), 0, st, A,
+                           topk, Tq, (int)H, (int)D, Nc, m, W, (int)k, q_pos0, scale, raw_pos0,
+                           raw_len);
         return hipGetLastError();
     }
     const int nw = (int)(H / 32);
-#define CSA_ATT_CASE(DD, NN, EE)                                                              \
-    launch_bf16<DD, NN, EE<DD>>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, topk, rk, \
-                                rv, raw_pos0, raw_len, o, ws, st)
+#define CSA_ATT_CASE(DD, NN, EE)                                                               \
+    launch_bf16<DD, NN, EE<DD>>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, io, topk, raw_pos0, \
+                                raw_len, ws, st)
     // 32 heads per wave.  (A 16-head engine on V_MFMA_F32_16X16X32_BF16 fits
     // four waves per SIMD but doubles the LDS operand reads per flop, and
     // measured slower.)
@@ -959,38 +977,40 @@ hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int
 
 template <int NW>
 static void launch_mx8_nw(const AttendPlan& p, int64_t B, int64_t Tq, int64_t Nc, int64_t m,
-                          int64_t W, int k, int64_t q_pos0, float scale, const void* q,
-                          const uint8_t* ck, const uint8_t* cv, const uint8_t* cks,
-                          const uint8_t* cvs, const int32_t* topk, const void* rk, const void* rv,
-                          int64_t raw_pos0, int64_t raw_len, void* o, void* ws, hipStream_t st) {
+                          int64_t W, int k, int64_t q_pos0, float scale, const AttendIO& io,
+                          const uint8_t* cks, const uint8_t* cvs, const int32_t* topk,
+                          int64_t raw_pos0, int64_t raw_len, void* ws, hipStream_t st) {
     constexpr int D = 128;
     const float scale_log2 = scale * 1.4426950408889634f;
-    const bool shared = ck == cv && cks == cvs && rk == rv;
+    const AttnArgs<uint16_t, uint8_t> A{
+        (const uint16_t*)io.q,  (const uint8_t*)io.ck,  (const uint8_t*)io.cv,
+        (const uint16_t*)io.rk, (const uint16_t*)io.rv, (uint16_t*)io.o,
+        io.qs, io.cks, io.cvs, io.rks, io.rvs, io.os};
+    const bool shared = io.ck == io.cv && cks == cvs && io.rk == io.rv &&
+                        io.rks.ss == io.rvs.ss && io.rks.rs == io.rvs.rs;
     auto kern = shared ? k_attend_mx8<NW, Heads32<D>, true> : k_attend_mx8<NW, Heads32<D>, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)Tq, (unsigned)p.splits, (unsigned)B), dim3(NW * 64),
-                       0, st, (const uint16_t*)q, ck, cv, cks, cvs, topk, (const uint16_t*)rk,
-                       (const uint16_t*)rv, (uint16_t*)o, (float*)ws, Tq, Nc, m, W, k, q_pos0,
-                       scale_log2, raw_pos0, raw_len, p.splits);
+                       0, st, A, cks, cvs, topk, (float*)ws, Tq, Nc, m, W, k, q_pos0, scale_log2,
+                       raw_pos0, raw_len, p.splits);
     if (p.splits > 1) {
         const int H = NW * 32;
         const uint16_t* po = (const uint16_t*)ws;
         const float* pml = (const float*)(po + B * Tq * p.splits * H * D);
         hipLaunchKernelGGL(k_attend_combine<uint16_t>,
                            dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0,
-                           st, po, pml, (uint16_t*)o, Tq, H, D, p.splits);
+                           st, po, pml, (uint16_t*)io.o, io.os, Tq, H, D, p.splits);
     }
 }
 
 hipError_t launch_attend_mx8(const AttendPlan& p, int64_t B, int64_t Tq, int64_t H, int64_t Nc,
                              int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
-                             const void* q, const uint8_t* ck, const uint8_t* cv,
-                             const uint8_t* cks, const uint8_t* cvs, const int32_t* topk,
-                             const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
-                             void* o, void* ws, hipStream_t st) {
+                             const AttendIO& io, const uint8_t* cks, const uint8_t* cvs,
+                             const int32_t* topk, int64_t raw_pos0, int64_t raw_len, void* ws,
+                             hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
 #define CSA_MX8_CASE(NN)                                                                        \
-    launch_mx8_nw<NN>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, q, ck, cv, cks, cvs, topk, rk, \
-                      rv, raw_pos0, raw_len, o, ws, st)
+    launch_mx8_nw<NN>(p, B, Tq, Nc, m, W, (int)k, q_pos0, scale, io, cks, cvs, topk, raw_pos0, \
+                      raw_len, ws, st)
     switch (H / 32) {
         case 1: CSA_MX8_CASE(1); break;
         case 2: CSA_MX8_CASE(2); break;

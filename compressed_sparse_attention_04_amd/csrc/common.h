@@ -15,6 +15,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 
+// Element strides of a [B][rows][...] tensor whose rows are contiguous:
+// element e of row r of sequence b sits at b * ss + r * rs + e.
+struct RowStrides {
+    int64_t ss, rs;
+};
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
 }

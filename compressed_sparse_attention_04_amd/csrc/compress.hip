@@ -46,23 +46,32 @@ struct OnlineSoftmax8 {
     }
 };
 
+// gate logits of one row (grow: the row's first element) for 8 channels
+// from c8: the row's single logit (gc = 1) or 8 per-channel logits
 template <typename T>
-__device__ __forceinline__ void load_gate8(const T* gate, int64_t row, int C, int gc, int c8,
-                                           float (&z)[8]) {
+__device__ __forceinline__ void load_gate8(const T* grow, int gc, int c8, float (&z)[8]) {
     if (gc == 1) {
-        float v = Elem<T>::load1(gate + row);
+        float v = Elem<T>::load1(grow);
 #pragma unroll
         for (int c = 0; c < 8; ++c) z[c] = v;
     } else {
-        Elem<T>::load8(gate + row * (int64_t)C + c8 * 8, z);
+        Elem<T>::load8(grow + c8 * 8, z);
     }
 }
+
+// Strided inputs and output of one pooling call
+template <typename T>
+struct PoolIO {
+    const T* x;
+    const T* gate;
+    T* out;
+    RowStrides xs, gs, os;
+};
 
 // Small m: one thread per (output row, 8-channel group).
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_compress_small(const T* __restrict__ x, const T* __restrict__ gate, T* __restrict__ out,
-                 int64_t B, int64_t T_, int C, int m, int gc, int64_t nout) {
+k_compress_small(PoolIO<T> io, int64_t B, int64_t T_, int C, int m, int gc, int64_t nout) {
     const int groups = C / 8;
     int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     int64_t total = B * nout * groups;
@@ -72,25 +81,25 @@ k_compress_small(const T* __restrict__ x, const T* __restrict__ gate, T* __restr
     int64_t b = bj / nout, j = bj % nout;
     OnlineSoftmax8 s;
     s.init();
-    int64_t row0 = b * T_ + j * m;
+    const T* xr = io.x + b * io.xs.ss + j * m * io.xs.rs + c8 * 8;
+    const T* gr = io.gate + b * io.gs.ss + j * m * io.gs.rs;
     for (int i = 0; i < m; ++i) {
         float xv[8], z[8];
-        Elem<T>::load8(x + (row0 + i) * (int64_t)C + c8 * 8, xv);
-        load_gate8(gate, row0 + i, C, gc, c8, z);
+        Elem<T>::load8(xr + i * io.xs.rs, xv);
+        load_gate8(gr + i * io.gs.rs, gc, c8, z);
         s.add(z, xv);
     }
     float o[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = s.acc[c] / s.den[c];
-    Elem<T>::store8(out + bj * (int64_t)C + c8 * 8, o);
+    Elem<T>::store8(io.out + b * io.os.ss + j * io.os.rs + c8 * 8, o);
 }
 
 // Large m: one 256-thread block per output row; the m rows are split over
 // R = 256 / (C/8) row groups whose partial softmax states merge in LDS.
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_compress_large(const T* __restrict__ x, const T* __restrict__ gate, T* __restrict__ out,
-                 int64_t B, int64_t T_, int C, int m, int gc, int64_t nout) {
+k_compress_large(PoolIO<T> io, int64_t B, int64_t T_, int C, int m, int gc, int64_t nout) {
     __shared__ float smx[256 * 8], sden[256 * 8], sacc[256 * 8];
     const int groups = C / 8;
     const int R = 256 / groups;
@@ -100,12 +109,13 @@ k_compress_large(const T* __restrict__ x, const T* __restrict__ gate, T* __restr
     int64_t b = bj / nout, j = bj % nout;
     OnlineSoftmax8 s;
     s.init();
-    int64_t row0 = b * T_ + j * m;
+    const T* xr = io.x + b * io.xs.ss + j * m * io.xs.rs + c8 * 8;
+    const T* gr = io.gate + b * io.gs.ss + j * m * io.gs.rs;
     if (rg < R) {
         for (int i = rg; i < m; i += R) {
             float xv[8], z[8];
-            Elem<T>::load8(x + (row0 + i) * (int64_t)C + c8 * 8, xv);
-            load_gate8(gate, row0 + i, C, gc, c8, z);
+            Elem<T>::load8(xr + i * io.xs.rs, xv);
+            load_gate8(gr + i * io.gs.rs, gc, c8, z);
             s.add(z, xv);
         }
     }
@@ -124,7 +134,7 @@ k_compress_large(const T* __restrict__ x, const T* __restrict__ gate, T* __restr
         float ov[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) ov[c] = s.acc[c] / s.den[c];
-        Elem<T>::store8(out + bj * (int64_t)C + c8 * 8, ov);
+        Elem<T>::store8(io.out + b * io.os.ss + j * io.os.rs + c8 * 8, ov);
     }
 }
 
@@ -172,10 +182,10 @@ __device__ __forceinline__ void block_row(const AppendSide<T>& sd, const AppendA
                                           float (&z)[8]) {
     if (i == a.m - 1) {
         Elem<T>::load8(sd.x_new + b * a.C + c8 * 8, xv);
-        load_gate8(sd.g_new, b, a.C, a.gc, c8, z);
+        load_gate8(sd.g_new + b * a.gc, a.gc, c8, z);
     } else {
         Elem<T>::load8(sd.win + (b * a.wcap + a.row_blk + i) * a.C + c8 * 8, xv);
-        load_gate8(sd.gblk, b * a.m + i, a.C, a.gc, c8, z);
+        load_gate8(sd.gblk + (b * a.m + i) * a.gc, a.gc, c8, z);
     }
 }
 
@@ -318,26 +328,30 @@ hipError_t launch_append(int dt, int64_t B, int64_t C, int64_t m, int64_t W, int
 }
 
 template <typename T>
-static hipError_t launch_compress_t(const void* x, const void* gate, void* out, int64_t B,
-                                    int64_t T_, int C, int m, int gc, hipStream_t st) {
+static hipError_t launch_compress_t(const PoolIO<T>& io, int64_t B, int64_t T_, int C, int m,
+                                    int gc, hipStream_t st) {
     int64_t nout = T_ / m;
     if (B * nout == 0) return hipSuccess;
     if (m <= 16) {
         int64_t total = B * nout * (C / 8);
         int64_t blocks = (total + 255) / 256;
-        hipLaunchKernelGGL(k_compress_small<T>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           (const T*)x, (const T*)gate, (T*)out, B, T_, C, m, gc, nout);
+        hipLaunchKernelGGL(k_compress_small<T>, dim3((unsigned)blocks), dim3(256), 0, st, io, B,
+                           T_, C, m, gc, nout);
     } else {
-        hipLaunchKernelGGL(k_compress_large<T>, dim3((unsigned)(B * nout)), dim3(256), 0, st,
-                           (const T*)x, (const T*)gate, (T*)out, B, T_, C, m, gc, nout);
+        hipLaunchKernelGGL(k_compress_large<T>, dim3((unsigned)(B * nout)), dim3(256), 0, st, io,
+                           B, T_, C, m, gc, nout);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_compress(int dt, const void* x, const void* gate, void* out, int64_t B,
-                           int64_t T_, int C, int m, int gc, hipStream_t st) {
-    if (dt == 0) return launch_compress_t<float>(x, gate, out, B, T_, C, m, gc, st);
-    return launch_compress_t<uint16_t>(x, gate, out, B, T_, C, m, gc, st);
+hipError_t launch_compress(int dt, const void* x, RowStrides xs, const void* gate, RowStrides gs,
+                           void* out, RowStrides os, int64_t B, int64_t T_, int C, int m, int gc,
+                           hipStream_t st) {
+    if (dt == 0)
+        return launch_compress_t<float>({(const float*)x, (const float*)gate, (float*)out, xs, gs,
+                                         os}, B, T_, C, m, gc, st);
+    return launch_compress_t<uint16_t>({(const uint16_t*)x, (const uint16_t*)gate, (uint16_t*)out,
+                                        xs, gs, os}, B, T_, C, m, gc, st);
 }
 
 }  // namespace csa

@@ -78,14 +78,14 @@ __host__ __device__ __forceinline__ u32x2* ws_meta(void* ws, int64_t rows, const
 // (qi, h) = (row / HI, row % HI), 32-value block kb of its dI values
 // (dI = 32 leaves block 1 zero); query qi of the tile is row q0 + qi.
 template <typename T, int HI>
-__device__ __forceinline__ void encode_q(const T* q_idx, int64_t b, int64_t Tq, int64_t q0,
+__device__ __forceinline__ void encode_q(const T* q_idx, RowStrides qs, int64_t b, int64_t q0,
                                          int qv, int dI, i32x8& aop, int& sa) {
     const int lane = threadIdx.x % WAVE, row = lane & 31, kb = lane >> 5;
     aop = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     sa = 127;
     const int qi = row / HI, h = row % HI;
     if (qi < qv && kb * 32 < dI) {
-        const T* src = q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + kb * 32);
+        const T* src = q_idx + b * qs.ss + (q0 + qi) * qs.rs + h * dI + kb * 32;
         float v[32];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -103,7 +103,7 @@ __device__ __forceinline__ void encode_q(const T* q_idx, int64_t b, int64_t Tq, 
 
 template <typename T, int HI>
 __global__ void __launch_bounds__(DS_NT)
-k_dscan(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+k_dscan(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ kc,
         const uint8_t* __restrict__ ks, void* ws, int64_t Tq, int dI, int64_t Nc, int64_t m,
         int64_t W, int64_t q_pos0, DecodeGeom g) {
     extern __shared__ uint32_t smem[];               // keys [Tq][ch] | hist [Tq][SEL_NB]
@@ -135,7 +135,7 @@ k_dscan(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
 
     i32x8 aop;
     int sa;
-    encode_q<T, HI>(q_idx, b, Tq, 0, qv, dI, aop, sa);
+    encode_q<T, HI>(q_idx, qs, b, 0, qv, dI, aop, sa);
     // lane slot u of a tile holds the scores of query qslot[u]; slots from
     // nlive on hold no query of this launch
     const int nlive = live_slots<HI>(qv);
@@ -345,7 +345,7 @@ __device__ __forceinline__ void exact_select(Scan&& scan, int nc, int need, int3
 
 template <typename T, int HI, int EPT>
 __global__ void __launch_bounds__(DM_NT)
-k_dmerge(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ kc,
          const uint8_t* __restrict__ ks, void* ws, int32_t* __restrict__ topk, int64_t Tq,
          int dI, int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0, DecodeGeom g) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -476,7 +476,7 @@ k_dmerge(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     // exact path: rescore every candidate of the row, pass by pass
     i32x8 aop;
     int sa;
-    encode_q<T, HI>(q_idx, b, Tq, q, 1, dI, aop, sa);
+    encode_q<T, HI>(q_idx, qs, b, q, 1, dI, aop, sa);
     const int lane = tid % WAVE, row = lane & 31, kb = lane >> 5;
     const int kbytes = dI / 2, kscales = dI / 32;
     const TileSrc ts{kc + b * Nc * kbytes, ks + b * Nc * kscales, kbytes, kscales, nc, row, kb};
@@ -504,12 +504,13 @@ size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap, int k) {
 
 template <typename T, int HI>
 static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W,
-                            int k, int64_t q_pos0, const void* q_idx, const uint8_t* kc,
-                            const uint8_t* ks, int32_t* topk, void* ws, const DecodeGeom& g,
-                            hipStream_t st) {
+                            int k, int64_t q_pos0, const void* q_idx, RowStrides qs,
+                            const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
+                            const DecodeGeom& g, hipStream_t st) {
     const size_t lds_scan = (size_t)Tq * (g.ch + SEL_NB) * sizeof(uint32_t);
     hipLaunchKernelGGL((k_dscan<T, HI>), dim3((unsigned)g.nchunks, (unsigned)B), dim3(DS_NT),
-                       lds_scan, st, (const T*)q_idx, kc, ks, ws, Tq, dI, Nc, m, W, q_pos0, g);
+                       lds_scan, st, (const T*)q_idx, qs, kc, ks, ws, Tq, dI, Nc, m, W, q_pos0,
+                       g);
     const size_t lds = sizeof(DmSmem);
 #define CSA_DM_CASE(E)                                                                       \
     do {                                                                                     \
@@ -517,7 +518,7 @@ static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, \
                             (int)lds);                                                       \
         hipLaunchKernelGGL(kern, dim3((unsigned)Tq, (unsigned)B), dim3(DM_NT), lds, st,      \
-                           (const T*)q_idx, kc, ks, ws, topk, Tq, dI, Nc, m, W, k, q_pos0,   \
+                           (const T*)q_idx, qs, kc, ks, ws, topk, Tq, dI, Nc, m, W, k, q_pos0, \
                            g);                                                               \
     } while (0)
     if (g.ept == 8) CSA_DM_CASE(8);
@@ -528,13 +529,13 @@ static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m
 
 hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
                                int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
-                               const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
-                               hipStream_t st) {
+                               RowStrides qs, const uint8_t* kc, const uint8_t* ks,
+                               int32_t* topk, void* ws, hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
     const int64_t ncand = n_candidates(q_pos0 + Tq - 1, m, W);
     const DecodeGeom g = decode_geom(Tq, ncand, k);
 #define CSA_DS_CASE(TT, HH) \
-    launch_decode_t<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk, ws, g, st)
+    launch_decode_t<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, qs, kc, ks, topk, ws, g, st)
     if (dt == 0) {
         if (HI == 1) CSA_DS_CASE(float, 1);
         else if (HI == 2) CSA_DS_CASE(float, 2);

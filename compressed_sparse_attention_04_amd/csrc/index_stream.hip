@@ -62,7 +62,7 @@ struct StreamSmem {
 
 template <typename T, int HI>
 __global__ void __launch_bounds__(ST_NT)
-k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ kc,
                const uint8_t* __restrict__ ks, int32_t* __restrict__ topk, int64_t Tq, int dI,
                int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -106,7 +106,8 @@ k_index_stream(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
         const int qi = brow / HI, h = brow % HI;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (qi < qv && bkb * 32 < dI)
-            Elem<T>::load4(q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + bkb * 32 + part * 4), v);
+            Elem<T>::load4(q_idx + b * qs.ss + (q0 + qi) * qs.rs + h * dI + bkb * 32 + part * 4,
+                           v);
         uint32_t amax = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7fffffffu);
@@ -440,24 +441,24 @@ int stream_max_candidates() { return ST_MAXW * 32; }
 template <typename T, int HI>
 static hipError_t launch_stream_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m,
                                   int64_t W, int k, int64_t q_pos0, const void* q_idx,
-                                  const uint8_t* kc, const uint8_t* ks, int32_t* topk,
-                                  hipStream_t st) {
+                                  RowStrides qs, const uint8_t* kc, const uint8_t* ks,
+                                  int32_t* topk, hipStream_t st) {
     auto kern = k_index_stream<T, HI>;
     const size_t lds = sizeof(StreamSmem);
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     dim3 grid((unsigned)((Tq + ST_QT - 1) / ST_QT), (unsigned)B);
-    hipLaunchKernelGGL(kern, grid, dim3(ST_NT), lds, st, (const T*)q_idx, kc, ks, topk, Tq, dI,
-                       Nc, m, W, k, q_pos0);
+    hipLaunchKernelGGL(kern, grid, dim3(ST_NT), lds, st, (const T*)q_idx, qs, kc, ks, topk, Tq,
+                       dI, Nc, m, W, k, q_pos0);
     return hipGetLastError();
 }
 
 hipError_t launch_index_stream(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
                                int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
-                               const uint8_t* kc, const uint8_t* ks, int32_t* topk,
-                               hipStream_t st) {
+                               RowStrides qs, const uint8_t* kc, const uint8_t* ks,
+                               int32_t* topk, hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
 #define CSA_ST_CASE(TT, HH) \
-    return launch_stream_t<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk, st)
+    return launch_stream_t<TT, HH>(B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, qs, kc, ks, topk, st)
     if (dt == 0) {
         if (HI == 1) CSA_ST_CASE(float, 1);
         if (HI == 2) CSA_ST_CASE(float, 2);

@@ -38,7 +38,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 template <typename T, int HI>
 __global__ void __launch_bounds__(IDX_NT)
-k_index_chunk(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
+k_index_chunk(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ kc,
               const uint8_t* __restrict__ ks, int32_t* __restrict__ topk,
               u32x2* __restrict__ part, int64_t Tq, int dI, int64_t Nc, int64_t m, int64_t W,
               int k, int64_t q_pos0, int ch, int64_t n_chunks) {
@@ -70,7 +70,7 @@ k_index_chunk(const T* __restrict__ q_idx, const uint8_t* __restrict__ kc,
     {
         const int qi = row / HI, h = row % HI;
         if (qi < qv && kb * 32 < dI) {
-            const T* src = q_idx + (((b * Tq + q0 + qi) * HI + h) * dI + kb * 32);
+            const T* src = q_idx + b * qs.ss + (q0 + qi) * qs.rs + h * dI + kb * 32;
             float v[32];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -203,12 +203,12 @@ int decode_max_rows();
 size_t decode_ws_bytes(int64_t B, int64_t Tq, int64_t ncap, int k);
 hipError_t launch_index_stream(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
                                int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
-                               const uint8_t* kc, const uint8_t* ks, int32_t* topk,
-                               hipStream_t st);
+                               RowStrides qs, const uint8_t* kc, const uint8_t* ks,
+                               int32_t* topk, hipStream_t st);
 hipError_t launch_index_decode(int dt, int64_t B, int64_t Tq, int HI, int dI, int64_t Nc,
                                int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
-                               const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
-                               hipStream_t st);
+                               RowStrides qs, const uint8_t* kc, const uint8_t* ks,
+                               int32_t* topk, void* ws, hipStream_t st);
 
 IndexPlan plan_index(int64_t B, int64_t Tq, int HI, int dI, int64_t Nc, int64_t m, int64_t W,
                      int k, int64_t q_pos0) {
@@ -237,15 +237,15 @@ int64_t index_merge_max() { return MERGE_MAX; }
 template <typename T, int HI>
 static hipError_t launch_chunk(const IndexPlan& p, int64_t B, int64_t Tq, int dI, int64_t Nc,
                                int64_t m, int64_t W, int k, int64_t q_pos0, const void* q_idx,
-                               const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
-                               hipStream_t st) {
+                               RowStrides qs, const uint8_t* kc, const uint8_t* ks,
+                               int32_t* topk, void* ws, hipStream_t st) {
     const int qv = (int)min((int64_t)p.qt, Tq);
     size_t lds = (size_t)qv * p.ch * sizeof(uint32_t);
     auto kern = k_index_chunk<T, HI>;
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)(SCORE_WORDS * sizeof(uint32_t)));
     dim3 grid((unsigned)p.n_chunks, (unsigned)p.n_qtiles, (unsigned)B);
-    hipLaunchKernelGGL(kern, grid, dim3(IDX_NT), lds, st, (const T*)q_idx, kc, ks, topk,
+    hipLaunchKernelGGL(kern, grid, dim3(IDX_NT), lds, st, (const T*)q_idx, qs, kc, ks, topk,
                        (u32x2*)ws, Tq, dI, Nc, m, W, k, q_pos0, p.ch, p.n_chunks);
     return hipGetLastError();
 }
@@ -259,18 +259,18 @@ static void launch_merge(const IndexPlan& p, int64_t B, int64_t Tq, int k, int64
 
 hipError_t launch_index_topk(int dt, const IndexPlan& p, int64_t B, int64_t Tq, int HI, int dI,
                              int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0,
-                             const void* q_idx, const uint8_t* kc, const uint8_t* ks,
-                             int32_t* topk, void* ws, hipStream_t st) {
+                             const void* q_idx, RowStrides qs, const uint8_t* kc,
+                             const uint8_t* ks, int32_t* topk, void* ws, hipStream_t st) {
     if (B == 0 || Tq == 0) return hipSuccess;
     if (p.path == IDX_STREAM)
-        return launch_index_stream(dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk,
-                                   st);
+        return launch_index_stream(dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, qs, kc, ks,
+                                   topk, st);
     if (p.path == IDX_DECODE)
-        return launch_index_decode(dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk,
-                                   ws, st);
+        return launch_index_decode(dt, B, Tq, HI, dI, Nc, m, W, k, q_pos0, q_idx, qs, kc, ks,
+                                   topk, ws, st);
     hipError_t e;
 #define CSA_IDX_CASE(TT, HH)                                                                  \
-    e = launch_chunk<TT, HH>(p, B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, kc, ks, topk, ws, st)
+    e = launch_chunk<TT, HH>(p, B, Tq, dI, Nc, m, W, k, q_pos0, q_idx, qs, kc, ks, topk, ws, st)
     if (dt == 0) {
         if (HI == 1) CSA_IDX_CASE(float, 1);
         else if (HI == 2) CSA_IDX_CASE(float, 2);

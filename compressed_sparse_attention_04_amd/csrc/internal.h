@@ -5,11 +5,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace csa {
 
 // dt: 0 = fp32, 1 = bf16 (same values as csa_dtype)
-hipError_t launch_compress(int dt, const void* x, const void* gate, void* out, int64_t B,
-                           int64_t T, int C, int m, int gc, hipStream_t st);
+// x [B][T][C] and gate [B][T][gc] rows, out [B][T/m][C] rows, at their strides
+hipError_t launch_compress(int dt, const void* x, RowStrides xs, const void* gate, RowStrides gs,
+                           void* out, RowStrides os, int64_t B, int64_t T, int C, int m, int gc,
+                           hipStream_t st);
 
 // one decode step of cache upkeep (see hca_append); *new_win_pos0 gets the
 // window buffer's first position after the call
@@ -19,8 +23,9 @@ hipError_t launch_append(int dt, int64_t B, int64_t C, int64_t m, int64_t W, int
                          const void* gv_new, void* rk, void* rv, void* gk_blk, void* gv_blk,
                          void* ck, void* cv, int64_t* new_win_pos0, hipStream_t st);
 
-hipError_t launch_quant_mxfp4(int dt, const void* x, uint8_t* codes, uint8_t* scales,
-                              int64_t rows, int d, hipStream_t st);
+// x rows at x_rs elements apart; codes and scales dense
+hipError_t launch_quant_mxfp4(int dt, const void* x, int64_t x_rs, uint8_t* codes,
+                              uint8_t* scales, int64_t rows, int d, hipStream_t st);
 
 // Indexer paths: STREAM (one block per 8 query rows streams all their
 // candidates), DECODE (<= 8 rows over a long context: chunked scoring to
@@ -38,31 +43,40 @@ struct IndexPlan {
 };
 IndexPlan plan_index(int64_t B, int64_t Tq, int HI, int dI, int64_t Nc, int64_t m, int64_t W,
                      int k, int64_t q_pos0);
+// q_idx rows (query tokens of [HI][dI]) at the strides qs; keys dense
 hipError_t launch_index_topk(int dt, const IndexPlan& p, int64_t B, int64_t Tq, int HI, int dI,
                              int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0,
-                             const void* q_idx, const uint8_t* k_codes, const uint8_t* k_scales,
-                             int32_t* topk, void* ws, hipStream_t st);
+                             const void* q_idx, RowStrides qs, const uint8_t* k_codes,
+                             const uint8_t* k_scales, int32_t* topk, void* ws, hipStream_t st);
 
 struct AttendPlan {
     int splits;        // key-list splits per query (1 = no combine pass)
     size_t ws_bytes;   // split partials
 };
-// topk == nullptr selects every candidate (HCA)
 AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t max_keys);
+
+// Tensors of one attention call: pointers and element strides (Q and O rows
+// are query tokens holding [H][D] contiguously; K and V rows are compressed
+// entries or raw tokens of D contiguous elements).
+struct AttendIO {
+    const void *q, *ck, *cv, *rk, *rv;
+    void* o;
+    RowStrides qs, cks, cvs, rks, rvs, os;
+};
+// topk == nullptr selects every candidate (HCA)
 hipError_t launch_attend(int dt, const AttendPlan& p, int64_t B, int64_t Tq, int64_t H,
                          int64_t D, int64_t Nc, int64_t m, int64_t W, int64_t k,
-                         int64_t q_pos0, float scale, const void* q, const void* ck,
-                         const void* cv, const int32_t* topk, const void* rk, const void* rv,
-                         int64_t raw_pos0, int64_t raw_len, void* o, void* ws, hipStream_t st);
+                         int64_t q_pos0, float scale, const AttendIO& io, const int32_t* topk,
+                         int64_t raw_pos0, int64_t raw_len, void* ws, hipStream_t st);
 
 // bf16 queries and window rows, compressed K/V rows as MXFP8 (E4M3 codes
-// [Nc][128] and E8M0 scales [Nc][4]); D = 128, the plan of the bf16 kernel
+// [Nc][128] and E8M0 scales [Nc][4], dense; io.ck / io.cv are the codes);
+// D = 128, the plan of the bf16 kernel
 hipError_t launch_attend_mx8(const AttendPlan& p, int64_t B, int64_t Tq, int64_t H, int64_t Nc,
                              int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
-                             const void* q, const uint8_t* ck, const uint8_t* cv,
-                             const uint8_t* cks, const uint8_t* cvs, const int32_t* topk,
-                             const void* rk, const void* rv, int64_t raw_pos0, int64_t raw_len,
-                             void* o, void* ws, hipStream_t st);
+                             const AttendIO& io, const uint8_t* cks, const uint8_t* cvs,
+                             const int32_t* topk, int64_t raw_pos0, int64_t raw_len, void* ws,
+                             hipStream_t st);
 
 hipError_t launch_quant_mxfp8(int dt, const void* x, uint8_t* codes, uint8_t* scales,
                               int64_t rows, int d, hipStream_t st);

@@ -24,7 +24,14 @@
  *   - Every pointer argument is device memory owned by the caller; the
  *     library never allocates, frees, synchronises, or keeps a pointer after
  *     the call returns.  Work is enqueued on `stream` (0 = null stream).
- *   - All tensors are dense, row-major, with the innermost index last.
+ *   - Tensors are row-major with the innermost index last.  The entry points
+ *     of the path's core steps (hca_compress, csa_quantize_mxfp4,
+ *     csa_index_topk, csa_attend, hca_attend) take their floating inputs
+ *     and outputs as strided views (csa_in / csa_out): a tensor of B
+ *     sequences of rows, each row contiguous, with element strides between
+ *     sequences and between rows, so a slice of a larger buffer (a window
+ *     of raw rows, a range of query rows) is passed without a copy.  Every
+ *     other tensor is dense.
  *   - Floating tensors are fp32 or bf16 as given by `dt` (one dtype per call);
  *     arithmetic is fp32 inside the kernels.
  *   - Positions: a sequence's tokens are at positions 0,1,2,...  Query row i
@@ -43,6 +50,10 @@
  *     shape the library has no kernel for), writes nothing, and sets a
  *     thread-local message read by csa_last_error().  A launch error
  *     returns CSA_EDEVICE.  Base pointers must be 16-byte aligned.
+ *   - Views: strides are >= 0 and in elements; consecutive rows do not
+ *     overlap (row_stride >= the row length); base and strides are
+ *     16-byte multiples (a per-token gate of one logit per row excepted);
+ *     an output's sequences do not overlap.  A failed check is CSA_EINVAL.
  */
 #ifndef CSA_H
 #define CSA_H
@@ -55,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -65,6 +76,18 @@ typedef enum csa_status {
     CSA_EUNSUPPORTED = 2,
     CSA_EDEVICE = 3
 } csa_status;
+
+/* Strided views: element (b, r, e) of a view of B sequences of rows, each
+ * row of contiguous elements, is at p + b * seq_stride + r * row_stride + e
+ * (elements of the tensor's dtype). */
+typedef struct csa_in {
+    const void *p;
+    int64_t seq_stride, row_stride;
+} csa_in;
+typedef struct csa_out {
+    void *p;
+    int64_t seq_stride, row_stride;
+} csa_out;
 
 /* Version of this ABI (CSA_ABI_VERSION of the build). */
 int csa_abi_version(void);
@@ -84,14 +107,14 @@ const char *csa_last_error(void);
  * for j < T/m (a trailing partial block is not emitted), with the softmax
  * over the block's m logits and g(c) = c if gate_channels == C, 0 if
  * gate_channels == 1 (one logit per token).
- *   x     [B, T, C]            dt
- *   gate  [B, T, gate_channels] dt
- *   out   [B, T/m, C]          dt (rounded to nearest even for bf16)
+ *   x     view of B x T rows of C               dt
+ *   gate  view of B x T rows of gate_channels   dt
+ *   out   view of B x T/m rows of C             dt (rounded to nearest even
+ *         for bf16)
  * Requires B >= 1, T >= 0, C % 8 == 0 and C <= 1024, m >= 1.
  */
-csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m,
-                        const void *x, const void *gate, int64_t gate_channels,
-                        void *out, hipStream_t stream);
+csa_status hca_compress(csa_dtype dt, int64_t B, int64_t T, int64_t C, int64_t m, csa_in x,
+                        csa_in gate, int64_t gate_channels, csa_out out, hipStream_t stream);
 
 /*
  * hca_append -- one decode step of cache upkeep (jiwasawa.github.io post,
@@ -138,12 +161,12 @@ csa_status hca_append(csa_dtype dt, int64_t B, int64_t C, int64_t m, int64_t W, 
  * nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even code, larger
  * magnitudes saturate to 6), code = magnitude index | 8 if x's sign bit is
  * set.  Element 2i of a row is the low nibble of byte i.
- *   x       [rows, d]      dt, finite values
+ *   x       view of rows rows of d (x.seq_stride is not used)   dt, finite
  *   codes   [rows, d/2]    uint8
  *   scales  [rows, d/32]   uint8 (E8M0)
  * Requires d % 32 == 0.
  */
-csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, const void *x,
+csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, csa_in x,
                               uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
 /*
@@ -159,7 +182,7 @@ csa_status csa_quantize_mxfp4(csa_dtype dt, int64_t rows, int64_t d, const void 
  * significant bits, e.g. N(0,1) data).  The kept entries are the first
  * min(k, n_cand(t)) candidates under the order (score descending, index
  * ascending); -0 counts as +0.
- *   q_idx      [B, Tq, HI, dI]   dt
+ *   q_idx      view of B x Tq rows of HI * dI ([HI][dI] per query)   dt
  *   k_codes    [B, Nc, dI/2]     uint8 (csa_quantize_mxfp4 of the indexer keys)
  *   k_scales   [B, Nc, dI/32]    uint8
  *   topk       [B, Tq, k]        int32 out: kept indices in ascending order,
@@ -173,9 +196,8 @@ csa_status csa_index_topk_workspace(int64_t B, int64_t Tq, int64_t HI, int64_t d
                                     int64_t q_pos0, size_t *bytes);
 csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
                           int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
-                          const void *q_idx, const uint8_t *k_codes,
-                          const uint8_t *k_scales, int32_t *topk, void *ws,
-                          size_t ws_bytes, hipStream_t stream);
+                          csa_in q_idx, const uint8_t *k_codes, const uint8_t *k_scales,
+                          int32_t *topk, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * csa_index_topk_noalloc -- csa_index_topk without a workspace argument, for
@@ -197,7 +219,7 @@ csa_status csa_index_topk(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64
 #define CSA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 csa_status csa_index_topk_noalloc(csa_dtype dt, int64_t B, int64_t Tq, int64_t HI, int64_t dI,
                                   int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
-                                  const void *q_idx, const uint8_t *k_codes,
+                                  csa_in q_idx, const uint8_t *k_codes,
                                   const uint8_t *k_scales, int32_t *topk, hipStream_t stream);
 
 /*
@@ -214,9 +236,13 @@ csa_status csa_index_topk_noalloc(csa_dtype dt, int64_t B, int64_t Tq, int64_t H
  * One vector per entry and raw token may serve as both key and value (the
  * "shared key-value" reading of the same post): pass the same buffer as ck
  * and cv and as rk and rv, and each row is then read once.
- *   q      [B, Tq, H, D]   dt         o   [B, Tq, H, D]  dt
- *   ck, cv [B, Nc, D]      dt         topk [B, Tq, k]    int32
- *   rk, rv [B, raw_len, D] dt, must cover positions w0..t of every query
+ *   q, o   views of B x Tq rows of H * D ([H][D] per query token)   dt
+ *   ck, cv views of B x Nc rows of D                                dt
+ *   rk, rv views of B x raw_len rows of D, covering positions w0..t of
+ *          every query                                              dt
+ *   topk   [B, Tq, k]      int32
+ *   (a sequence's rows of ck, cv, rk or rv must lie within 2 GiB of its
+ *   first row)
  *   ws     workspace of at least csa_attend_workspace(...) bytes
  * bf16 requires H % 32 == 0 (H <= 256) and D in {64, 128}; fp32 requires
  * D <= 256.
@@ -225,10 +251,9 @@ csa_status csa_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, 
                                 int64_t k, int64_t W, size_t *bytes);
 csa_status csa_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
                       int64_t Nc, int64_t m, int64_t W, int64_t k, int64_t q_pos0,
-                      float scale, const void *q, const void *ck, const void *cv,
-                      const int32_t *topk, const void *rk, const void *rv,
-                      int64_t raw_pos0, int64_t raw_len, void *o, void *ws,
-                      size_t ws_bytes, hipStream_t stream);
+                      float scale, csa_in q, csa_in ck, csa_in cv, const int32_t *topk,
+                      csa_in rk, csa_in rv, int64_t raw_pos0, int64_t raw_len, csa_out o,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * hca_attend -- dense attention over every compressed candidate joined with
@@ -242,10 +267,10 @@ csa_status hca_attend_workspace(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, 
                                 int64_t Nc, int64_t m, int64_t W, int64_t q_pos0,
                                 size_t *bytes);
 csa_status hca_attend(csa_dtype dt, int64_t B, int64_t Tq, int64_t H, int64_t D,
-                      int64_t Nc, int64_t m, int64_t W, int64_t q_pos0, float scale,
-                      const void *q, const void *ck, const void *cv, const void *rk,
-                      const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
-                      void *ws, size_t ws_bytes, hipStream_t stream);
+                      int64_t Nc, int64_t m, int64_t W, int64_t q_pos0, float scale, csa_in q,
+                      csa_in ck, csa_in cv, csa_in rk, csa_in rv, int64_t raw_pos0,
+                      int64_t raw_len, csa_out o, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
 
 /*
  * csa_quantize_mxfp8 -- MXFP8 (E4M3) encoding of rows, the storage of the

@@ -17,6 +17,14 @@ EINVAL, EUNSUP = 1, 2
 P = ctypes.c_void_p(0x1000)          # aligned non-null placeholder; never dereferenced
 
 
+def V(row, rows=1 << 20, p=0x1000, ss=None, rs=None, out=False):
+    """A view placeholder (never dereferenced): rows of `row` elements,
+    dense unless strides are given."""
+    rs = row if rs is None else rs
+    ss = rows * rs if ss is None else ss
+    return (binding.CsaOut if out else binding.CsaIn)(p, ss, rs)
+
+
 def declared():
     text = open(HEADER).read()
     return sorted(set(re.findall(r"^(?:csa_status|int|const char \*)\s*(\w+)\(", text, re.M)))
@@ -43,7 +51,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version(L):
     want = int(re.search(r"#define CSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.csa_abi_version() == want == 6
+    assert L.csa_abi_version() == want == 7
 
 
 def err(L):
@@ -51,15 +59,41 @@ def err(L):
 
 
 def test_compress_rejects(L):
-    assert L.hca_compress(7, 1, 8, 8, 4, P, P, 1, P, None) == EINVAL
+    x, g, o = V(8, 8), V(1, 8), V(8, 2, out=True)
+    assert L.hca_compress(7, 1, 8, 8, 4, x, g, 1, o, None) == EINVAL
     assert "dtype" in err(L)
-    assert L.hca_compress(1, 1, 8, 12, 4, P, P, 1, P, None) == EINVAL     # C % 8
-    assert L.hca_compress(1, 1, 8, 8, 0, P, P, 1, P, None) == EINVAL      # m
-    assert L.hca_compress(1, 1, 8, 8, 4, P, P, 3, P, None) == EINVAL      # gate channels
-    assert L.hca_compress(1, 1, 8, 8, 4, None, P, 1, P, None) == EINVAL   # null
+    assert L.hca_compress(1, 1, 8, 12, 4, V(12, 8), g, 1, V(12, 2, out=True), None) == EINVAL
+    assert L.hca_compress(1, 1, 8, 8, 0, x, g, 1, o, None) == EINVAL      # m
+    assert L.hca_compress(1, 1, 8, 8, 4, x, g, 3, o, None) == EINVAL      # gate channels
+    assert L.hca_compress(1, 1, 8, 8, 4, V(8, 8, p=0), g, 1, o, None) == EINVAL   # null
     assert "null" in err(L)
-    assert L.hca_compress(1, 1, 8, 8, 4, ctypes.c_void_p(0x1002), P, 1, P, None) == EINVAL
+    assert L.hca_compress(1, 1, 8, 8, 4, V(8, 8, p=0x1002), g, 1, o, None) == EINVAL
     assert "aligned" in err(L)
+
+
+def test_views_rejected(L):
+    """Strided views: rows that overlap, negative or misaligned strides, and
+    output sequences that overlap are refused before any launch."""
+    g = V(1, 64)
+    f = lambda x, o, B=1: L.hca_compress(1, B, 64, 128, 4, x, V(1, 64, ss=64), 1, o, None)
+    assert f(V(128, 64, rs=64), V(128, 16, out=True)) == EINVAL            # rows overlap
+    assert "row stride" in err(L)
+    assert f(V(128, 64, rs=-128), V(128, 16, out=True)) == EINVAL          # negative
+    assert f(V(128, 64, rs=132), V(128, 16, out=True)) == EINVAL           # 264-byte rows
+    assert "aligned" in err(L)
+    assert f(V(128, 64, ss=9000 * 128), V(128, 16, ss=8 * 128, out=True), B=2) == EINVAL
+    assert "overlap" in err(L)                                            # out sequences
+    # a window of raw rows and query rows taken from larger buffers pass the
+    # view checks (the raw-position check, made after them, is what fails)
+    q, ck = V(128 * 128, 4, ss=100 * 128 * 128), V(128, 300, rs=256)
+    st = L.hca_attend(1, 2, 4, 128, 128, 300, 4, 128, 1196, 1.0, q, ck, ck, V(128, 128, rs=512),
+                      V(128, 128, rs=512), 1073, 127, V(128 * 128, 4, out=True), None, 0, None)
+    assert st == EINVAL and "raw rows" in err(L)
+    # key rows spanning more than 2 GiB in one sequence
+    st = L.hca_attend(1, 1, 1, 128, 128, 300, 4, 128, 1199, 1.0, V(128 * 128, 1), V(128, 300,
+                      rs=1 << 23), V(128, 300), V(128, 128), V(128, 128), 1072, 128,
+                      V(128 * 128, 1, out=True), None, 0, None)
+    assert st == EUNSUP and "2 GiB" in err(L)
 
 
 def test_append_rejects(L):
@@ -86,8 +120,9 @@ def test_append_rejects(L):
 
 
 def test_quantize_rejects(L):
-    assert L.csa_quantize_mxfp4(1, 4, 48, P, P, P, None) == EINVAL
-    assert L.csa_quantize_mxfp4(1, 4, 64, P, None, P, None) == EINVAL
+    assert L.csa_quantize_mxfp4(1, 4, 48, V(48, 4), P, P, None) == EINVAL
+    assert L.csa_quantize_mxfp4(1, 4, 64, V(64, 4), None, P, None) == EINVAL
+    assert L.csa_quantize_mxfp4(1, 4, 64, V(64, 4, rs=32), P, P, None) == EINVAL   # overlap
 
 
 def test_mxfp8_rejects(L):
@@ -198,7 +233,7 @@ def test_index_workspace_and_rejects(L):
     assert "candidates" in err(L)
     # a workspace that is too small is refused before launch
     st = L.csa_index_topk(1, 16, 1, 4, 64, 262144, 4, 128, 512, (1 << 20) - 1,
-                          P, P, P, P, P, 1024, None)
+                          V(256, 1), P, P, P, P, 1024, None)
     assert st == EINVAL and "workspace" in err(L)
 
 
@@ -212,10 +247,11 @@ def test_attend_workspace_and_rejects(L):
     assert L.csa_attend_workspace(1, 1, 1, 96, 128, 512, 128, ctypes.byref(n)) == EUNSUP
     assert L.csa_attend_workspace(1, 1, 1, 128, 96, 512, 128, ctypes.byref(n)) == EUNSUP
     # raw rows must cover the window of every query
-    st = L.csa_attend(1, 1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, P, P, P,
-                      1073, 127, P, None, 0, None)
+    q, o, kv, r = V(128 * 128, 1), V(128 * 128, 1, out=True), V(128, 300), V(128, 128)
+    st = L.csa_attend(1, 1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, q, kv, kv, P, r, r,
+                      1073, 127, o, None, 0, None)
     assert st == EINVAL and "raw rows" in err(L)
-    st = L.hca_attend(1, 1, 1, 128, 128, 300, 4, 0, 1199, 1.0, P, P, P, P, P, 1072, 128, P,
+    st = L.hca_attend(1, 1, 1, 128, 128, 300, 4, 0, 1199, 1.0, q, kv, kv, r, r, 1072, 128, o,
                       None, 0, None)
     assert st == EINVAL and "window" in err(L)
 
@@ -232,10 +268,11 @@ def test_index_noalloc_rejects_before_the_device(L):
     any device call: a selection needing more than the static array (140,000
     query rows, up to 34,968 candidates: chunk lists of 2.6 GB) is refused."""
     f = L.csa_index_topk_noalloc
-    assert f(1, 1, 140000, 4, 64, 35000, 4, 128, 512, 0, P, P, P, P, None) == EUNSUP
+    q = V(256, 140000)
+    assert f(1, 1, 140000, 4, 64, 35000, 4, 128, 512, 0, q, P, P, P, None) == EUNSUP
     assert "scratch" in err(L)
-    assert f(1, 1, 16, 3, 64, 8192, 4, 128, 512, 0, P, P, P, P, None) == EUNSUP   # HI
-    assert f(1, 1, 16, 4, 64, 8192, 4, 128, 0, 0, P, P, P, P, None) == EINVAL     # k
-    assert f(1, 1, 16, 4, 64, 8192, 4, 128, 512, 0, None, P, P, P, None) == EINVAL
+    assert f(1, 1, 16, 3, 64, 8192, 4, 128, 512, 0, V(192, 16), P, P, P, None) == EUNSUP   # HI
+    assert f(1, 1, 16, 4, 64, 8192, 4, 128, 0, 0, q, P, P, P, None) == EINVAL     # k
+    assert f(1, 1, 16, 4, 64, 8192, 4, 128, 512, 0, V(256, 16, p=0), P, P, P, None) == EINVAL
     assert "null" in err(L)
-    assert f(1, 1, 1, 4, 64, 100, 4, 128, 512, 1 << 20, P, P, P, P, None) == EINVAL  # Nc
+    assert f(1, 1, 1, 4, 64, 100, 4, 128, 512, 1 << 20, V(256, 1), P, P, P, None) == EINVAL
