@@ -24,8 +24,9 @@ struct TileSrc {
 // operand), so the compiler can count them: the current batch is waited
 // for while the next one stays in flight.  STREAM: keys read once (decode)
 // bypass the caches' normal retention.
-// Offsets from the tile source's base are 32-bit: a source holds at most
-// 262,144 candidates of at most 32 code bytes.
+// Offsets from the tile source's base are 32-bit, formed by 24-bit
+// multiplies: a source holds at most 262,144 candidates of at most 32 code
+// bytes (2^23 bytes).
 template <int UNR, bool STREAM>
 __device__ __forceinline__ void load_batch(const TileSrc& ts, int v0, int stride,
                                            u32x4 (&kw)[UNR], int (&ksv)[UNR]) {
@@ -35,9 +36,9 @@ __device__ __forceinline__ void load_batch(const TileSrc& ts, int v0, int stride
     for (int x = 0; x < UNR; ++x) {
         const uint32_t j = (uint32_t)min((v0 + x) * stride * 32 + ts.row, ts.nc_max - 1);
         const u32x4* src =
-            reinterpret_cast<const u32x4*>(ts.kcb + (j * (uint32_t)ts.kbytes + koff));
+            reinterpret_cast<const u32x4*>(ts.kcb + (__umul24(j, (uint32_t)ts.kbytes) + koff));
         kw[x] = STREAM ? __builtin_nontemporal_load(src) : *src;
-        const int sc = ts.ksb[j * (uint32_t)ts.kscales + soff];
+        const int sc = ts.ksb[__umul24(j, (uint32_t)ts.kscales) + soff];
         ksv[x] = ts.kb < ts.kscales ? sc : 127;
     }
 }

@@ -10,21 +10,23 @@
 // than keeping 8 x 32K fp32 scores anywhere).  Key order: fp32 bits of the
 // score, larger first, ties to the lower candidate index.
 //
-// Rows with enough candidates take the sampled path:
+// Each row owns an 8 KB region of LDS, reused phase by phase (so two blocks
+// share a CU and four waves share a SIMD).  Rows with enough candidates take
+// the sampled path:
 //   1. a level-1 histogram (1/64-octave bins) of every 8th key tile;
-//   2. from the sample's rank statistics, a key range [lo, hi) that holds
-//      the k-th key with a margin of 3 sigma + 4 sample ranks each side;
-//   3. one pass over all keys: keys >= hi go to the kept bitmap, keys in
-//      [lo, hi) to the wave's own segment of a buffer (ballot compaction,
-//      no shared counter);
-//   4. if the counts prove that the k-th key lies in the buffer (kept < k
-//      <= kept + buffered, no overflow), an exact radix threshold over the
-//      buffer finishes the row.
+//   2. from the sample's rank statistics, a lower key bound lo that the k-th
+//      key clears with a margin of 3 sigma + 4 sample ranks;
+//   3. one pass over all keys: every key >= lo goes, with its candidate
+//      index, to the wave's own segment of the row region (ballot
+//      compaction, no shared counter);
+//   4. if the segments hold at least k keys and none overflowed, the k-th
+//      key is among them: an exact radix threshold over the collected keys
+//      finishes the row.
 // Other rows, and any row whose check fails, run the exact multi-pass
 // search: histogram passes narrow the range of the k-th key until it holds
 // at most 256 keys (or one key value), then a collecting pass.  Either way
 // ties at the threshold are resolved by candidate order and the kept set is
-// read out of the bitmap in ascending order.
+// read out of a candidate bitmap in ascending order.
 #include "internal.h"
 #include "mxfp4.h"
 #include "wave_select.h"
@@ -33,27 +35,33 @@
 namespace csa {
 
 constexpr int ST_NT = 512;             // 8 waves: one per query row at the decisions
+constexpr int ST_NWV = ST_NT / WAVE;
 constexpr int ST_QT = 8;               // query rows per block
-constexpr int ST_CAP = 256;            // collected keys per row (multi-pass search)
-constexpr int ST_SEG = 96;             // buffered keys per row and wave (sampled path)
-constexpr int ST_BUF = ST_SEG * (ST_NT / WAVE);
 constexpr int ST_MAXW = 1024;          // bitmap words per row -> 32768 candidates
+constexpr int ST_RW = 2 * ST_MAXW;     // 32-bit words of a row's region
+// sampled path: keys [ST_NWV][ST_SEG] from word 0, their candidate indices
+// (16 bits) [ST_NWV][ST_SEG] from word ST_JOFF
+constexpr int ST_SEG = 170;            // collected keys per row and wave
+constexpr int ST_BUF = ST_SEG * ST_NWV;
+constexpr int ST_JOFF = ST_BUF;
+static_assert(ST_JOFF + (ST_BUF + 1) / 2 <= ST_RW, "sampled buffers fit the row region");
+// multi-pass search: histogram at word 0; collection: kept bitmap at word 0,
+// (key, index) pairs at word ST_MAXW, then the tie bitmap there
+constexpr int ST_CAP = 256;            // collected keys per row (multi-pass search)
+constexpr int ST_SCR = ST_MAXW + 2 * ST_CAP;   // 256 words of radix scratch
+static_assert(ST_SCR + 256 <= ST_RW, "radix scratch fits the row region");
 constexpr int ST_SAMPLE = 8;           // one key tile in ST_SAMPLE is sampled
 constexpr int ST_SAMPLE_MIN = 2048;    // candidates a row needs for the sampled path
-// key tiles per wave and batch (two batches and two tiles' scores are live)
-template <int HI> constexpr int st_unr() { return 4; }
+constexpr int ST_SAMPLE_MAXK = 768;    // and at most this many kept ones
+constexpr int ST_UNR = 2;              // key tiles per wave and batch
 
 enum : int { M_DONE = 0, M_HIST1 = 1, M_HIST = 2, M_COLLECT = 3, M_SAMPLED = 4 };
 
 struct StreamSmem {
-    uint32_t sel[ST_QT][ST_MAXW];      // kept candidates
-    uint32_t hist[ST_QT][SEL_NB];      // histograms; radix scratch
-    uint32_t eq[ST_QT][ST_MAXW];       // candidates equal to the threshold key
-    u32x2 buf[ST_QT][ST_BUF];          // (key, index): one segment per wave (sampled
-                                       // path); the first ST_CAP: multi-pass buffer
-    int segcnt[ST_QT][ST_NT / WAVE];
+    uint32_t reg[ST_QT][ST_RW];        // one region per query row
     u32x4 aq[64];                      // MFMA A operand of lane kb*32 + row
     uint32_t as[64];                   // and its scale byte
+    int segcnt[ST_QT][ST_NWV];
     uint32_t lo[ST_QT], hi[ST_QT];
     int shift[ST_QT], mode[ST_QT], above[ST_QT], need[ST_QT], cnt[ST_QT], eqmode[ST_QT];
     int nc[ST_QT];
@@ -61,7 +69,7 @@ struct StreamSmem {
 };
 
 template <typename T, int HI>
-__global__ void __launch_bounds__(ST_NT)
+__global__ void __launch_bounds__(ST_NT) __attribute__((amdgpu_waves_per_eu(4)))
 k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ kc,
                const uint8_t* __restrict__ ks, int32_t* __restrict__ topk, int64_t Tq, int dI,
                int64_t Nc, int64_t m, int64_t W, int k, int64_t q_pos0) {
@@ -77,12 +85,10 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int row = lane & 31, kb = lane >> 5;
     const int nc_max = (int)n_candidates(q_pos0 + q0 + qv - 1, m, W);
-    const int nw = (nc_max + 31) / 32;
 
     // ---- per-query setup
     if (tid < ST_QT) {
         const int nc = tid < qv ? (int)n_candidates(q_pos0 + q0 + tid, m, W) : 0;
-        for (int w = 0; w < ST_NT / WAVE; ++w) S.segcnt[tid][w] = 0;
         const int need = min(nc, k);
         S.nc[tid] = nc;
         S.need[tid] = need;
@@ -93,8 +99,9 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         S.hi[tid] = KEY_END;
         S.shift[tid] = 0;
         // all candidates kept when there are at most k of them
-        S.mode[tid] = (need == 0 || nc <= k) ? M_DONE
-                      : nc >= ST_SAMPLE_MIN ? M_SAMPLED : M_HIST1;
+        S.mode[tid] = (need == 0 || nc <= k)                          ? M_DONE
+                      : (nc >= ST_SAMPLE_MIN && need <= ST_SAMPLE_MAXK) ? M_SAMPLED
+                                                                        : M_HIST1;
     }
     // ---- MXFP4 of the query rows, once per block: 8 threads per 32-value
     // block (lane kb*32 + row of the MFMA A operand: query row / HI, head
@@ -123,18 +130,18 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         if (part == 0) S.as[bl] = (uint32_t)(e + 127);
     }
     __syncthreads();
+    // row regions: the kept bitmap of rows that keep every candidate, a zero
+    // level-1 histogram for the others
     for (int q = 0; q < ST_QT; ++q) {
         const int nc = S.nc[q];
-        for (int w = tid; w < nw; w += ST_NT) {
-            // queries with nc <= k keep every candidate
-            uint32_t full = 0u;
-            if (nc <= k) {
+        const bool all = S.mode[q] == M_DONE;
+        for (int w = tid; w < ST_MAXW; w += ST_NT) {
+            uint32_t v = 0u;
+            if (all) {
                 const int lo_b = w * 32;
-                full = lo_b + 32 <= nc ? 0xFFFFFFFFu
-                                       : (lo_b >= nc ? 0u : ((1u << (nc - lo_b)) - 1u));
+                v = lo_b + 32 <= nc ? 0xFFFFFFFFu : (lo_b >= nc ? 0u : ((1u << (nc - lo_b)) - 1u));
             }
-            S.sel[q][w] = full;
-            S.eq[q][w] = 0u;
+            S.reg[q][w] = v;
         }
     }
     const u32x4 aw = S.aq[kb * 32 + row];
@@ -151,6 +158,11 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         qslot[u] = qi;
         ncq[u] = (qi < qv) ? S.nc[qi] : 0;
     }
+    if (tid == 0) {
+        int a = 0;
+        for (int q = 0; q < ST_QT; ++q) a |= S.mode[q] == M_SAMPLED;
+        S.any_sampled = a;
+    }
     __syncthreads();
 
     const int ntiles = (nc_max + 31) / 32;
@@ -158,144 +170,123 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
                      row, kb};
 
     // ================= sampled path
-    if (tid == 0) {
-        int a = 0;
-        for (int q = 0; q < ST_QT; ++q) a |= S.mode[q] == M_SAMPLED;
-        S.any_sampled = a;
-    }
-    for (int i = tid; i < ST_QT * SEL_NB; i += ST_NT) (&S.hist[0][0])[i] = 0u;
-    __syncthreads();
     if (S.any_sampled) {
         bool act[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) act[u] = qslot[u] < qv && S.mode[qslot[u]] == M_SAMPLED;
         // 1. level-1 histogram of the sampled tiles
-        stream_tiles<ST_NT, st_unr<HI>()>(ts, (ntiles + ST_SAMPLE - 1) / ST_SAMPLE, ST_SAMPLE, aop, sa,
-                     [&](const f32x16& acc, int j0) {
+        stream_tiles<ST_NT, ST_UNR>(ts, (ntiles + ST_SAMPLE - 1) / ST_SAMPLE, ST_SAMPLE, aop, sa,
+                                    [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
             uint32_t key[NU];
             tile_keys<HI>(acc, key);
 #pragma unroll
             for (int u = 0; u < NU; ++u)
-                if (act[u] && j < ncq[u])
-                    atomicAdd(&S.hist[qslot[u]][lvl1_bin(key[u])], 1u);
+                if (act[u] && j < ncq[u]) atomicAdd(&S.reg[qslot[u]][lvl1_bin(key[u])], 1u);
         });
         __syncthreads();
-        // 2. key range of the k-th key, per sampled row (wave q)
-        for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
+        // 2. lower key bound of the k-th key, per sampled row (wave q)
+        for (int q = wave; q < ST_QT; q += ST_NWV) {
             if (S.mode[q] != M_SAMPLED) continue;
             const int nc = S.nc[q], need = S.need[q];
             const int ns = (nc / (32 * ST_SAMPLE)) * 32 + min(32, nc % (32 * ST_SAMPLE));
             const float f = (float)ns / (float)nc;
             const float rt = (float)need * f;
             const float margin = 3.f * sqrtf(rt * (1.f - f)) + 4.f;
-            const int need_hi = (int)floorf(rt - margin);
             const int need_lo = (int)ceilf(rt + margin);
-            uint32_t khi = KEY_END, klo = 0u;
-            int gt, in;
-            if (need_hi >= 1) {
-                const int d = wave_hist_find(&S.hist[q][0], need_hi, &gt, &in);
-                uint32_t l0, h0;
-                lvl1_range(d, &l0, &h0);
-                khi = h0;
-            }
+            uint32_t klo = 0u;
             if (need_lo <= ns) {
-                const int d = wave_hist_find(&S.hist[q][0], need_lo, &gt, &in);
-                uint32_t l0, h0;
-                lvl1_range(d, &l0, &h0);
-                klo = l0;
+                int gt, in;
+                const int d = wave_hist_find(&S.reg[q][0], need_lo, &gt, &in);
+                uint32_t h0;
+                lvl1_range(d, &klo, &h0);
             }
-            if (lane == 0) {
-                S.lo[q] = klo;
-                S.hi[q] = khi;
-                S.cnt[q] = 0;
-            }
+            if (lane == 0) S.lo[q] = klo;
         }
         __syncthreads();
-        // 3. one pass over every key
-        uint32_t lo[NU], hi[NU];
+        // 3. one pass over every key: the keys >= lo, with their indices, go
+        // to this wave's segment of their row's region
+        uint32_t lo[NU];
+        int cnt[NU];                    // lanes of half-wave kb count the keys of its row
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int q = qslot[u] < ST_QT ? qslot[u] : 0;
-            lo[u] = S.lo[q];
-            hi[u] = S.hi[q];
+            lo[u] = act[u] ? S.lo[qslot[u]] : KEY_END;
+            cnt[u] = 0;
         }
-        int wc0[NU], wc1[NU];           // this wave's segment counts, half-waves 0 / 1
-#pragma unroll
-        for (int u = 0; u < NU; ++u) wc0[u] = wc1[u] = 0;
-        stream_tiles<ST_NT, st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+        stream_tiles<ST_NT, ST_UNR>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
             uint32_t keys[NU];
             tile_keys<HI>(acc, keys);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const bool ok = act[u] && j < ncq[u];
-                const uint32_t key = keys[u];
-                const bool above = ok && key >= hi[u];
-                const bool in = ok && !above && key >= lo[u];
-                const int q = qslot[u] < ST_QT ? qslot[u] : 0;
-                // the 32 lanes of a half-wave hold the tile's 32 keys of
-                // one query, and each bitmap word is written by one tile
-                // only (sel starts at zero for sampled rows)
-                const uint64_t bab = __ballot(above);
-                if (row == 0 && act[u]) S.sel[q][j0 >> 5] = kb ? (uint32_t)(bab >> 32) : (uint32_t)bab;
-                const uint64_t bin = __ballot(in);
-                if (bin != 0ull) {
-                    const uint32_t h0 = (uint32_t)bin, h1 = (uint32_t)(bin >> 32);
-                    if (in) {
-                        const uint32_t mine = kb ? h1 : h0;
-                        const int pos = (kb ? wc1[u] : wc0[u]) +
-                                        __popc(mine & ((1u << row) - 1u));
-                        if (pos < ST_SEG)
-                            S.buf[q][wave * ST_SEG + pos] = u32x2{key, (uint32_t)j};
+                // the 32 lanes of a half-wave hold the tile's 32 keys of one
+                // query row; the two halves serve different rows
+                const bool hit = act[u] && j < ncq[u] && keys[u] >= lo[u];
+                const uint64_t bal = __ballot(hit);
+                if (bal != 0ull) {
+                    const uint32_t mine = kb ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+                    if (hit) {
+                        const int pos = cnt[u] + __popc(mine & ((1u << row) - 1u));
+                        if (pos < ST_SEG) {
+                            uint32_t* r = &S.reg[qslot[u]][0];
+                            r[wave * ST_SEG + pos] = keys[u];
+                            reinterpret_cast<uint16_t*>(r + ST_JOFF)[wave * ST_SEG + pos] =
+                                (uint16_t)j;
+                        }
                     }
-                    wc0[u] += __popc(h0);
-                    wc1[u] += __popc(h1);
+                    cnt[u] += __popc(mine);
                 }
             }
         });
 #pragma unroll
         for (int u = 0; u < NU; ++u)
-            if (row == 0 && act[u]) S.segcnt[qslot[u]][wave] = kb ? wc1[u] : wc0[u];
+            if (row == 0 && act[u]) S.segcnt[qslot[u]][wave] = cnt[u];
         __syncthreads();
         // 4. check the counts and finish the row, or hand it to the search
-        for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
+        for (int q = wave; q < ST_QT; q += ST_NWV) {
             if (S.mode[q] != M_SAMPLED) continue;
             const int qnw = (S.nc[q] + 31) / 32;
-            int c = 0;
-            for (int w = lane; w < qnw; w += WAVE) c += __popc(S.sel[q][w]);
-            const int kept = wave_sum(c);
+            uint32_t* r = &S.reg[q][0];
             int nin = 0, over = 0;
-            for (int w = 0; w < ST_NT / WAVE; ++w) {
+            for (int w = 0; w < ST_NWV; ++w) {
                 nin += S.segcnt[q][w];
                 over |= S.segcnt[q][w] > ST_SEG;
             }
             const int need = S.need[q];
-            if (kept < need && kept + nin >= need && !over) {
-                constexpr int EPT = ST_BUF / WAVE;
-                uint32_t key[EPT];
+            if (nin >= need && !over) {
+                // every key >= lo is collected and the k-th key is one of them
+                constexpr int EPT = (ST_BUF + WAVE - 1) / WAVE;
+                uint32_t key[EPT], jj[EPT];
                 bool valid[EPT];
 #pragma unroll
                 for (int e = 0; e < EPT; ++e) {
-                    const int p = lane * EPT + e;
-                    valid[e] = p % ST_SEG < S.segcnt[q][p / ST_SEG];
-                    key[e] = valid[e] ? S.buf[q][p][0] : 0u;
+                    const int p = e * WAVE + lane;
+                    valid[e] = p < ST_BUF && p % ST_SEG < S.segcnt[q][min(p / ST_SEG, ST_NWV - 1)];
+                    key[e] = valid[e] ? r[p] : 0u;
+                    jj[e] = valid[e] ? reinterpret_cast<const uint16_t*>(r + ST_JOFF)[p] : 0u;
                 }
+                __builtin_amdgcn_wave_barrier();
                 uint32_t thr;
                 int need_eq;
-                wave_radix_threshold<EPT>(key, valid, need - kept, &S.hist[q][0], &thr, &need_eq);
+                wave_radix_threshold<EPT>(key, valid, need, r + ST_SCR, &thr, &need_eq);
+                // the region now holds the kept bitmap and the tie bitmap
+                for (int w = lane; w < qnw; w += WAVE) {
+                    r[w] = 0u;
+                    r[ST_MAXW + w] = 0u;
+                }
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int e = 0; e < EPT; ++e) {
                     if (!valid[e]) continue;
-                    const uint32_t j = S.buf[q][lane * EPT + e][1];
-                    if (key[e] > thr) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
-                    else if (key[e] == thr) atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
+                    const uint32_t bit = 1u << (jj[e] & 31);
+                    if (key[e] > thr) atomicOr(&r[jj[e] >> 5], bit);
+                    else if (key[e] == thr) atomicOr(&r[ST_MAXW + (jj[e] >> 5)], bit);
                 }
                 __builtin_amdgcn_wave_barrier();
-                wave_merge_first_bits(&S.sel[q][0], &S.eq[q][0], qnw, need_eq);
+                wave_merge_first_bits(r, r + ST_MAXW, qnw, need_eq);
                 if (lane == 0) S.mode[q] = M_DONE;
             } else {
-                for (int w = lane; w < qnw; w += WAVE) S.sel[q][w] = 0u;
+                for (int w = lane; w < ST_MAXW; w += WAVE) r[w] = 0u;
                 if (lane == 0) {
                     S.mode[q] = M_HIST1;
                     S.lo[q] = 0u;
@@ -309,7 +300,10 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
 
     // ================= exact multi-pass search for the remaining rows: every
     // row still searching starts at level 1 here, so EXACT_PASSES passes
-    // (level 1, the narrowing passes, the collection) finish every row
+    // (level 1, the narrowing passes, the collection) finish every row.  A
+    // row's histogram is zero whenever it enters a histogram pass; its kept
+    // bitmap (and, for a single key value, tie bitmap) is zero when it
+    // enters the collection.
 #pragma unroll 1
     for (int pass = 0; pass < EXACT_PASSES; ++pass) {
         // per-slot state of this pass (registers)
@@ -330,11 +324,10 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
             for (int q = 0; q < ST_QT; ++q) a |= S.mode[q] != M_DONE;
             S.any_active = a;
         }
-        for (int i = tid; i < ST_QT * SEL_NB; i += ST_NT) (&S.hist[0][0])[i] = 0u;
         __syncthreads();
         if (!S.any_active) break;
 
-        stream_tiles<ST_NT, st_unr<HI>()>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+        stream_tiles<ST_NT, ST_UNR>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
             const int j = j0 + row;
             uint32_t keys[NU];
             tile_keys<HI>(acc, keys);
@@ -342,21 +335,21 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
             for (int u = 0; u < NU; ++u) {
                 if (md[u] == M_DONE || j >= ncq[u]) continue;
                 const uint32_t key = keys[u];
-                const int q = qslot[u];
+                uint32_t* r = &S.reg[qslot[u]][0];
                 if (md[u] == M_HIST1) {
-                    atomicAdd(&S.hist[q][lvl1_bin(key)], 1u);
+                    atomicAdd(&r[lvl1_bin(key)], 1u);
                 } else if (md[u] == M_HIST) {
-                    if (key >= lo[u] && key < hi[u])
-                        atomicAdd(&S.hist[q][(key - lo[u]) >> sh[u]], 1u);
+                    if (key >= lo[u] && key < hi[u]) atomicAdd(&r[(key - lo[u]) >> sh[u]], 1u);
                 } else {                                  // collect
                     if (key >= hi[u]) {
-                        atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
+                        atomicOr(&r[j >> 5], 1u << (j & 31));
                     } else if (key >= lo[u]) {
                         if (eqm[u]) {
-                            atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
+                            atomicOr(&r[ST_MAXW + (j >> 5)], 1u << (j & 31));
                         } else {
-                            int pos = atomicAdd(&S.cnt[q], 1);
-                            if (pos < ST_CAP) S.buf[q][pos] = u32x2{key, (uint32_t)j};
+                            const int pos = atomicAdd(&S.cnt[qslot[u]], 1);
+                            if (pos < ST_CAP)
+                                reinterpret_cast<u32x2*>(r + ST_MAXW)[pos] = u32x2{key, (uint32_t)j};
                         }
                     }
                 }
@@ -365,12 +358,14 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         __syncthreads();
 
         // ---- per-query decisions: wave w handles query w
-        for (int q = wave; q < ST_QT; q += ST_NT / WAVE) {
+        for (int q = wave; q < ST_QT; q += ST_NWV) {
             const int mode = S.mode[q];
+            const int qnw = (S.nc[q] + 31) / 32;
+            uint32_t* r = &S.reg[q][0];
             if (mode == M_HIST1 || mode == M_HIST) {
                 const int rem = S.need[q] - S.above[q];
                 int gt, in;
-                const int d = wave_hist_find(&S.hist[q][0], rem, &gt, &in);
+                const int d = wave_hist_find(r, rem, &gt, &in);
                 uint32_t nlo, nhi;
                 if (mode == M_HIST1) {
                     lvl1_range(d, &nlo, &nhi);
@@ -379,14 +374,21 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
                     uint64_t top = (uint64_t)S.lo[q] + ((uint64_t)(d + 1) << S.shift[q]);
                     nhi = top < (uint64_t)S.hi[q] ? (uint32_t)top : S.hi[q];
                 }
+                const bool single = nhi - nlo == 1u;
+                const bool collect = in <= ST_CAP || single;
+                const bool eq = single && in > ST_CAP;
+                __builtin_amdgcn_wave_barrier();
+                // the next pass's zero histogram, or zero bitmaps for the collection
+                for (int w = lane; w < ST_MAXW; w += WAVE) r[w] = 0u;
+                if (eq)
+                    for (int w = lane; w < ST_MAXW; w += WAVE) r[ST_MAXW + w] = 0u;
                 if (lane == 0) {
                     S.above[q] += gt;
                     S.lo[q] = nlo;
                     S.hi[q] = nhi;
-                    const bool single = nhi - nlo == 1u;
-                    if (in <= ST_CAP || single) {
+                    if (collect) {
                         S.mode[q] = M_COLLECT;
-                        S.eqmode[q] = single && in > ST_CAP;
+                        S.eqmode[q] = eq;
                         S.cnt[q] = 0;
                     } else {
                         S.mode[q] = M_HIST;
@@ -402,26 +404,32 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
                     // exact threshold among the collected keys
                     const int n = min(S.cnt[q], ST_CAP);
                     constexpr int EPT = ST_CAP / WAVE;
-                    uint32_t key[EPT];
+                    uint32_t key[EPT], jj[EPT];
                     bool valid[EPT];
 #pragma unroll
                     for (int e = 0; e < EPT; ++e) {
-                        const int p = lane * EPT + e;
+                        const int p = e * WAVE + lane;
                         valid[e] = p < n;
-                        key[e] = valid[e] ? S.buf[q][p][0] : 0u;
+                        const u32x2 v = valid[e] ? reinterpret_cast<const u32x2*>(r + ST_MAXW)[p]
+                                                 : u32x2{0u, 0u};
+                        key[e] = v[0];
+                        jj[e] = v[1];
                     }
+                    __builtin_amdgcn_wave_barrier();
                     uint32_t thr;
-                    wave_radix_threshold<EPT>(key, valid, need_in, &S.hist[q][0], &thr, &need_eq);
+                    wave_radix_threshold<EPT>(key, valid, need_in, r + ST_SCR, &thr, &need_eq);
+                    for (int w = lane; w < qnw; w += WAVE) r[ST_MAXW + w] = 0u;
+                    __builtin_amdgcn_wave_barrier();
 #pragma unroll
                     for (int e = 0; e < EPT; ++e) {
                         if (!valid[e]) continue;
-                        const uint32_t j = S.buf[q][lane * EPT + e][1];
-                        if (key[e] > thr) atomicOr(&S.sel[q][j >> 5], 1u << (j & 31));
-                        else if (key[e] == thr) atomicOr(&S.eq[q][j >> 5], 1u << (j & 31));
+                        const uint32_t bit = 1u << (jj[e] & 31);
+                        if (key[e] > thr) atomicOr(&r[jj[e] >> 5], bit);
+                        else if (key[e] == thr) atomicOr(&r[ST_MAXW + (jj[e] >> 5)], bit);
                     }
                     __builtin_amdgcn_wave_barrier();
                 }
-                wave_merge_first_bits(&S.sel[q][0], &S.eq[q][0], nw, need_eq);
+                wave_merge_first_bits(r, r + ST_MAXW, qnw, need_eq);
                 if (lane == 0) S.mode[q] = M_DONE;
             }
         }
@@ -429,9 +437,9 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
     }
 
     // ---- read out: wave w writes query w
-    for (int q = wave; q < qv; q += ST_NT / WAVE) {
+    for (int q = wave; q < qv; q += ST_NWV) {
         const int nc = S.nc[q];
-        wave_emit_bitmap(&S.sel[q][0], (nc + 31) / 32, topk + (b * Tq + q0 + q) * k, k);
+        wave_emit_bitmap(&S.reg[q][0], (nc + 31) / 32, topk + (b * Tq + q0 + q) * k, k);
     }
 }
 
