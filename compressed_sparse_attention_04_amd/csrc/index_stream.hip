@@ -20,8 +20,8 @@
 //      index, to the wave's own segment of the row region (ballot
 //      compaction, no shared counter);
 //   4. if the segments hold at least k keys and none overflowed, the k-th
-//      key is among them: an exact radix threshold over the collected keys
-//      finishes the row.
+//      key is among them: its exact value, decided bit by bit with wave
+//      ballots over the collected keys, finishes the row.
 // Other rows, and any row whose check fails, run the exact multi-pass
 // search: histogram passes narrow the range of the k-th key until it holds
 // at most 256 keys (or one key value), then a collecting pass.  Either way
@@ -46,10 +46,9 @@ constexpr int ST_BUF = ST_SEG * ST_NWV;
 constexpr int ST_JOFF = ST_BUF;
 static_assert(ST_JOFF + (ST_BUF + 1) / 2 <= ST_RW, "sampled buffers fit the row region");
 // multi-pass search: histogram at word 0; collection: kept bitmap at word 0,
-// (key, index) pairs at word ST_MAXW, then the tie bitmap there
+// (key, index) pairs at word ST_MAXW, then the tie bitmap there; the read-out
+// stages the kept indices there too
 constexpr int ST_CAP = 256;            // collected keys per row (multi-pass search)
-constexpr int ST_SCR = ST_MAXW + 2 * ST_CAP;   // 256 words of radix scratch
-static_assert(ST_SCR + 256 <= ST_RW, "radix scratch fits the row region");
 constexpr int ST_SAMPLE = 8;           // one key tile in ST_SAMPLE is sampled
 constexpr int ST_SAMPLE_MIN = 2048;    // candidates a row needs for the sampled path
 constexpr int ST_SAMPLE_MAXK = 768;    // and at most this many kept ones
@@ -268,7 +267,7 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
                 __builtin_amdgcn_wave_barrier();
                 uint32_t thr;
                 int need_eq;
-                wave_radix_threshold<EPT>(key, valid, need, r + ST_SCR, &thr, &need_eq);
+                wave_ballot_threshold<EPT>(key, valid, need, &thr, &need_eq);
                 // the region now holds the kept bitmap and the tie bitmap
                 for (int w = lane; w < qnw; w += WAVE) {
                     r[w] = 0u;
@@ -417,7 +416,7 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
                     }
                     __builtin_amdgcn_wave_barrier();
                     uint32_t thr;
-                    wave_radix_threshold<EPT>(key, valid, need_in, r + ST_SCR, &thr, &need_eq);
+                    wave_ballot_threshold<EPT>(key, valid, need_in, &thr, &need_eq);
                     for (int w = lane; w < qnw; w += WAVE) r[ST_MAXW + w] = 0u;
                     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -436,10 +435,16 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         __syncthreads();
     }
 
-    // ---- read out: wave w writes query w
+    // ---- read out: wave w writes query w (through the free half of its
+    // region when k fits there)
     for (int q = wave; q < qv; q += ST_NWV) {
         const int nc = S.nc[q];
-        wave_emit_bitmap(&S.reg[q][0], (nc + 31) / 32, topk + (b * Tq + q0 + q) * k, k);
+        int32_t* out = topk + (b * Tq + q0 + q) * k;
+        if (k <= ST_MAXW)
+            wave_emit_bitmap_staged(&S.reg[q][0], (nc + 31) / 32,
+                                    reinterpret_cast<int32_t*>(&S.reg[q][ST_MAXW]), out, k);
+        else
+            wave_emit_bitmap(&S.reg[q][0], (nc + 31) / 32, out, k);
     }
 }
 

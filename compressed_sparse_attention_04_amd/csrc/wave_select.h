@@ -152,6 +152,45 @@ __device__ __forceinline__ void wave_radix_threshold(const uint32_t (&key)[EPT],
     *need_eq_out = rem;
 }
 
+// The same threshold without LDS: the bits of the need-th largest key are
+// decided from the top, a bit kept when at least need keys reach the value
+// with it set (counted with ballots).  The search starts below the leading
+// bits that every valid key shares.  need >= 1 and at most the number of
+// valid keys; keys below 0xFFFFFFFF.
+template <int EPT>
+__device__ __forceinline__ void wave_ballot_threshold(const uint32_t (&key)[EPT],
+                                                      const bool (&valid)[EPT], int need,
+                                                      uint32_t* T_out, int* need_eq_out) {
+    // key + 1 for a valid key, 0 otherwise
+    uint32_t kp[EPT];
+    uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        kp[e] = valid[e] ? key[e] + 1u : 0u;
+        hi = max(hi, kp[e]);
+        lo = valid[e] ? min(lo, kp[e]) : lo;
+    }
+    hi = wave_max_u32(hi);
+    lo = ~wave_max_u32(~lo);
+    const uint32_t diff = hi ^ lo;
+    int top = diff ? 31 - __builtin_clz(diff) : -1;     // highest bit where valid keys differ
+    uint32_t t = top >= 31 ? 0u : hi & ~((2u << top) - 1u);
+#pragma unroll 1
+    for (int bit = top; bit >= 0; --bit) {
+        const uint32_t cand = t | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) cnt += __popcll(__ballot(kp[e] >= cand));
+        if (cnt >= need) t = cand;
+    }
+    if (top < 0) t = hi;                                 // a single key value
+    int gt = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) gt += __popcll(__ballot(kp[e] > t));
+    *T_out = t - 1u;
+    *need_eq_out = need - gt;
+}
+
 // Keep the first need_eq set bits of eq (in candidate order) by OR-ing them
 // into sel; nw words, wave-wide (lane l owns words l*per .. l*per+per-1).
 __device__ __forceinline__ void wave_merge_first_bits(uint32_t* sel, const uint32_t* eq, int nw,
@@ -203,6 +242,31 @@ __device__ __forceinline__ void wave_emit_bitmap(const uint32_t* sel, int nw, in
         }
     }
     for (int s = total + lane; s < k; s += WAVE) out[s] = -1;
+}
+
+// wave_emit_bitmap through LDS: the indices are first written to stage
+// (k ints of scratch LDS) in ascending order, then copied to out with
+// consecutive lanes on consecutive entries.
+__device__ __forceinline__ void wave_emit_bitmap_staged(const uint32_t* sel, int nw,
+                                                        int32_t* stage, int32_t* out, int k) {
+    const int lane = threadIdx.x % WAVE;
+    const int per = (nw + WAVE - 1) / WAVE;
+    const int w0 = lane * per, w1 = min(nw, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    const int incl = wave_incl_scan(cnt);
+    int pos = incl - cnt;
+    const int total = __shfl(incl, WAVE - 1, WAVE);
+    for (int w = w0; w < w1 && pos < k; ++w) {
+        uint32_t bits = sel[w];
+        while (bits && pos < k) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            stage[pos++] = w * 32 + b;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int x = lane; x < k; x += WAVE) out[x] = x < total ? stage[x] : -1;
 }
 
 // Block-wide versions of the two bitmap steps above, for long rows: every
