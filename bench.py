@@ -45,33 +45,9 @@ sys.path.insert(0, ROOT)
 PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp4_TFLOPs": 10100.0}
 PIPE_SLICES = 8        # query slices of a pipelined CSA layer (selection | attention)
 
-# Kernel sources behind each stage: the HBM traffic recorded in
-# profiles/traffic.json for a stage is reported only while the digest of
-# these sources (comments and blank space removed) still matches.
-_IDX = ["indexer.hip", "index_stream.hip", "index_decode.hip", "wave_select.h", "select.h",
-        "mxfp4.h", "fp4_tiles.h", "common.h", "internal.h"]
-STAGE_SOURCES = {
-    "index_topk": _IDX,
-    "csa_attend": ["attend.hip", "common.h", "internal.h"],
-    "hca_attend": ["attend.hip", "common.h", "internal.h"],
-    "compress_m4": ["compress.hip", "common.h", "internal.h"],
-    "compress_m128": ["compress.hip", "common.h", "internal.h"],
-    "quantize_keys": ["mxfp4.hip", "mxfp4.h", "common.h", "internal.h"],
-}
-
-
-def source_digest(files):
-    """sha1 over the kernel sources with comments and blank space removed."""
-    import hashlib
-    import re
-    h = hashlib.sha1()
-    for f in files:
-        text = open(os.path.join(ROOT, "compressed_sparse_attention_04_amd", "csrc", f)).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", "", text)
-        h.update(f.encode())
-        h.update(re.sub(r"\s+", " ", text).strip().encode())
-    return h.hexdigest()
+# The HBM traffic recorded in profiles/traffic.json for a stage is reported
+# only while the digest of the stage's kernel sources still matches.
+from compressed_sparse_attention_04_amd.profsum import STAGE_SOURCES, source_digest  # noqa: E402
 
 
 def recorded_traffic(workload, stage):
@@ -703,6 +679,9 @@ def main():
                     help="timed steps of the prefill workload (default 10); the decode "
                          "workloads time max(steps, 100) steps")
     ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="timed steps of a decode workload (default max(steps, 100)); "
+                         "profiling runs take a few")
     ap.add_argument("--workload", default="all", choices=WORKLOADS,
                     help="all (default): hca_decode_1m, csa_decode_1m and pair_prefill_128k "
                          "in one process, one JSON line")
@@ -750,6 +729,8 @@ def main():
     steps = args.steps if args.steps is not None else 10
     warmup = args.warmup if args.warmup is not None else 2
     dsteps, dwarm = max(steps, 100), max(warmup, 5)
+    if args.decode_steps is not None:
+        dsteps, dwarm = args.decode_steps, min(dwarm, max(1, args.decode_steps))
     cpu = not args.no_cpu_baseline
     storage = {"kv": "one vector as key and value" if args.shared_kv else "separate K and V",
                "kv_format": ("compressed entries MXFP8 (E4M3), window bf16"

@@ -96,6 +96,24 @@ __device__ __forceinline__ int wave_sum(int v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
     return v;
 }
+// Lane exchanges with the pattern in the instruction (ds_swizzle bit mode:
+// lane j reads lane j ^ x within its 32; permlane32_swap for the halves), so
+// no lane-index register is formed (shuffle address registers computed once
+// and kept across a kernel have cost spills)
+template <int X>
+__device__ __forceinline__ uint32_t swizzle_xor(uint32_t v) {
+    static_assert(X > 0 && X < 32, "within 32 lanes");
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (X << 10));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_sw(uint32_t v) {
+    v = max(v, swizzle_xor<16>(v));
+    v = max(v, swizzle_xor<8>(v));
+    v = max(v, swizzle_xor<4>(v));
+    v = max(v, swizzle_xor<2>(v));
+    v = max(v, swizzle_xor<1>(v));
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((uint32_t)r[0], (uint32_t)r[1]);
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {

@@ -117,14 +117,15 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         uint32_t amax = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7fffffffu);
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, WAVE));
+        amax = max(amax, swizzle_xor<1>(amax));
+        amax = max(amax, swizzle_xor<2>(amax));
+        amax = max(amax, swizzle_xor<4>(amax));
         const int e = mxfp4_exponent(amax);
         const float p2e = pow2_neg(e);
         uint32_t c = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) c |= mxfp4_code(v[i], p2e) << (4 * i);
-        const uint32_t c2 = (uint32_t)__shfl_xor((int)c, 1, WAVE);
+        const uint32_t c2 = swizzle_xor<1>(c);
         if (!(part & 1)) S.aq[bl][part >> 1] = c | (c2 << 16);
         if (part == 0) S.as[bl] = (uint32_t)(e + 127);
     }
@@ -302,7 +303,15 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
     // (level 1, the narrowing passes, the collection) finish every row.  A
     // row's histogram is zero whenever it enters a histogram pass; its kept
     // bitmap (and, for a single key value, tie bitmap) is zero when it
-    // enters the collection.
+    // enters the collection.  (Entered only by blocks with such rows: its
+    // per-row state does not fit the registers next to the tile stream.)
+    if (tid == 0) {
+        int a = 0;
+        for (int q = 0; q < ST_QT; ++q) a |= S.mode[q] != M_DONE;
+        S.any_active = a;
+    }
+    __syncthreads();
+    if (S.any_active) {
 #pragma unroll 1
     for (int pass = 0; pass < EXACT_PASSES; ++pass) {
         // per-slot state of this pass (registers)
@@ -433,6 +442,7 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
             }
         }
         __syncthreads();
+    }
     }
 
     // ---- read out: wave w writes query w (through the free half of its

@@ -170,8 +170,8 @@ __device__ __forceinline__ void wave_ballot_threshold(const uint32_t (&key)[EPT]
         hi = max(hi, kp[e]);
         lo = valid[e] ? min(lo, kp[e]) : lo;
     }
-    hi = wave_max_u32(hi);
-    lo = ~wave_max_u32(~lo);
+    hi = wave_max_u32_sw(hi);
+    lo = ~wave_max_u32_sw(~lo);
     const uint32_t diff = hi ^ lo;
     int top = diff ? 31 - __builtin_clz(diff) : -1;     // highest bit where valid keys differ
     uint32_t t = top >= 31 ? 0u : hi & ~((2u << top) - 1u);
