@@ -314,10 +314,21 @@ struct Heads32 {
     // the V^T operands (independent of P) are read while the softmax runs
     __device__ __forceinline__ void tile(const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
                                          int nvalid, float scale_log2) {
+        tile(K, V, nvalid, scale_log2, [] {});
+    }
+    // the same with mid() (the copies of a later tile) issued right after the
+    // QK chain: the copy queue fills while the matrix cores run, instead of
+    // every wave of the block queueing its copies at the barrier
+    template <class F>
+    __device__ __forceinline__ void tile(const CSA_LDS uint8_t* K, const CSA_LDS uint8_t* V,
+                                         int nvalid, float scale_log2, F&& mid) {
         bf16x8 kop[D / 16];
         read_k(K, kop);
         __builtin_amdgcn_sched_barrier(0);
         qk(kop);
+        __builtin_amdgcn_sched_barrier(0);
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
         read_v<0, 1>(V);
         softmax_max(nvalid, scale_log2);
         read_v<1, 2>(V);
@@ -450,17 +461,17 @@ k_attend_bf16(AttnArgs<uint16_t, uint16_t> A, const int32_t* __restrict__ topk,
                                       (CSA_LDS uint8_t*)sk, (CSA_LDS uint8_t*)sv);
     };
     // one tile: wait for its copies, barrier (the stage written next is then
-    // free on every wave), issue the copies three tiles ahead, compute
+    // free on every wave), compute, with the copies three tiles ahead issued
+    // once the QK chain is on the matrix cores
     auto step = [&](int tau, uint8_t* ck_, uint8_t* cv_, uint8_t* nk_, uint8_t* nv_) {
         const int after = min(G::NST - 2, tau1 - tau - 1);
         if (after >= 2) CSA_WAIT_VM(2 * PER);
         else if (after == 1) CSA_WAIT_VM(PER);
         else CSA_WAIT_VM(0);
         lds_barrier();
-        issue(tau + G::NST - 1, nk_, nv_);
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
         eng.tile((const CSA_LDS uint8_t*)ck_, (const CSA_LDS uint8_t*)(SHARED ? ck_ : cv_), nvalid,
-                 scale_log2);
+                 scale_log2, [&] { issue(tau + G::NST - 1, nk_, nv_); });
     };
 
     issue(tau0, sK0, sV0);
