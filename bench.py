@@ -517,8 +517,11 @@ def cpu_baseline(name, n_layers=61):
 # --------------------------------------------------------------- timing
 def time_stages(stages, steps, warmup):
     """W untimed steps, then exactly `steps` timed steps bracketed by device
-    synchronisations; per-stage HIP events on the launch stream.  Returns
-    (ms per step from the host clock, mean ms per stage)."""
+    synchronisations (nothing else on the stream: the step time), then the same
+    number of steps again with a HIP event after every stage on the launch
+    stream (the stage times; an event record between kernels costs a few
+    microseconds of device time, so these steps are not the ones timed).
+    Returns (ms per step from the host clock, mean ms per stage)."""
     import torch
     stream = torch.cuda.current_stream()
 
@@ -531,15 +534,18 @@ def time_stages(stages, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(steps)]
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(steps):
         starts[s].record(stream)
         step(evs[s])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     stage_ms = np.zeros(len(stages))
     for s in range(steps):
         prev = starts[s]
