@@ -118,6 +118,9 @@ def test_index_bf16_one_chunk(T, q_pos0, Tq, B):
     (40000, 39990, 10, 2, 512),
     (40000, 16500, 9, 1, 300),
     (4 * 32768, 4 * 32768 - 20, 20, 1, 512),   # largest streaming candidate count
+    (40000, 39990, 10, 1, 768),    # largest k of the sampled path
+    (40000, 39990, 10, 1, 1000),   # k above it: exact search, read-out staged in LDS
+    (40000, 39990, 10, 1, 1500),   # k above the staging room: direct read-out
     # decode path (<= 8 rows, > 4096 candidates): chunked scores + select
     (4 * 70000, 4 * 70000 - 1, 1, 3, 512),
     (4 * 50000, 4 * 50000 - 8, 8, 2, 512),
