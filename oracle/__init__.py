@@ -50,6 +50,7 @@ def lib():
         L.oracle_mxfp4_value.argtypes = [ctypes.c_int, ctypes.c_int]
         L.oracle_mxfp4_value.restype = ctypes.c_double
         L.oracle_quant_mxfp8.argtypes = [_i64, _i64, _ptr, _ptr, _ptr]
+        L.oracle_quant_fp8_rows.argtypes = [_i64, _i64, _ptr, _ptr, _ptr]
         L.oracle_mxfp8_value.argtypes = [ctypes.c_int, ctypes.c_int]
         L.oracle_mxfp8_value.restype = ctypes.c_double
         L.oracle_e4m3_value.argtypes = [ctypes.c_int]
@@ -61,8 +62,11 @@ def lib():
         L.oracle_index_topk.argtypes = [_i64] * 8 + [_ptr] * 7
         L.oracle_attend.argtypes = ([_i64] * 8 + [_ptr, ctypes.c_double] + [_ptr] * 6
                                     + [_i64, _i64, _ptr])
-        for f in ("oracle_compress", "oracle_quant_mxfp4", "oracle_quant_mxfp8", "oracle_index_scores",
-                  "oracle_select_topk", "oracle_index_topk", "oracle_attend"):
+        L.oracle_attend_stats.argtypes = ([_i64] * 8 + [_ptr, ctypes.c_double] + [_ptr] * 6
+                                          + [_i64, _i64, _ptr, _ptr, _ptr])
+        for f in ("oracle_compress", "oracle_quant_mxfp4", "oracle_quant_mxfp8",
+                  "oracle_quant_fp8_rows", "oracle_index_scores", "oracle_select_topk",
+                  "oracle_index_topk", "oracle_attend", "oracle_attend_stats"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -125,6 +129,22 @@ def quant_mxfp8(x):
     codes = np.zeros(shape, np.uint8)
     scales = np.zeros(shape[:-1] + (d // 32,), np.uint8)
     _check(lib().oracle_quant_mxfp8(rows, d, _p(x), _p(codes), _p(scales)), "quant_mxfp8")
+    return codes, scales
+
+
+def quant_fp8_rows(x):
+    """E4M3 encoding of rows of x [..., d] (d % 32 == 0) with ONE scale
+    exponent per row (reading R13d: the FP8 attention arithmetic; the
+    exponent rule of the MXFP8 runs applied to the whole row).  Returns
+    (codes [..., d] uint8, scales [..., d/32] uint8), the row's exponent
+    repeated in each of its d/32 scale bytes (a valid MXFP8 row)."""
+    x = _f64(x)
+    shape = x.shape
+    d = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    codes = np.zeros(shape, np.uint8)
+    scales = np.zeros(shape[:-1] + (d // 32,), np.uint8)
+    _check(lib().oracle_quant_fp8_rows(rows, d, _p(x), _p(codes), _p(scales)), "quant_fp8_rows")
     return codes, scales
 
 
@@ -200,12 +220,8 @@ def index_topk(q_idx, k_codes, k_scales, q_pos, m: int, W: int, k: int):
     return out, bool(exact.value)
 
 
-def attend(q, ck, cv, topk, rk, rv, raw_pos0: int, q_pos, m: int, W: int,
-           scale: float = 1.0) -> np.ndarray:
-    """One softmax over the selected (topk given: CSA) or all (topk None:
-    HCA) compressed candidates joined with the raw window w0..t
-    (jiwasawa.github.io post, CSA "Shared Key-Value MQA" and HCA parts, SWA
-    branch).  q [B,Tq,H,D], ck/cv [B,Nc,D], rk/rv [B,raw_len,D] -> o (fp64)."""
+def _attend(q, ck, cv, topk, rk, rv, raw_pos0: int, q_pos, m: int, W: int, scale: float,
+            stats: bool):
     q = _f64(q)
     ck = _f64(ck)
     cv = _f64(cv)
@@ -222,10 +238,46 @@ def attend(q, ck, cv, topk, rk, rv, raw_pos0: int, q_pos, m: int, W: int,
         tk = np.ascontiguousarray(topk, np.int32)
         k = tk.shape[2]
     o = np.zeros((B, Tq, H, D), np.float64)
-    _check(lib().oracle_attend(B, Tq, H, D, Nc, m, W, k, _p(qp), scale, _p(q), _p(ck),
-                               _p(cv), None if tk is None else _p(tk), _p(rk), _p(rv),
-                               raw_pos0, raw_len, _p(o)), "attend")
-    return o
+    am = np.zeros((B, Tq, H, D), np.float64) if stats else None
+    rm = np.zeros((B, Tq, H, D), np.float64) if stats else None
+    _check(lib().oracle_attend_stats(B, Tq, H, D, Nc, m, W, k, _p(qp), scale, _p(q), _p(ck),
+                                     _p(cv), None if tk is None else _p(tk), _p(rk), _p(rv),
+                                     raw_pos0, raw_len, _p(o),
+                                     None if am is None else _p(am),
+                                     None if rm is None else _p(rm)), "attend")
+    return (o, am, rm) if stats else o
+
+
+def attend(q, ck, cv, topk, rk, rv, raw_pos0: int, q_pos, m: int, W: int,
+           scale: float = 1.0) -> np.ndarray:
+    """One softmax over the selected (topk given: CSA) or all (topk None:
+    HCA) compressed candidates joined with the raw window w0..t
+    (jiwasawa.github.io post, CSA "Shared Key-Value MQA" and HCA parts, SWA
+    branch).  q [B,Tq,H,D], ck/cv [B,Nc,D], rk/rv [B,raw_len,D] -> o (fp64)."""
+    return _attend(q, ck, cv, topk, rk, rv, raw_pos0, q_pos, m, W, scale, False)
+
+
+def attend_stats(q, ck, cv, topk, rk, rv, raw_pos0: int, q_pos, m: int, W: int,
+                 scale: float = 1.0):
+    """attend, plus per output element the softmax-weighted means
+    amean = sum p|v| / sum p and rms = sqrt(sum p^2 v^2) / sum p over the
+    key list: (o, amean, rms), each [B,Tq,H,D] fp64."""
+    return _attend(q, ck, cv, topk, rk, rv, raw_pos0, q_pos, m, W, scale, True)
+
+
+def attend_fp8(q, ck, ck_scales, cv, cv_scales, topk, rk, rk_scales, rv, rv_scales,
+               raw_pos0: int, q_pos, m: int, W: int, scale: float = 1.0):
+    """Attention with FP8 arithmetic (reading R13d; ai-papers.net article,
+    hybrid attention section: most KV entries in FP8).  Keys and values of
+    the compressed entries and of the raw window are FP8 rows (codes and
+    scales as quant_fp8_rows writes them, decoded exactly); each query
+    head's row of q [B,Tq,H,D] is encoded the same way (one exponent per
+    head row) and decoded; then one exact softmax over the key list as in
+    attend.  Returns (o, amean, rms) as attend_stats."""
+    qc, qs = quant_fp8_rows(q)
+    return attend_stats(dequant_mxfp8(qc, qs), dequant_mxfp8(ck, ck_scales),
+                        dequant_mxfp8(cv, cv_scales), topk, dequant_mxfp8(rk, rk_scales),
+                        dequant_mxfp8(rv, rv_scales), raw_pos0, q_pos, m, W, scale)
 
 
 def set_threads(n: int) -> None:

@@ -194,15 +194,19 @@ static int e4m3_round(double y)       /* y >= 0; nearest, ties to even code */
     return best;
 }
 
-int oracle_quant_mxfp8(int64_t rows, int64_t d, const double *x,
-                       uint8_t *codes, uint8_t *scales)
+/* E4M3 encoding of rows of d values in runs of `run` values (run divides d), */
+/* each run with its own scale exponent by the rule above; scales get one    */
+/* byte per 32 values, the run's exponent repeated over the run.             */
+static int quant_e4m3_runs(int64_t rows, int64_t d, int64_t run, const double *x,
+                           uint8_t *codes, uint8_t *scales)
 {
-    if (rows < 0 || d <= 0 || d % 32 != 0) return 1;
+    if (rows < 0 || d <= 0 || d % 32 != 0 || run <= 0 || run % 32 != 0 || d % run != 0)
+        return 1;
     for (int64_t r = 0; r < rows; ++r) {
-        for (int64_t blk = 0; blk < d / 32; ++blk) {
-            const double *v = x + r * d + blk * 32;
+        for (int64_t blk = 0; blk < d / run; ++blk) {
+            const double *v = x + r * d + blk * run;
             double amax = 0.0;
-            for (int i = 0; i < 32; ++i)
+            for (int64_t i = 0; i < run; ++i)
                 if (fabs(v[i]) > amax) amax = fabs(v[i]);
             int e;
             if (amax == 0.0) {
@@ -214,15 +218,40 @@ int oracle_quant_mxfp8(int64_t rows, int64_t d, const double *x,
                 if (e < -127) e = -127;
                 if (e > 127) e = 127;
             }
-            scales[r * (d / 32) + blk] = (uint8_t)(e + 127);
-            for (int i = 0; i < 32; ++i) {
+            for (int64_t s32 = 0; s32 < run / 32; ++s32)
+                scales[r * (d / 32) + blk * (run / 32) + s32] = (uint8_t)(e + 127);
+            for (int64_t i = 0; i < run; ++i) {
                 double y = ldexp(fabs(v[i]), -e);
-                codes[r * d + blk * 32 + i] =
+                codes[r * d + blk * run + i] =
                     (uint8_t)(e4m3_round(y) | (signbit(v[i]) ? 0x80 : 0));
             }
         }
     }
     return 0;
+}
+
+int oracle_quant_mxfp8(int64_t rows, int64_t d, const double *x,
+                       uint8_t *codes, uint8_t *scales)
+{
+    return quant_e4m3_runs(rows, d, 32, x, codes, scales);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 2c: FP8 rows for FP8 attention arithmetic.                          */
+/*                                                                          */
+/* [P5, hybrid attention section]: most KV entries in FP8.  Reading R13d:   */
+/* when attention itself runs in FP8, every row it reads (compressed K and  */
+/* V entries, raw window rows, and each query head's row) is E4M3 with ONE  */
+/* scale exponent for the whole row of d values, by the same rule as the    */
+/* 32-value runs above (e = floor(log2 max|x|) - 8 over the row).  One      */
+/* exponent per key is what a product that contracts over keys (P V) can   */
+/* carry; the exponent is stored in each of the row's d/32 scale bytes, so  */
+/* the result is also a valid MXFP8 row and decodes as one.                 */
+/* ------------------------------------------------------------------------ */
+int oracle_quant_fp8_rows(int64_t rows, int64_t d, const double *x,
+                          uint8_t *codes, uint8_t *scales)
+{
+    return quant_e4m3_runs(rows, d, d, x, codes, scales);
 }
 
 /* Value of one MXFP8 element: (-1)^s * e4m3[code & 127] * 2^(scale-127). */
@@ -460,12 +489,19 @@ int oracle_index_topk(int64_t B, int64_t Tq, int64_t HI, int64_t dI,
 /* q [B,Tq,H,D], ck/cv [B,Nc,D], topk [B,Tq,k], rk/rv [B,raw_len,D] with    */
 /* raw row r at position raw_pos0 + r, o [B,Tq,H,D].                        */
 /* ------------------------------------------------------------------------ */
-int oracle_attend(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
-                  int64_t m, int64_t W, int64_t k, const int64_t *q_pos,
-                  double scale, const double *q, const double *ck,
-                  const double *cv, const int32_t *topk, const double *rk,
-                  const double *rv, int64_t raw_pos0, int64_t raw_len,
-                  double *o)
+/* As oracle_attend below; when amean / rms are given ([B,Tq,H,D] each), */
+/* they receive, per output element, the weighted means                   */
+/*     amean = sum_s p_s |v_s[c]| / sum_s p_s,                             */
+/*     rms   = sqrt(sum_s p_s^2 v_s[c]^2) / sum_s p_s,                     */
+/* of the softmax weights p_s over the key list: the scales on which a     */
+/* relative perturbation of each weight moves the output (its worst case   */
+/* and its root-mean-square for independent perturbations).                */
+int oracle_attend_stats(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                        int64_t m, int64_t W, int64_t k, const int64_t *q_pos,
+                        double scale, const double *q, const double *ck,
+                        const double *cv, const int32_t *topk, const double *rk,
+                        const double *rv, int64_t raw_pos0, int64_t raw_len,
+                        double *o, double *amean, double *rms)
 {
     for (int64_t i = 0; i < Tq; ++i) {
         int64_t t = q_pos[i];
@@ -523,8 +559,33 @@ int oracle_attend(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
                     acc += exp(l[s] - lmax) / den * vp[s][c];
                 ov[c] = acc;
             }
+            if (amean && rms) {
+                double *av = amean + ((b * Tq + i) * H + h) * D;
+                double *rv2 = rms + ((b * Tq + i) * H + h) * D;
+                for (int64_t c = 0; c < D; ++c) {
+                    double a = 0.0, r2 = 0.0;
+                    for (int64_t s = 0; s < n; ++s) {
+                        double p = exp(l[s] - lmax) / den;
+                        a += p * fabs(vp[s][c]);
+                        r2 += p * p * vp[s][c] * vp[s][c];
+                    }
+                    av[c] = a;
+                    rv2[c] = sqrt(r2);
+                }
+            }
         }
         free(kp); free(vp); free(l);
     }
     return err;
+}
+
+int oracle_attend(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                  int64_t m, int64_t W, int64_t k, const int64_t *q_pos,
+                  double scale, const double *q, const double *ck,
+                  const double *cv, const int32_t *topk, const double *rk,
+                  const double *rv, int64_t raw_pos0, int64_t raw_len,
+                  double *o)
+{
+    return oracle_attend_stats(B, Tq, H, D, Nc, m, W, k, q_pos, scale, q, ck, cv, topk,
+                               rk, rv, raw_pos0, raw_len, o, NULL, NULL);
 }
