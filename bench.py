@@ -42,7 +42,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp4_TFLOPs": 10100.0}
+PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "fp8_TFLOPs": 5000.0,
+        "fp4_TFLOPs": 10100.0}
 PIPE_SLICES = 8        # query slices of a pipelined CSA layer (selection | attention)
 
 # The HBM traffic recorded in profiles/traffic.json for a stage is reported
@@ -91,7 +92,10 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
     one vector per entry and raw token serves as key and value (only K is
     compressed, and the same buffers are passed as K and V).  kv_fmt
     "mxfp8": the compressed entries are encoded to MXFP8 after pooling (a
-    timed stage) and attention reads them in that form.  pipeline (bf16
+    timed stage) and attention reads them in that form.  kv_fmt "fp8": FP8
+    arithmetic -- the compressed entries and the raw K/V rows are encoded to
+    FP8 rows (one exponent per row; a timed stage) and attention runs on FP8
+    MFMA (queries encoded inside the call).  pipeline (bf16
     entries): a CSA layer's selection and attention run as one
     csa_index_attend call over 8 query slices on two streams."""
     import torch
@@ -118,7 +122,20 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
                 csa.hca_compress(raw["k"], raw["gk"], m, out=ck),
                 csa.hca_compress(raw["v"], raw["gv"], m, out=cv))
         stages.append(Stage(f"compress_m{m}", compress, bytes_=cbytes, peak_key="hbm_GBps"))
-        mx = None
+        mx = f8 = None
+        if kv_fmt == "fp8":
+            # FP8 rows: compressed K, V and the raw K, V rows the windows read
+            f8 = {n: (torch.empty(t.shape, dtype=torch.uint8, device=dev),
+                      torch.empty(t.shape[:-1], dtype=torch.int32, device=dev))
+                  for n, t in (("ck", ck), ("cv", cv), ("rk", raw["k"]), ("rv", rv))}
+
+            def encode(ck=ck, cv=cv, raw=raw, rv=rv, f8=f8):
+                for n, t in (("ck", ck), ("cv", cv), ("rk", raw["k"]), ("rv", rv)):
+                    csa.csa_quantize_fp8_rows(t, codes=f8[n][0], scales=f8[n][1])
+
+            stages.append(Stage("encode_fp8", encode,
+                                bytes_=2 * (w.Nc + T) * (D * 2 + D + 4),
+                                peak_key="hbm_GBps"))
         if kv_fmt == "mxfp8":
             kc8 = torch.empty((1, w.Nc, D), dtype=torch.uint8, device=dev)
             ks8 = torch.empty((1, w.Nc, D // 32), dtype=torch.uint8, device=dev)
@@ -167,7 +184,12 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
                                                    q_pos0=w.q_pos0, topk=topk, ws=iws),
                                 flops=2.0 * w.HI * w.dI * float(nc.sum()),
                                 peak_key="fp4_TFLOPs"))
-            if mx is None:
+            if f8 is not None:
+                attend = lambda q=q, f8=f8, topk=topk, o=o, w=w: csa.csa_attend_fp8(
+                    q, f8["ck"][0], f8["cv"][0], f8["ck"][1], f8["cv"][1], topk, f8["rk"][0],
+                    f8["rv"][0], f8["rk"][1], f8["rv"][1], m=w.m, W=w.W, q_pos0=w.q_pos0,
+                    raw_pos0=0, out=o)
+            elif mx is None:
                 attend = lambda q=q, ck=ck, cv=cv, topk=topk, raw=raw, rv=rv, o=o, w=w: \
                     csa.csa_attend(q, ck, cv, topk, raw["k"], rv, m=w.m, W=w.W, q_pos0=w.q_pos0,
                                    raw_pos0=0, out=o)
@@ -177,10 +199,16 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
                                          m=w.m, W=w.W, q_pos0=w.q_pos0, raw_pos0=0, out=o)
             stages.append(Stage("csa_attend", attend,
                                 flops=4.0 * H * D * float(nkeys.sum()),
-                                bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
+                                bytes_=2.0 * w.Tq * H * D * 2,
+                                peak_key="fp8_TFLOPs" if f8 is not None else "bf16_TFLOPs"))
         else:
             nkeys, nc = attend_keys(q_pos, m, W, 0)
-            if mx is None:
+            if f8 is not None:
+                attend = lambda q=q, f8=f8, o=o, w=w: csa.hca_attend_fp8(
+                    q, f8["ck"][0], f8["cv"][0], f8["ck"][1], f8["cv"][1], f8["rk"][0],
+                    f8["rv"][0], f8["rk"][1], f8["rv"][1], m=w.m, W=w.W, q_pos0=w.q_pos0,
+                    raw_pos0=0, out=o)
+            elif mx is None:
                 attend = lambda q=q, ck=ck, cv=cv, raw=raw, rv=rv, o=o, w=w: \
                     csa.hca_attend(q, ck, cv, raw["k"], rv, m=w.m, W=w.W, q_pos0=w.q_pos0,
                                    raw_pos0=0, out=o)
@@ -190,7 +218,8 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
                                          W=w.W, q_pos0=w.q_pos0, raw_pos0=0, out=o)
             stages.append(Stage("hca_attend", attend,
                                 flops=4.0 * H * D * float(nkeys.sum()),
-                                bytes_=2.0 * w.Tq * H * D * 2, peak_key="bf16_TFLOPs"))
+                                bytes_=2.0 * w.Tq * H * D * 2,
+                                peak_key="fp8_TFLOPs" if f8 is not None else "bf16_TFLOPs"))
     return stages, tokens, notes
 
 
@@ -220,6 +249,11 @@ def _decode_caches(w, dev, with_keys, shared_kv=False, kv_fmt="bf16"):
                 if not shared_kv:
                     rv[b].copy_(x["v"][0, -w.W:])
     out = {"ck": ck, "cv": cv, "rk": rk, "rv": rv}
+    if kv_fmt == "fp8":
+        # every K/V row the step reads, window included, as FP8 rows
+        for n in ("ck", "cv", "rk", "rv"):
+            out[n], out[n + "s"] = csa.csa_quantize_fp8_rows(out[n])
+        del ck, cv, rk, rv
     if kv_fmt == "mxfp8":
         out["ck"], out["cks"] = csa.csa_quantize_mxfp8(ck)
         if shared_kv:
@@ -243,13 +277,15 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
 
     sparse = w.kind == "csa"
     mx8 = kv_fmt == "mxfp8"
+    f8 = kv_fmt == "fp8"
     base = _decode_caches(w, dev, sparse, shared_kv, kv_fmt)
     q = I.draw_queries(w, device=dev)
     t = w.q_pos0
     nkeys, nc = attend_keys([t], w.m, w.W, w.k if sparse else 0)
     nwin = min(w.W, t + 1)
-    entry_bytes = (w.D + w.D // 32) if mx8 else w.D * 2
-    kv_bytes = ((float(nkeys[0]) - nwin) * entry_bytes + nwin * w.D * 2) * (1 if shared_kv else 2)
+    entry_bytes = (w.D + w.D // 32) if mx8 else (w.D + 4) if f8 else w.D * 2
+    win_bytes = (w.D + 4) if f8 else w.D * 2
+    kv_bytes = ((float(nkeys[0]) - nwin) * entry_bytes + nwin * win_bytes) * (1 if shared_kv else 2)
     qo_bytes = w.H * w.D * 2 * 2
     key_bytes = float(nc[0]) * (w.dI // 2 + w.dI // 32) if sparse else 0.0
     step_bytes = w.B * (kv_bytes + qo_bytes + key_bytes)
@@ -284,7 +320,11 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
 
         def attend():
             c = copies[state["i"] % ncopy]
-            if mx8:
+            if f8:
+                csa.csa_attend_fp8(q, c["ck"], c["cv"], c["cks"], c["cvs"], topk, c["rk"], c["rv"],
+                                   c["rks"], c["rvs"], m=w.m, W=w.W, q_pos0=t,
+                                   raw_pos0=t - w.W + 1, out=o, ws=aws)
+            elif mx8:
                 csa.csa_attend_mxfp8(q, c["ck"], c["cv"], c["cks"], c["cvs"], topk, c["rk"],
                                      c["rv"], m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1,
                                      out=o, ws=aws)
@@ -303,7 +343,11 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
 
         def attend():
             c = copies[state["i"] % ncopy]
-            if mx8:
+            if f8:
+                csa.hca_attend_fp8(q, c["ck"], c["cv"], c["cks"], c["cvs"], c["rk"], c["rv"],
+                                   c["rks"], c["rvs"], m=w.m, W=w.W, q_pos0=t,
+                                   raw_pos0=t - w.W + 1, out=o, ws=aws)
+            elif mx8:
                 csa.hca_attend_mxfp8(q, c["ck"], c["cv"], c["cks"], c["cvs"], c["rk"], c["rv"],
                                      m=w.m, W=w.W, q_pos0=t, raw_pos0=t - w.W + 1, out=o,
                                      ws=aws)
@@ -597,11 +641,11 @@ def stage_table(stages, stage_ms):
 
 def prefill_step_roofline(stages, ms_per_step):
     """Whole-step MFMA fraction: the time every stage's MFMA work would take
-    at its dtype's dense peak (bf16 attention, FP4 indexer), over the
+    at its dtype's dense peak (bf16 or FP8 attention, FP4 indexer), over the
     measured step time."""
     ideal = 0.0
     for st in stages:
-        if st.peak_key in ("bf16_TFLOPs", "fp4_TFLOPs"):
+        if st.peak_key in ("bf16_TFLOPs", "fp8_TFLOPs", "fp4_TFLOPs"):
             ideal += st.flops / (PEAK[st.peak_key] * 1e12)
         ideal += st.fp4_flops / (PEAK["fp4_TFLOPs"] * 1e12)
     return {"frac": ideal / (ms_per_step / 1e3), "ideal_ms": ideal * 1e3,
@@ -697,10 +741,11 @@ def main():
     ap.add_argument("--shared-kv", action="store_true",
                     help="one vector per compressed entry and raw token serves as key and "
                          "value (the same buffers passed as K and V); default: separate K, V")
-    ap.add_argument("--kv-format", default="bf16", choices=["bf16", "mxfp8"],
-                    help="storage of the compressed entries: bf16 (default) or MXFP8 E4M3 "
-                         "codes with a power-of-two scale per 32 values (the raw window "
-                         "stays bf16)")
+    ap.add_argument("--kv-format", default="bf16", choices=["bf16", "mxfp8", "fp8"],
+                    help="bf16 (default); mxfp8: compressed entries as MXFP8 E4M3 codes "
+                         "with a power-of-two scale per 32 values (window bf16, bf16 "
+                         "arithmetic); fp8: FP8 arithmetic, every K/V row (entries and "
+                         "window) an E4M3 row with one exponent, FP8 MFMA for QK and PV")
     ap.add_argument("--pipeline", action="store_true",
                     help="run a CSA prefill layer's selection and attention as one "
                          "csa_index_attend call, pipelined over query slices on two streams "
@@ -739,8 +784,10 @@ def main():
         dsteps, dwarm = args.decode_steps, min(dwarm, max(1, args.decode_steps))
     cpu = not args.no_cpu_baseline
     storage = {"kv": "one vector as key and value" if args.shared_kv else "separate K and V",
-               "kv_format": ("compressed entries MXFP8 (E4M3), window bf16"
-                             if args.kv_format == "mxfp8" else "bf16")}
+               "kv_format": {"mxfp8": "compressed entries MXFP8 (E4M3), window bf16",
+                             "fp8": "FP8 rows (E4M3, one exponent per row) for entries and "
+                                    "window; queries encoded per head row; FP8 MFMA",
+                             "bf16": "bf16"}[args.kv_format]}
 
     decode = {}
     if args.workload == "all":
@@ -764,7 +811,8 @@ def main():
     out = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"),
            "n_gpus": 1, "steps": rec.pop("steps"), "warmup": rec.pop("warmup"),
            "ms_per_step": rec.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1))"}
+           "vs_baseline": None, "dtype": "fp8" if args.kv_format == "fp8" else "bf16",
+           "data": "synthetic (seeded N(0,1))"}
     out.update(rec)
     if decode:
         out["decode"] = decode

@@ -79,6 +79,11 @@ _SIGS = {
                          + [_p, _p, _sz, _p], ctypes.c_int),
     "hca_attend_mxfp8": ([_i64] * 8 + [ctypes.c_float] + [_p] * 7 + [_i64, _i64]
                          + [_p, _p, _sz, _p], ctypes.c_int),
+    "csa_quantize_fp8_rows": ([ctypes.c_int, _i64, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "csa_attend_fp8": ([_i64] * 9 + [ctypes.c_float] + [_p] * 10 + [_i64, _i64]
+                       + [_p, _p, _sz, _p], ctypes.c_int),
+    "hca_attend_fp8": ([_i64] * 8 + [ctypes.c_float] + [_p] * 9 + [_i64, _i64]
+                       + [_p, _p, _sz, _p], ctypes.c_int),
 }
 
 
@@ -441,3 +446,54 @@ def csa_index_attend(q, q_idx, k_codes, k_scales, ck, cv, rk, rv, *, m: int, W: 
           raw_pos0, raw_len, _ptr(topk), _ptr(out), n_chunks, _ptr(ws), wsb, _stream(q, stream),
           _stream(q, aux_stream))
     return topk, out
+
+
+def csa_quantize_fp8_rows(x: torch.Tensor, codes=None, scales=None, stream=None):
+    """E4M3 encoding of rows of x [..., d] with one scale per row: (codes
+    [..., d] uint8, scales [...] int32 words holding the fp32 bits of 2^e)."""
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = _keep(torch.empty(x.shape, dtype=torch.uint8, device=x.device), stream)
+    if scales is None:
+        scales = _keep(torch.empty(x.shape[:-1], dtype=torch.int32, device=x.device), stream)
+    _call("csa_quantize_fp8_rows", _dt(x), rows, d, _ptr(x), _ptr(codes), _ptr(scales),
+          _stream(x, stream))
+    return codes, scales
+
+
+def csa_attend_fp8(q, ck, cv, ck_scales, cv_scales, topk, rk, rv, rk_scales, rv_scales, *,
+                   m: int, W: int, q_pos0: int, raw_pos0: int, scale: float = 1.0, out=None,
+                   ws=None, stream=None):
+    """csa_attend with FP8 arithmetic: compressed and window rows as FP8 rows
+    (codes [B,N,128] uint8, scale words [B,N] int32); q and output bf16."""
+    B, Tq, H, D = q.shape
+    Nc = ck.shape[1]
+    k = topk.shape[2]
+    raw_len = rk.shape[1]
+    ws, wsb = _workspace(ws, q.device, lambda: csa_attend_workspace(CSA_BF16, B, Tq, H, D, k, W),
+                          stream)
+    if out is None:
+        out = _keep(torch.empty_like(q), stream)
+    _call("csa_attend_fp8", B, Tq, H, D, Nc, m, W, k, q_pos0, scale, _ptr(q), _ptr(ck),
+          _ptr(cv), _ptr(ck_scales), _ptr(cv_scales), _ptr(topk), _ptr(rk), _ptr(rv),
+          _ptr(rk_scales), _ptr(rv_scales), raw_pos0, raw_len, _ptr(out), _ptr(ws), wsb,
+          _stream(q, stream))
+    return out
+
+
+def hca_attend_fp8(q, ck, cv, ck_scales, cv_scales, rk, rv, rk_scales, rv_scales, *, m: int,
+                   W: int, q_pos0: int, raw_pos0: int, scale: float = 1.0, out=None, ws=None,
+                   stream=None):
+    """hca_attend with FP8 arithmetic (see csa_attend_fp8)."""
+    B, Tq, H, D = q.shape
+    Nc = ck.shape[1]
+    raw_len = rk.shape[1]
+    ws, wsb = _workspace(ws, q.device,
+        lambda: hca_attend_workspace(CSA_BF16, B, Tq, H, D, Nc, m, W, q_pos0), stream)
+    if out is None:
+        out = _keep(torch.empty_like(q), stream)
+    _call("hca_attend_fp8", B, Tq, H, D, Nc, m, W, q_pos0, scale, _ptr(q), _ptr(ck), _ptr(cv),
+          _ptr(ck_scales), _ptr(cv_scales), _ptr(rk), _ptr(rv), _ptr(rk_scales),
+          _ptr(rv_scales), raw_pos0, raw_len, _ptr(out), _ptr(ws), wsb, _stream(q, stream))
+    return out

@@ -811,3 +811,106 @@ csa_status hca_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t
 }
 
 }  // extern "C"
+
+// ---- FP8 arithmetic (one exponent per row) ------------------------------------
+
+extern "C" {
+
+csa_status csa_quantize_fp8_rows(csa_dtype dt, int64_t rows, int64_t d, const void* x,
+                                 void* codes, void* scales, hipStream_t stream) {
+    const char* fn = "csa_quantize_fp8_rows";
+    if (csa_status s = check_dtype(dt, fn)) return s;
+    CHECK(rows >= 0, CSA_EINVAL, "%s: rows must be >= 0", fn);
+    CHECK(d == 32 || d == 64 || d == 128 || d == 256, CSA_EUNSUPPORTED,
+          "%s: d must be 32, 64, 128 or 256 (got %lld)", fn, (long long)d);
+    if (rows == 0) return ok();
+    CHECK(x && codes && scales, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(aligned16(x) && aligned16(codes), CSA_EINVAL, "%s: x and codes must be 16-byte aligned",
+          fn);
+    CHECK(((uintptr_t)scales & 3u) == 0, CSA_EINVAL, "%s: scales must be 4-byte aligned", fn);
+    return launched(csa::launch_quant_fp8_rows((int)dt, x, (uint8_t*)codes, (uint32_t*)scales,
+                                               rows, (int)d, stream),
+                    fn);
+}
+
+}  // extern "C"
+
+// bf16 queries and output, FP8 rows for every K/V source; D = 128.
+static csa_status fp8_args(const char* fn, int64_t B, int64_t Tq, int64_t H, int64_t D,
+                           const void* q, const void* ck, const void* cv, const void* cks,
+                           const void* cvs, const void* rk, const void* rv, const void* rks,
+                           const void* rvs, const void* o) {
+    if (csa_status s = attend_shape(fn, CSA_BF16, B, Tq, H, D)) return s;
+    CHECK(D == 128, CSA_EUNSUPPORTED, "%s: FP8 attention needs D = 128", fn);
+    CHECK(q && ck && cv && cks && cvs && rk && rv && rks && rvs && o, CSA_EINVAL,
+          "%s: null pointer", fn);
+    CHECK(aligned16(q) && aligned16(ck) && aligned16(cv) && aligned16(rk) && aligned16(rv) &&
+              aligned16(o), CSA_EINVAL, "%s: q, o and the code tensors must be 16-byte aligned",
+          fn);
+    CHECK(((uintptr_t)cks & 3u) == 0 && ((uintptr_t)cvs & 3u) == 0 &&
+              ((uintptr_t)rks & 3u) == 0 && ((uintptr_t)rvs & 3u) == 0,
+          CSA_EINVAL, "%s: scale tensors must be 4-byte aligned", fn);
+    return CSA_OK;
+}
+
+static csa::Fp8IO fp8_io(const void* q, const void* ck, const void* cv, const void* cks,
+                         const void* cvs, const void* rk, const void* rv, const void* rks,
+                         const void* rvs, void* o) {
+    return csa::Fp8IO{(const uint16_t*)q,  (const uint8_t*)ck,  (const uint8_t*)cv,
+                      (const uint8_t*)cks, (const uint8_t*)cvs, (const uint8_t*)rk,
+                      (const uint8_t*)rv,  (const uint8_t*)rks, (const uint8_t*)rvs,
+                      (uint16_t*)o};
+}
+
+extern "C" {
+
+csa_status csa_attend_fp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc, int64_t m,
+                          int64_t W, int64_t k, int64_t q_pos0, float scale, const void* q,
+                          const void* ck, const void* cv, const void* ck_scales,
+                          const void* cv_scales, const int32_t* topk, const void* rk,
+                          const void* rv, const void* rk_scales, const void* rv_scales,
+                          int64_t raw_pos0, int64_t raw_len, void* o, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    const char* fn = "csa_attend_fp8";
+    if (csa_status s = fp8_args(fn, B, Tq, H, D, q, ck, cv, ck_scales, cv_scales, rk, rv,
+                                rk_scales, rv_scales, o))
+        return s;
+    CHECK(topk, CSA_EINVAL, "%s: null pointer", fn);
+    CHECK(k >= 1 && k <= 2048, CSA_EINVAL, "%s: k must be in [1, 2048]", fn);
+    CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
+    if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
+    if (csa_status s = attend_ranges(fn, Nc, D, raw_len, k, W, q_pos0, Tq, m)) return s;
+    csa::AttendPlan p = csa::plan_attend(1, B, Tq, H, D, k + W);
+    CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
+          "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    return launched(csa::launch_attend_fp8(p, B, Tq, H, Nc, m, W, k, q_pos0, scale,
+                                           fp8_io(q, ck, cv, ck_scales, cv_scales, rk, rv,
+                                                  rk_scales, rv_scales, o),
+                                           topk, raw_pos0, raw_len, ws, stream),
+                    fn);
+}
+
+csa_status hca_attend_fp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc, int64_t m,
+                          int64_t W, int64_t q_pos0, float scale, const void* q, const void* ck,
+                          const void* cv, const void* ck_scales, const void* cv_scales,
+                          const void* rk, const void* rv, const void* rk_scales,
+                          const void* rv_scales, int64_t raw_pos0, int64_t raw_len, void* o,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "hca_attend_fp8";
+    if (csa_status s = fp8_args(fn, B, Tq, H, D, q, ck, cv, ck_scales, cv_scales, rk, rv,
+                                rk_scales, rv_scales, o))
+        return s;
+    CHECK(raw_len >= 0, CSA_EINVAL, "%s: raw_len must be >= 0", fn);
+    if (csa_status s = check_positions(fn, Tq, Nc, m, W, q_pos0, raw_pos0, raw_len)) return s;
+    if (csa_status s = attend_ranges(fn, Nc, D, raw_len, 0, W, q_pos0, Tq, m)) return s;
+    csa::AttendPlan p = csa::plan_attend(1, B, Tq, H, D, hca_max_keys(Tq, m, W, q_pos0));
+    CHECK(ws_bytes >= p.ws_bytes && (p.ws_bytes == 0 || (ws && aligned16(ws))), CSA_EINVAL,
+          "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, p.ws_bytes);
+    return launched(csa::launch_attend_fp8(p, B, Tq, H, Nc, m, W, 0, q_pos0, scale,
+                                           fp8_io(q, ck, cv, ck_scales, cv_scales, rk, rv,
+                                                  rk_scales, rv_scales, o),
+                                           nullptr, raw_pos0, raw_len, ws, stream),
+                    fn);
+}
+
+}  // extern "C"

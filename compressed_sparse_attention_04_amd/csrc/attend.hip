@@ -24,6 +24,7 @@
 // (log-sum-exp weights).
 #include "common.h"
 #include "internal.h"
+#include "attend_common.h"
 
 namespace csa {
 
@@ -56,8 +57,6 @@ __device__ __forceinline__ int64_t list_row(const KeyList& L, int64_t s, const i
     }
     return -((L.w0 + (s - L.nsel) - raw_pos0) + 2);
 }
-
-#define CSA_LDS __attribute__((address_space(3)))
 
 // Key rows of one tile are copied straight from global memory into LDS
 // (global_load_lds, 16 bytes per lane, lane-contiguous).  A row of D bf16 is
@@ -148,19 +147,6 @@ struct AttnArgs {
     TQ* o;
     RowStrides qs, cks, cvs, rks, rvs, os;
 };
-
-// Maximum / sum of a value over lanes l and l ^ 32 (a VALU lane swap, so it
-// does not queue behind LDS reads)
-__device__ __forceinline__ float max_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Per-wave attention engine.  An engine owns HPW heads of the block's
 // query token: their Q^T operand, running softmax state and accumulators,
@@ -365,19 +351,6 @@ struct Heads32 {
     }
 };
 
-// vmcnt wait (other counters untouched) leaving n copies in flight
-#define CSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x3f70 | ((n) & 15) | (((n) >> 4) << 14))
-
-// Block barrier without a memory fence: LDS writes are drained explicitly
-// and the copies each wave waited for are complete, so no outstanding copy
-// into another stage is waited for here.
-__device__ __forceinline__ void lds_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 template <int NW, int D, class E, bool SHARED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 k_attend_bf16(AttnArgs<uint16_t, uint16_t> A, const int32_t* __restrict__ topk,
@@ -521,18 +494,6 @@ struct Mx8Geom {
     static constexpr int BYTES = SC_OFF + 2 * ATT_KT * 4; // 8448
     static constexpr int NCOPY_CODES = CODE_B / 1024;     // 4 per tensor
 };
-
-// vmcnt wait leaving n (wave-uniform, 0 .. 18) copies in flight
-__device__ __forceinline__ void wait_vm_leaving(int n) {
-    switch (n) {
-#define CSA_WCASE(x) case x: CSA_WAIT_VM(x); break;
-        CSA_WCASE(1) CSA_WCASE(2) CSA_WCASE(3) CSA_WCASE(4) CSA_WCASE(5) CSA_WCASE(6)
-        CSA_WCASE(7) CSA_WCASE(8) CSA_WCASE(9) CSA_WCASE(10) CSA_WCASE(11) CSA_WCASE(12)
-        CSA_WCASE(13) CSA_WCASE(14) CSA_WCASE(15) CSA_WCASE(16) CSA_WCASE(17) CSA_WCASE(18)
-#undef CSA_WCASE
-        default: CSA_WAIT_VM(0); break;
-    }
-}
 
 // copies of this wave for one compressed tile
 template <int NW, bool SHARED>
@@ -895,6 +856,16 @@ k_attend_f32(AttnArgs<float, float> A, const int32_t* __restrict__ topk, int64_t
             if (d < D) oh[d] = acc[e] / den;
         }
     }
+}
+
+// merge of the bf16 split partials in ws (the layout plan_attend sizes) into o
+void launch_attend_combine(const void* ws, int64_t B, int64_t Tq, int H, int D, int splits,
+                           void* o, RowStrides os, hipStream_t st) {
+    const uint16_t* po = (const uint16_t*)ws;
+    const float* pml = (const float*)(po + B * Tq * splits * H * D);
+    hipLaunchKernelGGL(k_attend_combine<uint16_t>,
+                       dim3((unsigned)Tq, (unsigned)B, (unsigned)((H + 7) / 8)), dim3(256), 0, st,
+                       po, pml, (uint16_t*)o, os, Tq, H, D, splits);
 }
 
 AttendPlan plan_attend(int dt, int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t max_keys) {

@@ -80,5 +80,27 @@ hipError_t launch_attend_mx8(const AttendPlan& p, int64_t B, int64_t Tq, int64_t
 
 hipError_t launch_quant_mxfp8(int dt, const void* x, uint8_t* codes, uint8_t* scales,
                               int64_t rows, int d, hipStream_t st);
+// one scale per row of d values (d / 32 in {1, 2, 4, 8}): a 32-bit word per
+// row holding the fp32 power of two 2^e
+hipError_t launch_quant_fp8_rows(int dt, const void* x, uint8_t* codes, uint32_t* scales,
+                                 int64_t rows, int d, hipStream_t st);
+
+// merge of bf16 split partials (layout of plan_attend's workspace) into o
+void launch_attend_combine(const void* ws, int64_t B, int64_t Tq, int H, int D, int splits,
+                           void* o, RowStrides os, hipStream_t st);
+
+// FP8 arithmetic: bf16 queries (encoded per head row inside), FP8 rows for
+// compressed K/V and window K/V (E4M3 codes [rows][128] and one scale word
+// per row [rows], the fp32 bits of 2^e, dense), bf16 output; D = 128, the
+// plan of the bf16 kernel
+struct Fp8IO {
+    const uint16_t* q;
+    const uint8_t *ck, *cv, *cks, *cvs, *rk, *rv, *rks, *rvs;
+    uint16_t* o;
+};
+hipError_t launch_attend_fp8(const AttendPlan& p, int64_t B, int64_t Tq, int64_t H, int64_t Nc,
+                             int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                             const Fp8IO& io, const int32_t* topk, int64_t raw_pos0,
+                             int64_t raw_len, void* ws, hipStream_t st);
 
 }  // namespace csa

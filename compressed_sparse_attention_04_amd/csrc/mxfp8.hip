@@ -8,27 +8,22 @@
 // 448.  Inputs must be finite.
 #include "internal.h"
 #include "common.h"
+#include "e4m3.h"
 
 namespace csa {
 
-// E4M3 code of y (|y| may exceed 448: saturates).  With a = min(|y|, 448)
-// and E = max(floor(log2 a), -6), the code is 8 (E + 6) + rne(a * 2^(3-E)):
-// the rounded significand q is in [8, 16] for E > -6 (q = 16 carries into
-// the next exponent), and for E = -6 it is the subnormal step count 0 .. 8.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const float a = fminf(fabsf(y), 448.f);
-    int E = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;   // zero / subnormal: < -6
-    E = E < -6 ? -6 : E;
-    const float q = rintf(ldexpf(a, 3 - E));                  // exact scaling, then RNE
-    const uint32_t code = (uint32_t)(8 * (E + 6)) + (uint32_t)q;
-    return code | (__float_as_uint(y) >> 31 << 7);
-}
-
-template <typename T>
+// One thread per run of 32 values.  ROW = false: the run has its own scale,
+// one byte per run (MXFP8).  ROW = true: the ROWN = d / 32 consecutive
+// threads of a row (lanes of one wave, ROWN a power of two dividing 64)
+// share the row's maximum, so the whole row takes one scale, written once as
+// a 32-bit word holding the bits of the fp32 power of two 2^e (the byte
+// e + 127 in bits 23..30; zero for a zero row).
+template <typename T, int ROWN, bool ROW>
 __global__ void __launch_bounds__(256)
 k_quant_mxfp8(const T* __restrict__ x, uint8_t* __restrict__ codes,
-              uint8_t* __restrict__ scales, int64_t nblocks) {
+              void* __restrict__ scales, int64_t nblocks) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // nblocks is a multiple of ROWN: a row's threads are all present or all gone
     if (g >= nblocks) return;
     float v[32];
 #pragma unroll
@@ -41,6 +36,8 @@ k_quant_mxfp8(const T* __restrict__ x, uint8_t* __restrict__ codes,
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int o = 1; o < ROWN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
     // floor(log2 amax) from the exponent field; a subnormal or zero maximum
     // gives at most -127 - 8, clamped to -127
     int e = (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 - 8;
@@ -56,7 +53,11 @@ k_quant_mxfp8(const T* __restrict__ x, uint8_t* __restrict__ codes,
     u32x4* out = reinterpret_cast<u32x4*>(codes + g * 32);
     out[0] = u32x4{w[0], w[1], w[2], w[3]};
     out[1] = u32x4{w[4], w[5], w[6], w[7]};
-    scales[g] = (uint8_t)(e + 127);
+    if constexpr (ROW) {
+        if (g % ROWN == 0) static_cast<uint32_t*>(scales)[g / ROWN] = (uint32_t)(e + 127) << 23;
+    } else {
+        static_cast<uint8_t*>(scales)[g] = (uint8_t)(e + 127);
+    }
 }
 
 hipError_t launch_quant_mxfp8(int dt, const void* x, uint8_t* codes, uint8_t* scales,
@@ -65,11 +66,37 @@ hipError_t launch_quant_mxfp8(int dt, const void* x, uint8_t* codes, uint8_t* sc
     if (nb == 0) return hipSuccess;
     const dim3 grid((unsigned)((nb + 255) / 256));
     if (dt == 0)
-        hipLaunchKernelGGL(k_quant_mxfp8<float>, grid, dim3(256), 0, st, (const float*)x, codes,
-                           scales, nb);
+        hipLaunchKernelGGL((k_quant_mxfp8<float, 1, false>), grid, dim3(256), 0, st,
+                           (const float*)x, codes, (void*)scales, nb);
     else
-        hipLaunchKernelGGL(k_quant_mxfp8<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)x,
-                           codes, scales, nb);
+        hipLaunchKernelGGL((k_quant_mxfp8<uint16_t, 1, false>), grid, dim3(256), 0, st,
+                           (const uint16_t*)x, codes, (void*)scales, nb);
+    return hipGetLastError();
+}
+
+template <int ROWN>
+static void launch_rows(int dt, const void* x, uint8_t* codes, uint32_t* scales, int64_t nb,
+                        hipStream_t st) {
+    const dim3 grid((unsigned)((nb + 255) / 256));
+    if (dt == 0)
+        hipLaunchKernelGGL((k_quant_mxfp8<float, ROWN, true>), grid, dim3(256), 0, st,
+                           (const float*)x, codes, (void*)scales, nb);
+    else
+        hipLaunchKernelGGL((k_quant_mxfp8<uint16_t, ROWN, true>), grid, dim3(256), 0, st,
+                           (const uint16_t*)x, codes, (void*)scales, nb);
+}
+
+hipError_t launch_quant_fp8_rows(int dt, const void* x, uint8_t* codes, uint32_t* scales,
+                                 int64_t rows, int d, hipStream_t st) {
+    const int64_t nb = rows * (d / 32);
+    if (nb == 0) return hipSuccess;
+    switch (d / 32) {
+        case 1: launch_rows<1>(dt, x, codes, scales, nb, st); break;
+        case 2: launch_rows<2>(dt, x, codes, scales, nb, st); break;
+        case 4: launch_rows<4>(dt, x, codes, scales, nb, st); break;
+        case 8: launch_rows<8>(dt, x, codes, scales, nb, st); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 7
+#define CSA_ABI_VERSION 8
 
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -319,6 +319,64 @@ csa_status hca_attend_mxfp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t
                             const void *ck_scales, const void *cv_scales, const void *rk,
                             const void *rv, int64_t raw_pos0, int64_t raw_len, void *o,
                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_quantize_fp8_rows -- E4M3 encoding of rows with ONE scale exponent per
+ * row: the storage of every row that the FP8-arithmetic attention reads
+ * (ai-papers.net article, hybrid attention section: most KV entries in FP8).
+ * The exponent rule of csa_quantize_mxfp8 is applied to the whole row:
+ * e = floor(log2 max|row|) - 8, clamped to [-127, 127] (-127 for a zero row);
+ * each value x * 2^-e rounded to the nearest E4M3 value, ties to the even
+ * code, saturating at 448, bit 7 = x's sign bit.  The row's scale is one
+ * 32-bit word: the bits of the fp32 power of two 2^e, i.e. the E8M0 byte
+ * e + 127 in bits 23..30 and zeros elsewhere (all zero for a zero row).
+ *   x       [rows, d]   dt, finite values, 16-byte aligned
+ *   codes   [rows, d]   uint8, 16-byte aligned
+ *   scales  [rows]      uint32 words, 4-byte aligned
+ * Requires d in {32, 64, 128, 256} (else CSA_EUNSUPPORTED).  Caller-owned
+ * device memory; nothing is allocated.
+ */
+csa_status csa_quantize_fp8_rows(csa_dtype dt, int64_t rows, int64_t d, const void *x,
+                                 void *codes, void *scales, hipStream_t stream);
+
+/*
+ * csa_attend_fp8 / hca_attend_fp8 -- csa_attend / hca_attend with FP8
+ * arithmetic (ai-papers.net article, hybrid attention section: most KV
+ * entries in FP8; jiwasawa.github.io post: shared-KV MQA over the selected
+ * entries, dense HCA, the SWA window).  Every key and value row, compressed
+ * entries and raw window rows alike, is an FP8 row as csa_quantize_fp8_rows
+ * writes it, and each query head's row is encoded the same way inside the
+ * call; the scores are the exact products of those values (scaled FP8 MFMA,
+ * fp32 accumulation) and the softmax runs in fp32.  The probabilities, times
+ * each value row's own scale, are rounded to E4M3 for the value product (a
+ * relative error of at most 2^-4 per probability while p * 2^(e_v - E) >=
+ * 2^-12, E the largest value exponent among the 64 keys it is processed
+ * with); the softmax denominators add the unrounded probabilities.
+ *   q, o                 [B, Tq, H, 128]  bf16, 16-byte aligned
+ *   ck, cv               [B, Nc, 128]     uint8 E4M3 codes, 16-byte aligned
+ *   ck_scales, cv_scales [B, Nc]          uint32 scale words, 4-byte aligned
+ *   rk, rv               [B, raw_len, 128] codes; rk_scales, rv_scales
+ *                        [B, raw_len] words, as for the compressed rows
+ *   topk as for csa_attend; ws of at least csa_attend_workspace /
+ *   hca_attend_workspace (CSA_BF16, same sizes) bytes.
+ * Requires D = 128 and H in {32, 64, 128, 256}; other arguments and errors
+ * as for csa_attend / hca_attend.
+ */
+csa_status csa_attend_fp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                          int64_t m, int64_t W, int64_t k, int64_t q_pos0, float scale,
+                          const void *q, const void *ck, const void *cv,
+                          const void *ck_scales, const void *cv_scales,
+                          const int32_t *topk, const void *rk, const void *rv,
+                          const void *rk_scales, const void *rv_scales, int64_t raw_pos0,
+                          int64_t raw_len, void *o, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+csa_status hca_attend_fp8(int64_t B, int64_t Tq, int64_t H, int64_t D, int64_t Nc,
+                          int64_t m, int64_t W, int64_t q_pos0, float scale,
+                          const void *q, const void *ck, const void *cv,
+                          const void *ck_scales, const void *cv_scales, const void *rk,
+                          const void *rv, const void *rk_scales, const void *rv_scales,
+                          int64_t raw_pos0, int64_t raw_len, void *o, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
 
 /*
  * csa_index_attend -- csa_index_topk followed by csa_attend over the same

@@ -43,7 +43,8 @@ def test_exports_every_declared_symbol(L):
     assert {"hca_compress", "csa_index_topk", "csa_attend", "hca_attend",
             "csa_quantize_mxfp4", "hca_append", "csa_quantize_mxfp8", "csa_attend_mxfp8",
             "hca_attend_mxfp8", "csa_layer_schedule", "csa_stack_workspace",
-            "csa_stack_attend", "csa_index_attend_workspace", "csa_index_attend"} <= set(names)
+            "csa_stack_attend", "csa_index_attend_workspace", "csa_index_attend",
+            "csa_quantize_fp8_rows", "csa_attend_fp8", "hca_attend_fp8"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGS), "binding and header disagree"
@@ -51,7 +52,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version(L):
     want = int(re.search(r"#define CSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert L.csa_abi_version() == want == 7
+    assert L.csa_abi_version() == want == 8
 
 
 def err(L):
@@ -143,6 +144,33 @@ def test_mxfp8_rejects(L):
     st = L.csa_attend_mxfp8(1, 1, 128, 128, 300, 4, 128, 16, 1199, 1.0, P, P, P, S, S, P, P, P,
                             1073, 127, P, None, 0, None)
     assert st == EINVAL and "raw rows" in err(L)
+
+
+def test_fp8_rejects(L):
+    assert L.csa_quantize_fp8_rows(1, 4, 96, P, P, P, None) == EUNSUP          # d
+    assert L.csa_quantize_fp8_rows(1, 4, 64, P, None, P, None) == EINVAL       # null
+    assert L.csa_quantize_fp8_rows(5, 4, 64, P, P, P, None) == EINVAL          # dtype
+    assert L.csa_quantize_fp8_rows(1, 4, 64, ctypes.c_void_p(0x1008), P, P, None) == EINVAL
+    assert L.csa_quantize_fp8_rows(1, 0, 64, None, None, None, None) == 0      # nothing to do
+    S = ctypes.c_void_p(0x1004)                        # 4-byte aligned scales are fine
+    def hca(D=128, H=128, cks=S, rvs=S, q=P, p0=1072, rl=128):
+        return L.hca_attend_fp8(1, 1, H, D, 300, 4, 128, 1199, 1.0, q, P, P, cks, S, P, P, S,
+                                rvs, p0, rl, P, None, 0, None)
+    assert hca(D=64) == EUNSUP and "D = 128" in err(L)
+    assert hca(H=96) == EUNSUP
+    assert hca(cks=ctypes.c_void_p(0x1002)) == EINVAL and "4-byte" in err(L)
+    assert hca(rvs=None) == EINVAL and "null" in err(L)
+    assert hca(q=None) == EINVAL and "null" in err(L)
+    assert hca(p0=1073, rl=127) == EINVAL and "raw rows" in err(L)
+    def csa(topk=P, k=16):
+        return L.csa_attend_fp8(1, 1, 128, 128, 300, 4, 128, k, 1199, 1.0, P, P, P, S, S, topk,
+                                P, P, S, S, 1072, 128, P, None, 0, None)
+    assert csa(topk=None) == EINVAL and "null" in err(L)
+    assert csa(k=0) == EINVAL and csa(k=4096) == EINVAL
+    # the split plan of a decode row needs a workspace
+    st = L.hca_attend_fp8(4, 1, 128, 128, 8191, 128, 128, 1048575, 1.0, P, P, P, S, S, P, P, S,
+                          S, 1048448, 128, P, None, 0, None)
+    assert st == EINVAL and "workspace" in err(L)
 
 
 def test_index_attend_rejects(L):
