@@ -197,7 +197,7 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
                 attend = lambda q=q, mx=mx, topk=topk, raw=raw, rv=rv, o=o, w=w: \
                     csa.csa_attend_mxfp8(q, mx[0], mx[1], mx[2], mx[3], topk, raw["k"], rv,
                                          m=w.m, W=w.W, q_pos0=w.q_pos0, raw_pos0=0, out=o)
-            stages.append(Stage("csa_attend", attend,
+            stages.append(Stage("csa_attend_fp8" if f8 is not None else "csa_attend", attend,
                                 flops=4.0 * H * D * float(nkeys.sum()),
                                 bytes_=2.0 * w.Tq * H * D * 2,
                                 peak_key="fp8_TFLOPs" if f8 is not None else "bf16_TFLOPs"))
@@ -216,7 +216,7 @@ def setup_prefill(dev, layers, shared_kv=False, kv_fmt="bf16", pipeline=False):
                 attend = lambda q=q, mx=mx, raw=raw, rv=rv, o=o, w=w: \
                     csa.hca_attend_mxfp8(q, mx[0], mx[1], mx[2], mx[3], raw["k"], rv, m=w.m,
                                          W=w.W, q_pos0=w.q_pos0, raw_pos0=0, out=o)
-            stages.append(Stage("hca_attend", attend,
+            stages.append(Stage("hca_attend_fp8" if f8 is not None else "hca_attend", attend,
                                 flops=4.0 * H * D * float(nkeys.sum()),
                                 bytes_=2.0 * w.Tq * H * D * 2,
                                 peak_key="fp8_TFLOPs" if f8 is not None else "bf16_TFLOPs"))
@@ -335,7 +335,8 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
 
         stages.append(Stage("index_topk", index, flops=2.0 * w.HI * w.dI * float(nc[0]) * w.B,
                             bytes_=w.B * key_bytes, peak_key="hbm_GBps"))
-        stages.append(Stage("csa_attend", attend, flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
+        stages.append(Stage("csa_attend_fp8" if f8 else "csa_attend", attend,
+                            flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
                             bytes_=w.B * (kv_bytes + qo_bytes), peak_key="hbm_GBps"))
     else:
         aws = torch.empty(max(1, csa.hca_attend_workspace(1, w.B, 1, w.H, w.D, w.Nc, w.m, w.W, t)),
@@ -356,7 +357,8 @@ def setup_decode(dev, w, min_bytes=600e6, shared_kv=False, kv_fmt="bf16"):
                                raw_pos0=t - w.W + 1, out=o, ws=aws)
             state["i"] += 1
 
-        stages.append(Stage("hca_attend", attend, flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
+        stages.append(Stage("hca_attend_fp8" if f8 else "hca_attend", attend,
+                            flops=4.0 * w.H * w.D * float(nkeys[0]) * w.B,
                             bytes_=w.B * (kv_bytes + qo_bytes), peak_key="hbm_GBps"))
     return stages, w.B, {"cache_copies": ncopy, "step_bytes": step_bytes}
 
@@ -409,6 +411,11 @@ def setup_stack_decode(dev, n_layers=61, B=16):
 
 
 # --------------------------------------------------------------- CPU baseline
+def note(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def oracle_threads():
     """Host threads for the oracle: OMP_NUM_THREADS when set, else every core
     this process may run on."""
@@ -477,11 +484,15 @@ def _cpu_prefill(layers, threads):
     return per_token, "; ".join(desc)
 
 
-def _cpu_decode(w, S):
+def _cpu_decode(w, S, fp8=False):
     """Oracle seconds of the decode step of S sequences of workload w (every
     candidate scored and selected; attention over the kept entries or all
     candidates plus the window).  Cache rows that the step does not read are
-    left untouched (zero pages), the rows it reads are drawn."""
+    left untouched (zero pages), the rows it reads are drawn.  fp8: the
+    oracle's FP8 attention (attend_fp8: every key and value row decoded from
+    its FP8 encoding, the queries encoded per head row, exact attention),
+    here spelled through its pieces so that only the rows the step reads are
+    encoded (untimed); the query encoding and the attention are timed."""
     import torch
 
     import oracle
@@ -495,6 +506,7 @@ def _cpu_decode(w, S):
     nc = int(n_cand([t], w.m, w.W)[0])
     tk = None
     el = 0.0
+    fp8_rows = lambda a: oracle.dequant_mxfp8(*oracle.quant_fp8_rows(a)) if fp8 else a
     if w.kind == "csa":
         kc, ks = oracle.quant_mxfp4(f64(I.draw_indexer_keys(ws)))
         qi = f64(I.draw_indexer_queries(ws))
@@ -503,23 +515,30 @@ def _cpu_decode(w, S):
         el += time.perf_counter() - t0
         ck = np.zeros((S, w.Nc, w.D))
         cv = np.zeros((S, w.Nc, w.D))
-        vals_k = f64(I.draw_cache(ws, "ck", w.k))
-        vals_v = f64(I.draw_cache(ws, "cv", w.k))
+        vals_k = fp8_rows(f64(I.draw_cache(ws, "ck", w.k)))
+        vals_v = fp8_rows(f64(I.draw_cache(ws, "cv", w.k)))
         for b in range(S):
             sel = tk[b, 0][tk[b, 0] >= 0]
             ck[b, sel] = vals_k[b, :len(sel)]
             cv[b, sel] = vals_v[b, :len(sel)]
     else:
-        ck = f64(I.draw_cache(ws, "ck", nc))
-        cv = f64(I.draw_cache(ws, "cv", nc))
+        ck = fp8_rows(f64(I.draw_cache(ws, "ck", nc)))
+        cv = fp8_rows(f64(I.draw_cache(ws, "cv", nc)))
+    if fp8:
+        rk, rv = fp8_rows(rk), fp8_rows(rv)
+        t0 = time.perf_counter()
+        q = fp8_rows(q)
+        oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
+        return el + time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.attend(q, ck, cv, tk, rk, rv, t - w.W + 1, [t], w.m, w.W)
     return el + time.perf_counter() - t0
 
 
-def cpu_baseline(name, n_layers=61):
+def cpu_baseline(name, n_layers=61, fp8=False):
     """The oracle, unchanged, timed on a bounded sample of the same workload,
-    with every host thread and with one thread."""
+    with every host thread and with one thread (fp8: the FP8 arithmetic's
+    attention for the decode workloads)."""
     import oracle
     from compressed_sparse_attention_04_amd import inputs as I
 
@@ -527,6 +546,7 @@ def cpu_baseline(name, n_layers=61):
     threads = oracle_threads()
     res = {}
     for th in sorted({threads, 1}, reverse=True):
+        note(f"oracle baseline of {name}{' (FP8)' if fp8 else ''} at {th} thread(s)")
         oracle.set_threads(th)
         if name in ("pair_prefill_128k", "csa_prefill_32k"):
             layers = [I.PAIR_CSA_128K, I.PAIR_HCA_128K] if name == "pair_prefill_128k" \
@@ -545,10 +565,12 @@ def cpu_baseline(name, n_layers=61):
                        f"sequence, scaled to {ncsa} CSA + {n_layers - ncsa} HCA layers")
         else:
             w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
-            S = min(th, w.B)
-            res[th] = (S / _cpu_decode(w, S),
+            # (the FP8 HCA sample encodes every compressed row it reads)
+            S = min(th, w.B, 4 if fp8 and w.kind == "hca" else w.B)
+            res[th] = (S / _cpu_decode(w, S, fp8),
                        f"full decode step of {S} of the {w.B} sequences (every candidate "
-                       "scored and selected where the layer selects)")
+                       "scored and selected where the layer selects"
+                       + ("; FP8 attention" if fp8 else "") + ")")
     oracle.set_threads(threads)
     v, sample = res[threads]
     out = {"value": v, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample}
@@ -671,6 +693,7 @@ def run_prefill(dev, name, args, steps, warmup):
         wl["csa_schedule"] = (f"selection and attention pipelined over {PIPE_SLICES} query "
                               "slices on two streams (csa_index_attend)")
     ms, stage_ms = time_stages(stages, steps, warmup)
+    note(f"{name}: {ms:.2f} ms per step")
     traffic_ok = not args.shared_kv and args.kv_format == "bf16"
     rec = {"metric": "prefill tokens/s", "value": round(tokens / (ms / 1e3), 1),
            "unit": "tokens/s", "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
@@ -681,7 +704,7 @@ def run_prefill(dev, name, args, steps, warmup):
     return rec
 
 
-def run_decode(dev, name, args, steps, warmup):
+def run_decode(dev, name, args, steps, warmup, kv_fmt=None):
     import torch
     from compressed_sparse_attention_04_amd import inputs as I
     if name == "stack_decode_1m":
@@ -694,18 +717,21 @@ def run_decode(dev, name, args, steps, warmup):
         metric = "1M-ctx decode tokens/s/GPU (attention stack)"
     else:
         w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
-        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv,
-                                             kv_fmt=args.kv_format)
+        kv_fmt = kv_fmt or args.kv_format
+        stages, tokens, notes = setup_decode(dev, w, shared_kv=args.shared_kv, kv_fmt=kv_fmt)
         wl = {"workload": name.replace("_1m", "") + "_1m_ctx", "context": w.T,
               "batch": w.B, "heads": w.H, "kv_heads": 1, "head_dim": w.D, "m": w.m,
               "top_k": w.k if w.kind == "csa" else None, "window": w.W}
         metric = "1M-ctx decode tokens/s/GPU"
     ms, stage_ms = time_stages(stages, steps, warmup)
-    traffic_ok = not args.shared_kv and args.kv_format == "bf16"
+    note(f"{name} ({kv_fmt or args.kv_format}): {ms * 1e3:.1f} us per step")
+    fmt = kv_fmt or args.kv_format
+    traffic_ok = not args.shared_kv and fmt in ("bf16", "fp8")
+    tname = name + ("_fp8" if fmt == "fp8" else "")
     hbm = notes["step_bytes"] / (ms / 1e3) / 1e9
     rec = {"metric": metric, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "config": wl,
-           "roofline": kernel_roofline(stages, stage_ms, name, traffic_ok)}
+           "roofline": kernel_roofline(stages, stage_ms, tname, traffic_ok)}
     rec["roofline"]["step"] = {"frac": hbm / PEAK["hbm_GBps"], "achieved_GBps": hbm,
                                "scope": "whole step: algorithmic bytes over the measured "
                                         "step time"}
@@ -790,9 +816,19 @@ def main():
                              "bf16": "bf16"}[args.kv_format]}
 
     decode = {}
+    fp8_decode = args.workload == "all" and args.kv_format == "bf16" and not args.shared_kv
     if args.workload == "all":
         for name in ("hca_decode_1m", "csa_decode_1m"):
             decode[name] = run_decode(dev, name, args, dsteps, dwarm)
+        if fp8_decode:
+            # the same decode steps with FP8 arithmetic (entries and window as
+            # FP8 rows, FP8 MFMA for QK and PV)
+            for name in ("hca_decode_1m", "csa_decode_1m"):
+                r = run_decode(dev, name, args, dsteps, dwarm, kv_fmt="fp8")
+                r["config"]["kv_format"] = ("FP8 rows (E4M3, one power-of-two scale per row) "
+                                            "for entries and window; FP8 MFMA for QK and PV")
+                r["dtype"] = "fp8"
+                decode[name + "_fp8"] = r
         rec = run_prefill(dev, "pair_prefill_128k", args, steps, warmup)
         name = "pair_prefill_128k"
     elif args.workload.endswith("decode_1m"):
@@ -803,9 +839,10 @@ def main():
         rec = run_prefill(dev, name, args, steps, warmup)
     rec["config"].update(storage)
     if cpu:
-        rec["cpu_baseline"] = cpu_baseline(name, n_layers=args.layers)
+        rec["cpu_baseline"] = cpu_baseline(name, n_layers=args.layers,
+                                           fp8=args.kv_format == "fp8")
         for dn, d in decode.items():
-            d["cpu_baseline"] = cpu_baseline(dn)
+            d["cpu_baseline"] = cpu_baseline(dn.replace("_fp8", ""), fp8=dn.endswith("_fp8"))
     else:
         rec["cpu_baseline"] = None
     out = {"metric": rec.pop("metric"), "value": rec.pop("value"), "unit": rec.pop("unit"),

@@ -722,9 +722,12 @@ k_attend_mx8(AttnArgs<uint16_t, uint8_t> A, const uint8_t* __restrict__ cks,
 // Log-sum-exp merge of the split partials.  Grid (query, sequence, head
 // group of 8); D/4 threads per head, 4 dims each.  The threads of a head
 // read the splits' maxima and sums in parallel (at most 64 splits) and
-// share the weights through LDS; the accumulator loads are unrolled so
-// several are in flight.
+// share the weights through LDS.  The partial outputs of the first
+// CMB_PRE splits are loaded together with the maxima and sums (they do not
+// depend on the weights), so a decode merge is one round trip to memory;
+// further splits are loaded in batches of 8.
 constexpr int CMB_MAXS = 64;
+constexpr int CMB_PRE = 16;
 
 template <typename TO>
 __global__ void __launch_bounds__(256)
@@ -737,6 +740,14 @@ k_attend_combine(const uint16_t* __restrict__ po, const float* __restrict__ pml,
     const int h = blockIdx.z * 8 + hh;
     const bool live = threadIdx.x < 8 * per_head && h < H;
     const int64_t rec0 = (b * Tq + i) * splits * (int64_t)H + (live ? h : 0);
+    const int d0 = t * 4;
+    const uint16_t* base = po + rec0 * D + d0;
+    const int64_t sstride = (int64_t)H * D;
+    u32x2 pre[CMB_PRE];
+#pragma unroll
+    for (int u = 0; u < CMB_PRE; ++u)
+        pre[u] = live && u < splits ? *reinterpret_cast<const u32x2*>(base + u * sstride)
+                                    : u32x2{0u, 0u};
     // maxima and sums of the splits t, t + per_head, ...
     float ms[CMB_MAXS / 16], ls[CMB_MAXS / 16];
     float M = -INFINITY;
@@ -767,12 +778,17 @@ k_attend_combine(const uint16_t* __restrict__ po, const float* __restrict__ pml,
     }
     __syncthreads();
     if (!live) return;
-    const int d0 = t * 4;
-    const uint16_t* base = po + rec0 * D + d0;
-    const int64_t sstride = (int64_t)H * D;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < CMB_PRE; ++u) {
+        const float w = u < splits ? sw[hh][u] : 0.f;
+        a[0] += bf16_bits_to_f32(pre[u][0] & 0xffffu) * w;
+        a[1] += bf16_bits_to_f32(pre[u][0] >> 16) * w;
+        a[2] += bf16_bits_to_f32(pre[u][1] & 0xffffu) * w;
+        a[3] += bf16_bits_to_f32(pre[u][1] >> 16) * w;
+    }
     constexpr int U = 8;
-    for (int s0 = 0; s0 < splits; s0 += U) {
+    for (int s0 = CMB_PRE; s0 < splits; s0 += U) {
         u32x2 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)

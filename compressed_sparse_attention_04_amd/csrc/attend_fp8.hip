@@ -277,6 +277,53 @@ struct Fp8Heads {
         }
     }
 
+    // V^T operands of the tile (kept in rd until the PV product)
+    i32x2 rd[4][4];
+    __device__ __forceinline__ void read_v(const CSA_LDS uint8_t* stg) {
+        using G = F8Geom;
+        const int lane = threadIdx.x % 64, h = lane >> 5;
+        // V^T operands by transposing reads: group g = lane / 16 reads dims
+        // 32b + 16 (g % 2) + 0..15 of 8 keys per read; lane 2j + a of the
+        // group points at key 16x + 4h + 8 (j / 4) + j % 4, bytes 8a..8a+7.
+        // The swizzle of those keys does not depend on x, so the four reads
+        // of one dim block are one address 16 key rows (2 KB) apart.  They
+        // are issued together in one asm block that waits for them itself
+        // (the compiler cannot always tell these reads from the copies in
+        // flight into other stages, and would wait for every copy).
+        const int gi = lane & 15, j = gi >> 1, a = gi & 1, c16 = (lane >> 4) & 1;
+        const int key0 = 4 * h + 8 * (j >> 2) + (j & 3);
+        const int sw = f8_swz(key0);
+        const uint32_t vbase =
+            (uint32_t)(uintptr_t)(stg + G::CODE_B + key0 * G::ROWB + 8 * a);
+        const uint32_t v0 = vbase + (uint32_t)(((0 + c16) ^ sw) * 16);
+        const uint32_t v1 = vbase + (uint32_t)(((2 + c16) ^ sw) * 16);
+        const uint32_t v2 = vbase + (uint32_t)(((4 + c16) ^ sw) * 16);
+        const uint32_t v3 = vbase + (uint32_t)(((6 + c16) ^ sw) * 16);
+        asm volatile(
+            "ds_read_b64_tr_b8 %0, %16\n\t"
+            "ds_read_b64_tr_b8 %1, %16 offset:2048\n\t"
+            "ds_read_b64_tr_b8 %2, %16 offset:4096\n\t"
+            "ds_read_b64_tr_b8 %3, %16 offset:6144\n\t"
+            "ds_read_b64_tr_b8 %4, %17\n\t"
+            "ds_read_b64_tr_b8 %5, %17 offset:2048\n\t"
+            "ds_read_b64_tr_b8 %6, %17 offset:4096\n\t"
+            "ds_read_b64_tr_b8 %7, %17 offset:6144\n\t"
+            "ds_read_b64_tr_b8 %8, %18\n\t"
+            "ds_read_b64_tr_b8 %9, %18 offset:2048\n\t"
+            "ds_read_b64_tr_b8 %10, %18 offset:4096\n\t"
+            "ds_read_b64_tr_b8 %11, %18 offset:6144\n\t"
+            "ds_read_b64_tr_b8 %12, %19\n\t"
+            "ds_read_b64_tr_b8 %13, %19 offset:2048\n\t"
+            "ds_read_b64_tr_b8 %14, %19 offset:4096\n\t"
+            "ds_read_b64_tr_b8 %15, %19 offset:6144\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(rd[0][0]), "=&v"(rd[0][1]), "=&v"(rd[0][2]), "=&v"(rd[0][3]),
+              "=&v"(rd[1][0]), "=&v"(rd[1][1]), "=&v"(rd[1][2]), "=&v"(rd[1][3]),
+              "=&v"(rd[2][0]), "=&v"(rd[2][1]), "=&v"(rd[2][2]), "=&v"(rd[2][3]),
+              "=&v"(rd[3][0]), "=&v"(rd[3][1]), "=&v"(rd[3][2]), "=&v"(rd[3][3])
+            : "v"(v0), "v"(v1), "v"(v2), "v"(v3));
+    }
+
     // softmax of the tile (the first nvalid keys count), P folded with the
     // V exponents and rounded to E4M3, then O^T += V^T P^T
     __device__ __forceinline__ void rest(const CSA_LDS uint8_t* stg, int nvalid, float scale_log2) {
@@ -366,33 +413,6 @@ struct Fp8Heads {
             pop[w] = __builtin_bit_cast(int, pk);
         }
         const int psc = (int)(emax >> 23);
-        // V^T operands by transposing reads: group g = lane / 16 reads dims
-        // 32b + 16 (g % 2) + 0..15 of 8 keys per read; lane 2j + a of the
-        // group points at key 16x + 4h + 8 (j / 4) + j % 4, bytes 8a..8a+7.
-        // The swizzle of those keys does not depend on x, so the four reads
-        // of one dim block are one address 16 key rows (2 KB) apart.  They
-        // are issued together in one asm block that waits for them itself
-        // (the compiler cannot always tell these reads from the copies in
-        // flight into other stages, and would wait for every copy).
-        const int gi = lane & 15, j = gi >> 1, a = gi & 1, c16 = (lane >> 4) & 1;
-        const int key0 = 4 * h + 8 * (j >> 2) + (j & 3);
-        const int sw = f8_swz(key0);
-        const uint32_t vbase =
-            (uint32_t)(uintptr_t)(stg + G::CODE_B + key0 * G::ROWB + 8 * a);
-        i32x2 rd[4][4];
-#define CSA_TR8(B)                                                                          \
-        asm volatile("ds_read_b64_tr_b8 %0, %4\n\t"                                          \
-                     "ds_read_b64_tr_b8 %1, %4 offset:2048\n\t"                               \
-                     "ds_read_b64_tr_b8 %2, %4 offset:4096\n\t"                               \
-                     "ds_read_b64_tr_b8 %3, %4 offset:6144\n\t"                               \
-                     "s_waitcnt lgkmcnt(0)"                                                 \
-                     : "=&v"(rd[B][0]), "=&v"(rd[B][1]), "=&v"(rd[B][2]), "=&v"(rd[B][3])     \
-                     : "v"(vbase + (uint32_t)((((2 * B + c16) ^ sw) * 16))));
-        CSA_TR8(0)
-        CSA_TR8(1)
-        CSA_TR8(2)
-        CSA_TR8(3)
-#undef CSA_TR8
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const i32x8 vop = {rd[b][0][0], rd[b][0][1], rd[b][1][0], rd[b][1][1],
@@ -535,6 +555,9 @@ k_attend_fp8(Fp8IO A, const int32_t* __restrict__ topk, float* __restrict__ part
         lds_barrier();
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
         eng.qk((const CSA_LDS uint8_t*)cur);
+        __builtin_amdgcn_sched_barrier(0);
+        // the V^T reads wait while the QK products run
+        eng.read_v((const CSA_LDS uint8_t*)cur);
         __builtin_amdgcn_sched_barrier(0);
         issue(tau + 3, nxt);
         __builtin_amdgcn_sched_barrier(0);

@@ -40,6 +40,10 @@ STAGE_SOURCES = {
     "index_topk": _IDX,
     "csa_attend": ["attend.hip", "common.h", "internal.h"],
     "hca_attend": ["attend.hip", "common.h", "internal.h"],
+    "csa_attend_fp8": ["attend_fp8.hip", "attend_common.h", "attend.hip", "common.h",
+                       "internal.h"],
+    "hca_attend_fp8": ["attend_fp8.hip", "attend_common.h", "attend.hip", "common.h",
+                       "internal.h"],
     "compress_m4": ["compress.hip", "common.h", "internal.h"],
     "compress_m128": ["compress.hip", "common.h", "internal.h"],
     "quantize_keys": ["mxfp4.hip", "mxfp4.h", "common.h", "internal.h"],
@@ -60,6 +64,11 @@ STEP_KERNELS = {
     "hca_decode_1m": [("hca_attend", "k_attend_bf16"), ("hca_attend", "k_attend_combine")],
     "csa_decode_1m": [("index_topk", "k_dscan"), ("index_topk", "k_dmerge"),
                       ("csa_attend", "k_attend_bf16"), ("csa_attend", "k_attend_combine")],
+    "hca_decode_1m_fp8": [("hca_attend_fp8", "k_attend_fp8"),
+                          ("hca_attend_fp8", "k_attend_combine")],
+    "csa_decode_1m_fp8": [("index_topk", "k_dscan"), ("index_topk", "k_dmerge"),
+                          ("csa_attend_fp8", "k_attend_fp8"),
+                          ("csa_attend_fp8", "k_attend_combine")],
 }
 
 
