@@ -414,9 +414,10 @@ k_attend_bf16(AttnArgs<uint16_t, uint16_t> A, const int32_t* __restrict__ topk,
     // this split's range of tiles
     const int ct = (nval + KT - 1) / KT;
     const int ntile = ct + (nwin + KT - 1) / KT;
-    const int tps = (ntile + splits - 1) / splits;
-    const int tau0 = split * tps;
-    const int tau1 = min(ntile, tau0 + tps);
+    // the ntile tiles dealt evenly over the splits (they differ by at most one
+    // tile, so the blocks of a decode launch finish together)
+    const int tau0 = (int)((int64_t)split * ntile / splits);
+    const int tau1 = (int)((int64_t)(split + 1) * ntile / splits);
 
     const KvRows kv{reinterpret_cast<const char*>(A.ck + b * A.cks.ss),
                     reinterpret_cast<const char*>(A.cv + b * A.cvs.ss),
@@ -636,9 +637,10 @@ k_attend_mx8(AttnArgs<uint16_t, uint8_t> A, const uint8_t* __restrict__ cks,
 
     const int ct = (nval + KT - 1) / KT;
     const int ntile = ct + (nwin + KT - 1) / KT;
-    const int tps = (ntile + splits - 1) / splits;
-    const int tau0 = split * tps;
-    const int tau1 = min(ntile, tau0 + tps);
+    // the ntile tiles dealt evenly over the splits (they differ by at most one
+    // tile, so the blocks of a decode launch finish together)
+    const int tau0 = (int)((int64_t)split * ntile / splits);
+    const int tau1 = (int)((int64_t)(split + 1) * ntile / splits);
 
     const uint8_t* ckb = A.ck + b * Nc * D;
     const uint8_t* cvb = A.cv + b * Nc * D;
