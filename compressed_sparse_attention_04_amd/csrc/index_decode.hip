@@ -223,15 +223,46 @@ k_dscan(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ 
 }
 
 // ---- the exact path of a merging block -------------------------------------
+// The key of the need-th largest among n <= DM_NT / 2 keys cb[0..n-1][0]
+// (LDS, any order) and how many keys equal to it are kept, from each key's
+// exact rank: threads 2p and 2p + 1 count the keys above and equal to key p
+// over the two halves of the list (16-byte broadcast reads, two keys each)
+// and add their counts.  The value T with gt < need <= gt + eq is the
+// need-th largest, and need - gt keys equal to it are kept; every thread
+// holding a key equal to T writes the same T and need - gt.  The block
+// synchronises before the results are read.  1 <= need <= n.
+__device__ __forceinline__ void bin_rank_threshold(const u32x2* cb, int n, int need,
+                                                   uint32_t* T_out, int* need_eq_out) {
+    const int tid = threadIdx.x, p = tid >> 1, h = tid & 1;
+    const uint32_t x = p < n ? cb[p][0] : 0u;
+    const int npair = (n + 1) / 2, mid = (npair + 1) / 2;
+    const int j1 = h ? npair : mid;
+    int gt = 0, eq = 0;
+    for (int jp = h ? mid : 0; jp < j1; ++jp) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(cb + 2 * jp);
+        const bool v1 = 2 * jp + 1 < n;            // entry n (odd n): not a key
+        gt += (int)(w[0] > x) + (int)(v1 && w[2] > x);
+        eq += (int)(w[0] == x) + (int)(v1 && w[2] == x);
+    }
+    gt += __shfl_xor(gt, 1, WAVE);
+    eq += __shfl_xor(eq, 1, WAVE);
+    if (h == 0 && p < n && gt < need && need <= gt + eq) {
+        *T_out = x;
+        *need_eq_out = need - gt;
+    }
+}
+
 struct DmSmem {
     SelectSmem sel_sm;
     uint32_t cnt[DM_UCAP / 32];      // list counts per chunk (nchunks <= DM_UCAP / 32)
     __attribute__((aligned(16))) uint32_t sel[DM_MAXW];
     __attribute__((aligned(16))) uint32_t eq[DM_MAXW];
     uint32_t hist[SEL_NB];
-    u32x2 cb[DM_CAP];
-    uint32_t lo, hi, tau_need, tau_thr;
-    int above, in, ccnt, total, need_eq, unlisted;
+    __attribute__((aligned(16))) u32x2 cb[DM_CAP];
+    uint32_t lo, hi, tau_thr;
+    int above, in, ccnt, need_eq;
+    int w_total[DM_NT / WAVE], w_ul[DM_NT / WAVE];
+    uint32_t w_tau[DM_NT / WAVE];
     int scratch[DM_NT / WAVE + 1];
 };
 
@@ -375,23 +406,44 @@ k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__
         ent[e] = u32x2{v[0], v[1]};
         ent[e + 1] = u32x2{v[2], v[3]};
     }
-    if (tid == 0) {
-        S.tau_need = 0u;
-        S.total = 0;
-        S.unlisted = 0;
-    }
-    __syncthreads();
+    // the chunks' (count, tau), loaded with the union (nchk <= DM_NT: at most
+    // DM_UCAP / 32 chunks).  The union's size, the largest tau of a chunk
+    // that left keys out and whether any did: wave reductions, one word
+    // per wave in LDS (single-address LDS atomics from every thread cost
+    // more than the rest of the merge)
+    const u32x2 mt0 = tid < nchk ? meta[tid] : u32x2{0u, 0u};
+    int w_tot = 0, w_ul = 0;
+    uint32_t w_tau = 0u;
     for (int c = tid; c < nchk; c += DM_NT) {
-        const u32x2 mt = meta[c];
+        const u32x2 mt = c == tid ? mt0 : meta[c];
         S.cnt[c] = mt[0];
         const int nv = min(ch, nc - c * ch);
-        atomicAdd(&S.total, (int)mt[0]);
+        w_tot += (int)mt[0];
         if ((int)mt[0] < nv) {                       // the chunk left keys out
-            atomicMax(&S.tau_need, mt[1]);
-            S.unlisted = 1;
+            w_tau = max(w_tau, mt[1]);
+            w_ul = 1;
+        }
+    }
+    {
+        const int wave = tid / WAVE;
+        w_tot = wave_sum(w_tot);
+        w_tau = wave_max_u32_sw(w_tau);
+        const bool ul = __ballot(w_ul != 0) != 0;
+        if (tid % WAVE == 0) {
+            S.w_total[wave] = w_tot;
+            S.w_tau[wave] = w_tau;
+            S.w_ul[wave] = ul ? 1 : 0;
         }
     }
     __syncthreads();
+    int total = 0, unlisted = 0;
+    uint32_t tau_need = 0u;
+#pragma unroll
+    for (int w = 0; w < DM_NT / WAVE; ++w) {
+        total += S.w_total[w];
+        tau_need = max(tau_need, S.w_tau[w]);
+        unlisted |= S.w_ul[w];
+    }
     uint32_t key[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -404,7 +456,7 @@ k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__
     // wave; a bin with more keys than the buffer takes the block-wide radix
     // search.  The selection is key > thr, or key == thr among the first
     // need_eq such keys in union order (= ascending candidate index).
-    bool exact_needed = S.total < need;
+    bool exact_needed = total < need;
     if (!exact_needed) {
         for (int i = tid; i < SEL_NB; i += DM_NT) S.hist[i] = 0u;
         if (tid == 0) S.ccnt = 0;
@@ -436,7 +488,10 @@ k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__
                 if (key[e] && v >= lo && v < hi) S.cb[atomicAdd(&S.ccnt, 1)] = u32x2{v, 0u};
             }
             __syncthreads();
-            if (tid < WAVE) {
+            if (S.in <= DM_NT / 2) {
+                // few keys in the bin (the rule): their exact ranks
+                bin_rank_threshold(S.cb, S.in, need - S.above, &S.tau_thr, &S.need_eq);
+            } else if (tid < WAVE) {
                 constexpr int CE = DM_CAP / WAVE;
                 uint32_t ck[CE];
                 bool valid[CE];
@@ -461,7 +516,7 @@ k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__
             block_topk_threshold<DM_NT, EPT>(key, need, S.sel_sm, &thr1, &need_eq);
         }
         // thr1 - 1 is the k-th key of the union; every left-out key is < tau
-        exact_needed = S.unlisted && thr1 - 1u < S.tau_need;
+        exact_needed = unlisted && thr1 - 1u < tau_need;
         if (!exact_needed) {
             int base, total;
             const uint32_t flags = block_select_flags<DM_NT, EPT>(key, thr1, need_eq, S.sel_sm,
