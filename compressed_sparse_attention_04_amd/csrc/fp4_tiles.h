@@ -100,6 +100,64 @@ __device__ __forceinline__ void stream_tiles_from(const TileSrc& ts, int nv, int
     }
 }
 
+// One query row (decode): its HI head scores are the A rows 0..HI-1, which
+// the MFMA leaves in registers 0..HI-1 of lanes 0-31 only.  The tiles are
+// therefore taken in pairs (stride 1): the scores of the pair's second tile
+// are swapped into lanes 32-63 of the first tile's registers (a permlane32
+// swap per head), so one pass of f covers 64 keys.  f(s, j, ok): head
+// scores s[0..HI-1] of key j (lanes 0-31: the first tile's keys, lanes
+// 32-63: the second's); ok is false on lanes 32-63 when the wave's last
+// tile has no partner.  One pair's scores are live at a time (the register
+// budget of four waves per SIMD), and they pass through an empty asm before
+// f, whose branches depend on the lane.
+template <int NT, int UNR, int HI, bool STREAM, typename F>
+__device__ __forceinline__ void stream_tile_pairs(const TileSrc& ts, int nv, const i32x8& aop,
+                                                  int sa, u32x4 (&kwA)[UNR], int (&ksA)[UNR],
+                                                  F&& f) {
+    static_assert(UNR % 2 == 0, "tiles go in pairs");
+    constexpr int NWV = NT / WAVE;
+    const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+    u32x4 kwB[UNR];
+    int ksB[UNR];
+    auto mfma = [&](const u32x4& kw, int ksv) {
+        const i32x8 bop = {(int)kw[0], (int)kw[1], (int)kw[2], (int)kw[3], 0, 0, 0, 0};
+        const f32x16 zero = {};
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, zero, 4, 4, 0, sa, 0,
+                                                                ksv);
+    };
+    auto run = [&](const u32x4 (&kw)[UNR], const int (&ksv)[UNR], int v0) {
+#pragma unroll
+        for (int x = 0; x < UNR; x += 2) {
+            if (v0 + x >= nv) break;
+            const f32x16 a0 = mfma(kw[x], ksv[x]), a1 = mfma(kw[x + 1], ksv[x + 1]);
+            float sc[HI];
+#pragma unroll
+            for (int h = 0; h < HI; ++h) {
+                const auto r = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(a0[h]), __float_as_uint(a1[h]), false, false);
+                uint32_t v = r[0];
+                asm volatile("" : "+v"(v));
+                sc[h] = __uint_as_float(v);
+            }
+            const int j = (v0 + x + (lane >> 5)) * 32 + (lane & 31);
+            f(sc, j, lane < 32 || v0 + x + 1 < nv);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int v0 = wave * UNR;
+    if (v0 >= nv) return;
+    while (true) {
+        load_batch<UNR, STREAM>(ts, v0 + NWV * UNR, 1, kwB, ksB);
+        run(kwA, ksA, v0);
+        v0 += NWV * UNR;
+        if (v0 >= nv) break;
+        load_batch<UNR, STREAM>(ts, v0 + NWV * UNR, 1, kwA, ksA);
+        run(kwB, ksB, v0);
+        v0 += NWV * UNR;
+        if (v0 >= nv) break;
+    }
+}
+
 template <int NT, int UNR, bool STREAM = false, typename F>
 __device__ __forceinline__ void stream_tiles(const TileSrc& ts, int nv, int stride,
                                              const i32x8& aop, int sa, F&& f) {

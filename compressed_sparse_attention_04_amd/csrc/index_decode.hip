@@ -101,7 +101,7 @@ __device__ __forceinline__ void encode_q(const T* q_idx, RowStrides qs, int64_t 
     }
 }
 
-template <typename T, int HI>
+template <typename T, int HI, bool ONE>
 __global__ void __launch_bounds__(DS_NT)
 k_dscan(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ kc,
         const uint8_t* __restrict__ ks, void* ws, int64_t Tq, int dI, int64_t Nc, int64_t m,
@@ -150,19 +150,37 @@ k_dscan(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__ 
     }
     __syncthreads();
 
-    stream_tiles_from<DS_NT, DS_UNR, true>(ts, ntiles, 1, aop, sa, kwA, ksA,
-                                           [&](const f32x16& acc, int jt) {
-        const int jj = jt + row;
-        uint32_t key[NU];
-        tile_keys<HI>(acc, key, nlive);
+    if constexpr (ONE) {
+        // one query row (Tq = 1): tiles in pairs, 64 keys per pass (the ReLU head sum
+        // in the order of score_key); nv0 for every lane (nvq holds it on
+        // lanes 0-31 only)
+        const int nv0 = (int)max((int64_t)0, min((int64_t)nkeys, n_candidates(q_pos0, m, W) - c0));
+        stream_tile_pairs<DS_NT, DS_UNR, HI, true>(ts, ntiles, aop, sa, kwA, ksA,
+                                                   [&](const float (&sc)[HI], int jj, bool ok) {
+            float sum = __int_as_float(max(__float_as_int(sc[0]), 0));
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int q = qslot[u];
-            if (u >= nlive || q >= qv || jj >= nkeys) continue;
-            keys[q * ch + jj] = key[u];
-            if (jj < nvq[u]) atomicAdd(&hist[q * SEL_NB + lvl1_bin(key[u])], 1u);
-        }
-    });
+            for (int hh = 1; hh < HI; ++hh) sum += __int_as_float(max(__float_as_int(sc[hh]), 0));
+            const uint32_t key = __float_as_uint(sum);
+            if (ok && jj < nkeys) {
+                keys[jj] = key;
+                if (jj < nv0) atomicAdd(&hist[lvl1_bin(key)], 1u);
+            }
+        });
+    } else {
+        stream_tiles_from<DS_NT, DS_UNR, true>(ts, ntiles, 1, aop, sa, kwA, ksA,
+                                               [&](const f32x16& acc, int jt) {
+            const int jj = jt + row;
+            uint32_t key[NU];
+            tile_keys<HI>(acc, key, nlive);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int q = qslot[u];
+                if (u >= nlive || q >= qv || jj >= nkeys) continue;
+                keys[q * ch + jj] = key[u];
+                if (jj < nvq[u]) atomicAdd(&hist[q * SEL_NB + lvl1_bin(key[u])], 1u);
+            }
+        });
+    }
     __syncthreads();
 
     u32x2* meta = ws_meta(ws, Tq * gridDim.y, g);
@@ -563,9 +581,14 @@ static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m
                             const uint8_t* kc, const uint8_t* ks, int32_t* topk, void* ws,
                             const DecodeGeom& g, hipStream_t st) {
     const size_t lds_scan = (size_t)Tq * (g.ch + SEL_NB) * sizeof(uint32_t);
-    hipLaunchKernelGGL((k_dscan<T, HI>), dim3((unsigned)g.nchunks, (unsigned)B), dim3(DS_NT),
-                       lds_scan, st, (const T*)q_idx, qs, kc, ks, ws, Tq, dI, Nc, m, W, q_pos0,
-                       g);
+    if (Tq == 1)
+        hipLaunchKernelGGL((k_dscan<T, HI, true>), dim3((unsigned)g.nchunks, (unsigned)B),
+                           dim3(DS_NT), lds_scan, st, (const T*)q_idx, qs, kc, ks, ws, Tq, dI, Nc,
+                           m, W, q_pos0, g);
+    else
+        hipLaunchKernelGGL((k_dscan<T, HI, false>), dim3((unsigned)g.nchunks, (unsigned)B),
+                           dim3(DS_NT), lds_scan, st, (const T*)q_idx, qs, kc, ks, ws, Tq, dI, Nc,
+                           m, W, q_pos0, g);
     const size_t lds = sizeof(DmSmem);
 #define CSA_DM_CASE(E)                                                                       \
     do {                                                                                     \
