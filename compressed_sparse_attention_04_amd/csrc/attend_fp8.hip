@@ -24,7 +24,9 @@
 //                    (relative error <= 2^-4) down to p = 2^(-12 + E - eV).
 // V^T operands come from transposing LDS reads (ds_read_b64_tr_b8).  K and
 // V codes of a tile are copied straight into LDS (global_load_lds) three
-// tiles ahead; with splits, the bf16 partials go to the combine kernel of
+// tiles ahead, and the S^T products of a tile are issued one step before
+// its softmax, so that they run while the previous tile's softmax takes the
+// vector unit.  With splits, the bf16 partials go to the combine kernel of
 // the bf16 path.
 #include "attend_common.h"
 #include "common.h"
@@ -70,6 +72,15 @@ __device__ __forceinline__ int f8_swz(int r) {
 template <int NW>
 constexpr int f8_copies() {
     return 2 * (F8Geom::NCODE / NW) + (NW == 1 ? 2 : 1);
+}
+
+// LDS address of a stage, computed where it is used: the loop runs the four
+// stages in turn, and addresses derived from four constant stage bases would
+// otherwise be kept in registers across the loop.
+__device__ __forceinline__ uint32_t f8_stage(const CSA_LDS uint8_t* stg) {
+    uint32_t a = (uint32_t)(uintptr_t)stg;
+    asm volatile("" : "+s"(a));
+    return a;
 }
 
 // Rows of one sequence: codes (128 bytes per row) and scale words (4 bytes)
@@ -153,9 +164,32 @@ struct Fp8Heads {
     i32x8 qop[2];
     int qsc;                      // E8M0 exponent of this lane's head row
     float m_run, mb, l_run;
-    f32x16 sacc[2];               // S^T of the current tile's two halves
 
     u32x4 qraw[8];                // the lane's 64 query values (bf16), until encoded
+    uint32_t ko[5], vo[5];        // the lane's LDS read offsets within a stage
+
+    // K operand reads: chunk 4s + h (+ 2) of row 32t + rr (the two halves t
+    // are 4 KB apart), and row rr's scale word.  V^T reads: group g = lane /
+    // 16 reads dims 32b + 16 (g % 2) + 0..15 of 8 keys per read; lane 2j + a
+    // of the group points at key 16x + 4h + 8 (j / 4) + j % 4, bytes
+    // 8a..8a+7.  The swizzle of those keys does not depend on x, so the four
+    // reads of one dim block are one address 16 key rows (2 KB) apart.  Then
+    // the V scale words of the lane's keys 32t + 8q + 4h + 0..3.
+    __device__ __forceinline__ void offsets() {
+        using G = F8Geom;
+        const int lane = threadIdx.x % 64, rr = lane & 31, h = lane >> 5;
+        const int sw = f8_swz(rr);                  // = f8_swz(32 t + rr)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ko[c] = rr * G::ROWB + (((2 * c + h) ^ sw) * 16);
+        ko[4] = G::KS_OFF + rr * 4;
+        const int gi = lane & 15, j = gi >> 1, a = gi & 1, c16 = (lane >> 4) & 1;
+        const int key0 = 4 * h + 8 * (j >> 2) + (j & 3);
+        const int swv = f8_swz(key0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            vo[c] = G::CODE_B + key0 * G::ROWB + 8 * a + (((2 * c + c16) ^ swv) * 16);
+        vo[4] = G::VS_OFF + 16 * h;
+    }
 
     // qh: the query token's [H][128] bf16 rows, from this wave's first head;
     // lane (c + 32h) holds dims 16h + 32u + 0..15 (u = 0..3) of head c.  The
@@ -230,20 +264,16 @@ struct Fp8Heads {
         l_run = 0.f;
     }
 
-    // S^T of both halves of the tile in stage stg.  The tile's LDS reads are
-    // asm blocks that wait for themselves: the tile's copies are complete
+    // S^T of both halves of the tile in stage stg into s.  The K reads are
+    // one asm block that waits for itself: the tile's copies are complete
     // (explicit vmcnt wait and barrier), and the compiler, which cannot
     // always tell a stage's reads from the copies in flight into the other
-    // stages, would otherwise wait for every copy.
-    __device__ __forceinline__ void qk(const CSA_LDS uint8_t* stg) {
-        using G = F8Geom;
-        const int lane = threadIdx.x % 64, rr = lane & 31, h = lane >> 5;
-        const int sw = f8_swz(rr);                  // = f8_swz(32 t + rr)
-        // chunk 4s + h (+ 2) of row 32t + rr; the two halves t are 4 KB apart
-        const uint32_t row = (uint32_t)(uintptr_t)(stg + rr * G::ROWB);
-        const uint32_t a0 = row + ((h ^ sw) * 16), a1 = row + (((2 + h) ^ sw) * 16);
-        const uint32_t a2 = row + (((4 + h) ^ sw) * 16), a3 = row + (((6 + h) ^ sw) * 16);
-        const uint32_t as = (uint32_t)(uintptr_t)(stg + G::KS_OFF + rr * 4);
+    // stages, would otherwise wait for every copy.  The products are left
+    // running; the softmax of the previous tile overlaps them.
+    __device__ __forceinline__ void qk(const CSA_LDS uint8_t* stg, f32x16 (&s)[2]) {
+        const uint32_t sb = f8_stage(stg);
+        const uint32_t a0 = sb + ko[0], a1 = sb + ko[1], a2 = sb + ko[2], a3 = sb + ko[3];
+        const uint32_t as = sb + ko[4];
         u32x4 k[2][4];
         uint32_t ksw[2];
         asm volatile(
@@ -265,87 +295,66 @@ struct Fp8Heads {
         for (int t = 0; t < 2; ++t) {
             f32x16 s_ = {};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const u32x4 lo = k[t][2 * s], hi = k[t][2 * s + 1];
+            for (int q = 0; q < 2; ++q) {
+                const u32x4 lo = k[t][2 * q], hi = k[t][2 * q + 1];
                 const i32x8 kop = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 // the row's E8M0 exponent for both blocks of the step
                 s_ = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    kop, qop[s], s_, 0, 0, 0, (int)(ksw[t] >> 23), 0, qsc);
+                    kop, qop[q], s_, 0, 0, 0, (int)(ksw[t] >> 23), 0, qsc);
             }
-            sacc[t] = s_;
+            s[t] = s_;
         }
     }
 
-    // V^T operands of the tile (kept in rd until the PV product)
-    i32x2 rd[4][4];
-    __device__ __forceinline__ void read_v(const CSA_LDS uint8_t* stg) {
-        using G = F8Geom;
-        const int lane = threadIdx.x % 64, h = lane >> 5;
-        // V^T operands by transposing reads: group g = lane / 16 reads dims
-        // 32b + 16 (g % 2) + 0..15 of 8 keys per read; lane 2j + a of the
-        // group points at key 16x + 4h + 8 (j / 4) + j % 4, bytes 8a..8a+7.
-        // The swizzle of those keys does not depend on x, so the four reads
-        // of one dim block are one address 16 key rows (2 KB) apart.  They
-        // are issued together in one asm block that waits for them itself
-        // (the compiler cannot always tell these reads from the copies in
-        // flight into other stages, and would wait for every copy).
-        const int gi = lane & 15, j = gi >> 1, a = gi & 1, c16 = (lane >> 4) & 1;
-        const int key0 = 4 * h + 8 * (j >> 2) + (j & 3);
-        const int sw = f8_swz(key0);
-        const uint32_t vbase =
-            (uint32_t)(uintptr_t)(stg + G::CODE_B + key0 * G::ROWB + 8 * a);
-        const uint32_t v0 = vbase + (uint32_t)(((0 + c16) ^ sw) * 16);
-        const uint32_t v1 = vbase + (uint32_t)(((2 + c16) ^ sw) * 16);
-        const uint32_t v2 = vbase + (uint32_t)(((4 + c16) ^ sw) * 16);
-        const uint32_t v3 = vbase + (uint32_t)(((6 + c16) ^ sw) * 16);
-        asm volatile(
-            "ds_read_b64_tr_b8 %0, %16\n\t"
-            "ds_read_b64_tr_b8 %1, %16 offset:2048\n\t"
-            "ds_read_b64_tr_b8 %2, %16 offset:4096\n\t"
-            "ds_read_b64_tr_b8 %3, %16 offset:6144\n\t"
-            "ds_read_b64_tr_b8 %4, %17\n\t"
-            "ds_read_b64_tr_b8 %5, %17 offset:2048\n\t"
-            "ds_read_b64_tr_b8 %6, %17 offset:4096\n\t"
-            "ds_read_b64_tr_b8 %7, %17 offset:6144\n\t"
-            "ds_read_b64_tr_b8 %8, %18\n\t"
-            "ds_read_b64_tr_b8 %9, %18 offset:2048\n\t"
-            "ds_read_b64_tr_b8 %10, %18 offset:4096\n\t"
-            "ds_read_b64_tr_b8 %11, %18 offset:6144\n\t"
-            "ds_read_b64_tr_b8 %12, %19\n\t"
-            "ds_read_b64_tr_b8 %13, %19 offset:2048\n\t"
-            "ds_read_b64_tr_b8 %14, %19 offset:4096\n\t"
-            "ds_read_b64_tr_b8 %15, %19 offset:6144\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(rd[0][0]), "=&v"(rd[0][1]), "=&v"(rd[0][2]), "=&v"(rd[0][3]),
-              "=&v"(rd[1][0]), "=&v"(rd[1][1]), "=&v"(rd[1][2]), "=&v"(rd[1][3]),
-              "=&v"(rd[2][0]), "=&v"(rd[2][1]), "=&v"(rd[2][2]), "=&v"(rd[2][3]),
-              "=&v"(rd[3][0]), "=&v"(rd[3][1]), "=&v"(rd[3][2]), "=&v"(rd[3][3])
-            : "v"(v0), "v"(v1), "v"(v2), "v"(v3));
-    }
-
-    // softmax of the tile (the first nvalid keys count), P folded with the
-    // V exponents and rounded to E4M3, then O^T += V^T P^T
-    __device__ __forceinline__ void rest(const CSA_LDS uint8_t* stg, int nvalid, float scale_log2) {
+    // The tile in stage stg, whose S^T is in s: its V scale words and V^T
+    // operands (one asm block that waits for itself, as the K reads), the
+    // softmax (the first nvalid keys count), P folded with the V exponents
+    // and rounded to E4M3, then O^T += V^T P^T.
+    __device__ __forceinline__ void rest(const CSA_LDS uint8_t* stg, f32x16 (&s)[2], int nvalid,
+                                         float scale_log2) {
         using G = F8Geom;
         const int lane = threadIdx.x % 64, h = lane >> 5;
         // V scale words of this lane's keys: 4 consecutive keys 32t + 8q + 4h + 0..3
         u32x4 ve[2][4];
+        i32x2 rd[4][4];                             // V^T operands
         {
-            const uint32_t av = (uint32_t)(uintptr_t)(stg + G::VS_OFF + 16 * h);
+            const uint32_t sb = f8_stage(stg);
+            const uint32_t v0 = sb + vo[0], v1 = sb + vo[1], v2 = sb + vo[2], v3 = sb + vo[3];
+            const uint32_t av = sb + vo[4];
             asm volatile(
-                "ds_read_b128 %0, %8\n\t"
-                "ds_read_b128 %1, %8 offset:32\n\t"
-                "ds_read_b128 %2, %8 offset:64\n\t"
-                "ds_read_b128 %3, %8 offset:96\n\t"
-                "ds_read_b128 %4, %8 offset:128\n\t"
-                "ds_read_b128 %5, %8 offset:160\n\t"
-                "ds_read_b128 %6, %8 offset:192\n\t"
-                "ds_read_b128 %7, %8 offset:224\n\t"
+                "ds_read_b128 %0, %28\n\t"
+                "ds_read_b128 %1, %28 offset:32\n\t"
+                "ds_read_b128 %2, %28 offset:64\n\t"
+                "ds_read_b128 %3, %28 offset:96\n\t"
+                "ds_read_b128 %4, %28 offset:128\n\t"
+                "ds_read_b128 %5, %28 offset:160\n\t"
+                "ds_read_b128 %6, %28 offset:192\n\t"
+                "ds_read_b128 %7, %28 offset:224\n\t"
+                "ds_read_b64_tr_b8 %8, %24\n\t"
+                "ds_read_b64_tr_b8 %9, %24 offset:2048\n\t"
+                "ds_read_b64_tr_b8 %10, %24 offset:4096\n\t"
+                "ds_read_b64_tr_b8 %11, %24 offset:6144\n\t"
+                "ds_read_b64_tr_b8 %12, %25\n\t"
+                "ds_read_b64_tr_b8 %13, %25 offset:2048\n\t"
+                "ds_read_b64_tr_b8 %14, %25 offset:4096\n\t"
+                "ds_read_b64_tr_b8 %15, %25 offset:6144\n\t"
+                "ds_read_b64_tr_b8 %16, %26\n\t"
+                "ds_read_b64_tr_b8 %17, %26 offset:2048\n\t"
+                "ds_read_b64_tr_b8 %18, %26 offset:4096\n\t"
+                "ds_read_b64_tr_b8 %19, %26 offset:6144\n\t"
+                "ds_read_b64_tr_b8 %20, %27\n\t"
+                "ds_read_b64_tr_b8 %21, %27 offset:2048\n\t"
+                "ds_read_b64_tr_b8 %22, %27 offset:4096\n\t"
+                "ds_read_b64_tr_b8 %23, %27 offset:6144\n\t"
                 "s_waitcnt lgkmcnt(0)"
                 : "=&v"(ve[0][0]), "=&v"(ve[0][1]), "=&v"(ve[0][2]), "=&v"(ve[0][3]),
-                  "=&v"(ve[1][0]), "=&v"(ve[1][1]), "=&v"(ve[1][2]), "=&v"(ve[1][3])
-                : "v"(av));
+                  "=&v"(ve[1][0]), "=&v"(ve[1][1]), "=&v"(ve[1][2]), "=&v"(ve[1][3]),
+                  "=&v"(rd[0][0]), "=&v"(rd[0][1]), "=&v"(rd[0][2]), "=&v"(rd[0][3]),
+                  "=&v"(rd[1][0]), "=&v"(rd[1][1]), "=&v"(rd[1][2]), "=&v"(rd[1][3]),
+                  "=&v"(rd[2][0]), "=&v"(rd[2][1]), "=&v"(rd[2][2]), "=&v"(rd[2][3]),
+                  "=&v"(rd[3][0]), "=&v"(rd[3][1]), "=&v"(rd[3][2]), "=&v"(rd[3][3])
+                : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "v"(av));
         }
         // mask, maximum, lazy rescaling (as the bf16 engine, with p <= 4 so
         // that P has 6 octaves of headroom below E4M3's largest value)
@@ -355,14 +364,14 @@ struct Fp8Heads {
                 const int lim = nvalid - 32 * t - 4 * h;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (8 * (r / 4) + (r % 4) >= lim) sacc[t][r] = -INFINITY;
+                    if (8 * (r / 4) + (r % 4) >= lim) s[t][r] = -INFINITY;
             }
         }
         float tm = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, sacc[t][r]);
+            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[t][r]);
         const float tmax = max_halves(tm);
         const bool grow = (tmax - m_run) * scale_log2 > 2.f;
         if (__ballot(grow)) {
@@ -378,16 +387,16 @@ struct Fp8Heads {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
         }
-        // probabilities (<= 4), their sum, and the largest V scale word
-        float p[2][16];
+        // probabilities (<= 4, in place of the scores), their sum, and the
+        // largest V scale word
         uint32_t emax = 7u << 23;                    // E >= 7: the block scale E - 6 >= 1
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[t][r] = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, mb));
-                ps[r % 4] += p[t][r];
+                s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, mb));
+                ps[r % 4] += s[t][r];
                 emax = max(emax, (uint32_t)ve[t][r / 4][r % 4]);
             }
         l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
@@ -403,10 +412,10 @@ struct Fp8Heads {
         for (int w = 0; w < 8; ++w) {
             const int t = w / 4, r0 = 4 * (w % 4);
             const u32x4 f = ve[t][r0 / 4];            // scale words 2^eV
-            const float a0 = p[t][r0] * __uint_as_float(f[0]);
-            const float a1 = p[t][r0 + 1] * __uint_as_float(f[1]);
-            const float a2 = p[t][r0 + 2] * __uint_as_float(f[2]);
-            const float a3 = p[t][r0 + 3] * __uint_as_float(f[3]);
+            const float a0 = s[t][r0] * __uint_as_float(f[0]);
+            const float a1 = s[t][r0 + 1] * __uint_as_float(f[1]);
+            const float a2 = s[t][r0 + 2] * __uint_as_float(f[2]);
+            const float a3 = s[t][r0 + 3] * __uint_as_float(f[3]);
             typedef short s16x2 __attribute__((ext_vector_type(2)));
             s16x2 pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, a0, a1, esc, false);
             pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, a2, a3, esc, true);
@@ -545,33 +554,44 @@ k_attend_fp8(Fp8IO A, const int32_t* __restrict__ topk, float* __restrict__ part
         asm volatile("" ::"v"(p0.scale), "v"(p1.scale), "v"(p2.scale));
     }
     eng.encode_q();
-    // one tile: wait for its copies (the next two tiles' stay in flight),
-    // barrier (the stage written next is then free on every wave), QK, the
-    // copies three tiles ahead, then softmax and PV
-    auto step = [&](int tau, uint8_t* cur, uint8_t* nxt) {
-        if (tau + 2 < tau1) CSA_WAIT_VM(2 * PER);
-        else if (tau + 1 < tau1) CSA_WAIT_VM(PER);
+    eng.offsets();
+    // S^T of the first tile.  Then one step per tile tau: wait for tile
+    // tau + 1's copies (tile tau + 2's stay in flight), barrier (every wave
+    // is done with tile tau - 1, whose stage the copies for tile tau + 3
+    // then overwrite), the products S^T of tile tau + 1 (on stale bytes of
+    // its stage when tau is the last tile; never used), the copies, then
+    // tile tau's softmax and PV, which overlap the S^T products.
+    f32x16 sA[2], sB[2];
+    if (tau0 + 2 < tau1) CSA_WAIT_VM(2 * PER);
+    else if (tau0 + 1 < tau1) CSA_WAIT_VM(PER);
+    else CSA_WAIT_VM(0);
+    lds_barrier();
+    eng.qk((const CSA_LDS uint8_t*)sS0, sA);
+    auto step = [&](int tau, uint8_t* cur, uint8_t* nxt, uint8_t* cpy, f32x16 (&s_cur)[2],
+                    f32x16 (&s_nxt)[2]) {
+        if (tau + 2 < tau1) CSA_WAIT_VM(PER);
         else CSA_WAIT_VM(0);
         lds_barrier();
         const int nvalid = tau < ct ? nval - KT * tau : nwin - KT * (tau - ct);
-        eng.qk((const CSA_LDS uint8_t*)cur);
+        eng.qk((const CSA_LDS uint8_t*)nxt, s_nxt);
+        // an empty asm naming the products: the compiler would otherwise
+        // move them down to their first use, in the next step (it reads
+        // nothing, so the wave does not wait for them here)
+        asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]));
         __builtin_amdgcn_sched_barrier(0);
-        // the V^T reads wait while the QK products run
-        eng.read_v((const CSA_LDS uint8_t*)cur);
+        issue(tau + 3, cpy);
         __builtin_amdgcn_sched_barrier(0);
-        issue(tau + 3, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        eng.rest((const CSA_LDS uint8_t*)cur, nvalid, scale_log2);
+        eng.rest((const CSA_LDS uint8_t*)cur, s_cur, nvalid, scale_log2);
     };
 
     for (int tau = tau0; tau < tau1; tau += 4) {
-        step(tau, sS0, sS3);
+        step(tau, sS0, sS1, sS3, sA, sB);
         if (tau + 1 >= tau1) break;
-        step(tau + 1, sS1, sS0);
+        step(tau + 1, sS1, sS2, sS0, sB, sA);
         if (tau + 2 >= tau1) break;
-        step(tau + 2, sS2, sS1);
+        step(tau + 2, sS2, sS3, sS1, sA, sB);
         if (tau + 3 >= tau1) break;
-        step(tau + 3, sS3, sS2);
+        step(tau + 3, sS3, sS0, sS2, sB, sA);
     }
     uint16_t* o_row = A.o + (b * Tq + i) * (int64_t)H * D + wave * 32 * D;
     if (splits == 1) {
