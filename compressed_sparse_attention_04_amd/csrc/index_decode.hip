@@ -254,13 +254,22 @@ __device__ __forceinline__ void bin_rank_threshold(const u32x2* cb, int n, int n
     const int tid = threadIdx.x, p = tid >> 1, h = tid & 1;
     const uint32_t x = p < n ? cb[p][0] : 0u;
     const int npair = (n + 1) / 2, mid = (npair + 1) / 2;
-    const int j1 = h ? npair : mid;
+    const int j0 = h ? mid : 0, j1 = h ? npair : mid;
     int gt = 0, eq = 0;
-    for (int jp = h ? mid : 0; jp < j1; ++jp) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(cb + 2 * jp);
-        const bool v1 = 2 * jp + 1 < n;            // entry n (odd n): not a key
-        gt += (int)(w[0] > x) + (int)(v1 && w[2] > x);
-        eq += (int)(w[0] == x) + (int)(v1 && w[2] == x);
+    // four pair reads in flight per round (indices clamped into the half,
+    // the surplus masked)
+    for (int jp = j0; jp < j1; jp += 4) {
+        u32x4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            w[u] = *reinterpret_cast<const u32x4*>(cb + 2 * min(jp + u, j1 - 1));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool v0 = jp + u < j1;
+            const bool v1 = v0 && 2 * (jp + u) + 1 < n;  // entry n (odd n): not a key
+            gt += (int)(v0 && w[u][0] > x) + (int)(v1 && w[u][2] > x);
+            eq += (int)(v0 && w[u][0] == x) + (int)(v1 && w[u][2] == x);
+        }
     }
     gt += __shfl_xor(gt, 1, WAVE);
     eq += __shfl_xor(eq, 1, WAVE);
@@ -477,7 +486,6 @@ k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__
     bool exact_needed = total < need;
     if (!exact_needed) {
         for (int i = tid; i < SEL_NB; i += DM_NT) S.hist[i] = 0u;
-        if (tid == 0) S.ccnt = 0;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
@@ -499,12 +507,28 @@ k_dmerge(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __restrict__
         uint32_t thr1;                               // threshold in key + 1 form
         int need_eq;
         if (S.in <= DM_CAP) {
+            // the bin's keys, at offsets from a block prefix sum of the
+            // threads' counts (a returning atomic on one LDS word costs a
+            // round trip per slot and wave)
             const uint32_t lo = S.lo, hi = S.hi;
+            uint32_t inb = 0u;
+            int cnt = 0;
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
                 const uint32_t v = key[e] - 1u;
-                if (key[e] && v >= lo && v < hi) S.cb[atomicAdd(&S.ccnt, 1)] = u32x2{v, 0u};
+                if (key[e] && v >= lo && v < hi) {
+                    inb |= 1u << e;
+                    ++cnt;
+                }
             }
+            const int incl = wave_incl_scan(cnt);
+            if (tid % WAVE == WAVE - 1) S.w_total[tid / WAVE] = incl;
+            __syncthreads();
+            int pos = incl - cnt;
+            for (int w = 0; w < tid / WAVE; ++w) pos += S.w_total[w];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (inb & (1u << e)) S.cb[pos++] = u32x2{key[e] - 1u, 0u};
             __syncthreads();
             if (S.in <= DM_NT / 2) {
                 // few keys in the bin (the rule): their exact ranks
