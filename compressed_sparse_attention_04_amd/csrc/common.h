@@ -114,6 +114,15 @@ __device__ __forceinline__ uint32_t wave_max_u32_sw(uint32_t v) {
     const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return max((uint32_t)r[0], (uint32_t)r[1]);
 }
+__device__ __forceinline__ uint32_t wave_or_u32_sw(uint32_t v) {
+    v |= swizzle_xor<16>(v);
+    v |= swizzle_xor<8>(v);
+    v |= swizzle_xor<4>(v);
+    v |= swizzle_xor<2>(v);
+    v |= swizzle_xor<1>(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (uint32_t)r[0] | (uint32_t)r[1];
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {

@@ -27,6 +27,7 @@
 // at most 256 keys (or one key value), then a collecting pass.  Either way
 // ties at the threshold are resolved by candidate order and the kept set is
 // read out of a candidate bitmap in ascending order.
+#include <type_traits>
 #include "internal.h"
 #include "mxfp4.h"
 #include "wave_select.h"
@@ -53,6 +54,9 @@ constexpr int ST_SAMPLE = 8;           // one key tile in ST_SAMPLE is sampled
 constexpr int ST_SAMPLE_MIN = 2048;    // candidates a row needs for the sampled path
 constexpr int ST_SAMPLE_MAXK = 768;    // and at most this many kept ones
 constexpr int ST_UNR = 2;              // key tiles per wave and batch
+// registers per lane of the sampled finish (a segment of up to 8 x that many
+// collected keys)
+constexpr int ST_FIN_EPT0 = 12, ST_FIN_EPT1 = 16, ST_FIN_EPT2 = (ST_SEG + 7) / 8;
 
 enum : int { M_DONE = 0, M_HIST1 = 1, M_HIST = 2, M_COLLECT = 3, M_SAMPLED = 4 };
 
@@ -206,6 +210,8 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
         __syncthreads();
         // 3. one pass over every key: the keys >= lo, with their indices, go
         // to this wave's segment of their row's region
+        // (a slot of no sampled row gets the bound KEY_END, which no key
+        // reaches)
         uint32_t lo[NU];
         int cnt[NU];                    // lanes of half-wave kb count the keys of its row
 #pragma unroll
@@ -213,7 +219,11 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
             lo[u] = act[u] ? S.lo[qslot[u]] : KEY_END;
             cnt[u] = 0;
         }
-        stream_tiles<ST_NT, ST_UNR>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+        // tiles below every row's candidate count need no per-lane bound
+        int nc_min = S.nc[0];
+        for (int q = 1; q < qv; ++q) nc_min = min(nc_min, S.nc[q]);
+        nc_min = __builtin_amdgcn_readfirstlane(nc_min);
+        auto collect = [&](const f32x16& acc, int j0, auto bounded) {
             const int j = j0 + row;
             uint32_t keys[NU];
             tile_keys<HI>(acc, keys);
@@ -221,7 +231,8 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
             for (int u = 0; u < NU; ++u) {
                 // the 32 lanes of a half-wave hold the tile's 32 keys of one
                 // query row; the two halves serve different rows
-                const bool hit = act[u] && j < ncq[u] && keys[u] >= lo[u];
+                bool hit = keys[u] >= lo[u];
+                if constexpr (decltype(bounded)::value) hit = hit && j < ncq[u];
                 const uint64_t bal = __ballot(hit);
                 if (bal != 0ull) {
                     const uint32_t mine = kb ? (uint32_t)(bal >> 32) : (uint32_t)bal;
@@ -237,6 +248,12 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
                     cnt[u] += __popc(mine);
                 }
             }
+        };
+        stream_tiles<ST_NT, ST_UNR>(ts, ntiles, 1, aop, sa, [&](const f32x16& acc, int j0) {
+            // j0 is the same on every lane: a scalar branch
+            if (__builtin_amdgcn_readfirstlane(j0) + 32 <= nc_min)
+                collect(acc, j0, std::false_type{});
+            else collect(acc, j0, std::true_type{});
         });
 #pragma unroll
         for (int u = 0; u < NU; ++u)
@@ -254,36 +271,51 @@ k_index_stream(const T* __restrict__ q_idx, RowStrides qs, const uint8_t* __rest
             }
             const int need = S.need[q];
             if (nin >= need && !over) {
-                // every key >= lo is collected and the k-th key is one of them
-                constexpr int EPT = (ST_BUF + WAVE - 1) / WAVE;
-                uint32_t key[EPT], jj[EPT];
-                bool valid[EPT];
+                // every key >= lo is collected and the k-th key is one of
+                // them.  Lane l takes entries l / 8 + 8 e of segment l % 8,
+                // so EPT registers cover segments of up to 8 EPT entries:
+                // the smallest of three register counts that holds the
+                // fullest segment is used.
+                const int mycnt = S.segcnt[q][lane % ST_NWV];
+                int maxc = 0;
+                for (int w = 0; w < ST_NWV; ++w) maxc = max(maxc, S.segcnt[q][w]);
+                const int rbase = (lane % ST_NWV) * ST_SEG + lane / ST_NWV;
+                auto finish = [&](auto ept) {
+                    constexpr int EPT = decltype(ept)::value;
+                    uint32_t key[EPT], jj[EPT];
+                    bool valid[EPT];
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const int p = e * WAVE + lane;
-                    valid[e] = p < ST_BUF && p % ST_SEG < S.segcnt[q][min(p / ST_SEG, ST_NWV - 1)];
-                    key[e] = valid[e] ? r[p] : 0u;
-                    jj[e] = valid[e] ? reinterpret_cast<const uint16_t*>(r + ST_JOFF)[p] : 0u;
-                }
-                __builtin_amdgcn_wave_barrier();
-                uint32_t thr;
-                int need_eq;
-                wave_ballot_threshold<EPT>(key, valid, need, &thr, &need_eq);
-                // the region now holds the kept bitmap and the tie bitmap
-                for (int w = lane; w < qnw; w += WAVE) {
-                    r[w] = 0u;
-                    r[ST_MAXW + w] = 0u;
-                }
-                __builtin_amdgcn_wave_barrier();
+                    for (int e = 0; e < EPT; ++e) {
+                        const int pos = 8 * e + lane / ST_NWV;
+                        const int p = rbase + 8 * e;
+                        valid[e] = pos < mycnt;
+                        key[e] = valid[e] ? r[p] : 0u;
+                        jj[e] = valid[e] ? reinterpret_cast<const uint16_t*>(r + ST_JOFF)[p] : 0u;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    uint32_t thr;
+                    int need_eq;
+                    wave_ballot_threshold<EPT>(key, valid, need, &thr, &need_eq);
+                    // the region now holds the kept bitmap and the tie bitmap
+                    for (int w = lane; w < qnw; w += WAVE) {
+                        r[w] = 0u;
+                        r[ST_MAXW + w] = 0u;
+                    }
+                    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    if (!valid[e]) continue;
-                    const uint32_t bit = 1u << (jj[e] & 31);
-                    if (key[e] > thr) atomicOr(&r[jj[e] >> 5], bit);
-                    else if (key[e] == thr) atomicOr(&r[ST_MAXW + (jj[e] >> 5)], bit);
-                }
-                __builtin_amdgcn_wave_barrier();
-                wave_merge_first_bits(r, r + ST_MAXW, qnw, need_eq);
+                    for (int e = 0; e < EPT; ++e) {
+                        if (!valid[e]) continue;
+                        const uint32_t bit = 1u << (jj[e] & 31);
+                        if (key[e] > thr) atomicOr(&r[jj[e] >> 5], bit);
+                        else if (key[e] == thr) atomicOr(&r[ST_MAXW + (jj[e] >> 5)], bit);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    wave_merge_first_bits(r, r + ST_MAXW, qnw, need_eq);
+                };
+                static_assert(8 * ST_FIN_EPT2 >= ST_SEG, "the widest finish covers a segment");
+                if (maxc <= 8 * ST_FIN_EPT0) finish(std::integral_constant<int, ST_FIN_EPT0>{});
+                else if (maxc <= 8 * ST_FIN_EPT1) finish(std::integral_constant<int, ST_FIN_EPT1>{});
+                else finish(std::integral_constant<int, ST_FIN_EPT2>{});
                 if (lane == 0) S.mode[q] = M_DONE;
             } else {
                 for (int w = lane; w < ST_MAXW; w += WAVE) r[w] = 0u;

@@ -154,9 +154,12 @@ __device__ __forceinline__ void wave_radix_threshold(const uint32_t (&key)[EPT],
 
 // The same threshold without LDS: the bits of the need-th largest key are
 // decided from the top, a bit kept when at least need keys reach the value
-// with it set (counted with ballots).  The search starts below the leading
-// bits that every valid key shares.  need >= 1 and at most the number of
-// valid keys; keys below 0xFFFFFFFF.
+// with it set (counted with ballots).  The search covers only the bits in
+// which the valid keys differ: it starts below the leading bits they all
+// share and stops above the trailing ones (scores of FP4 products are
+// multiples of a power of two, so the low bits of every key are often
+// equal), which then take the shared values.  need >= 1 and at most the
+// number of valid keys; keys below 0xFFFFFFFF.
 template <int EPT>
 __device__ __forceinline__ void wave_ballot_threshold(const uint32_t (&key)[EPT],
                                                       const bool (&valid)[EPT], int need,
@@ -174,15 +177,25 @@ __device__ __forceinline__ void wave_ballot_threshold(const uint32_t (&key)[EPT]
     lo = ~wave_max_u32_sw(~lo);
     const uint32_t diff = hi ^ lo;
     int top = diff ? 31 - __builtin_clz(diff) : -1;     // highest bit where valid keys differ
+    // lowest bit where some valid key differs from the largest one
+    uint32_t dif = 0u;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) dif |= valid[e] ? kp[e] ^ hi : 0u;
+    dif = wave_or_u32_sw(dif);
+    const int low = dif ? __builtin_ctz(dif) : 0;
     uint32_t t = top >= 31 ? 0u : hi & ~((2u << top) - 1u);
 #pragma unroll 1
-    for (int bit = top; bit >= 0; --bit) {
+    for (int bit = top; bit >= low; --bit) {
         const uint32_t cand = t | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) cnt += __popcll(__ballot(kp[e] >= cand));
         if (cnt >= need) t = cand;
     }
+    // below bit low every valid key has the bits of the largest: fewer than
+    // need keys lie above the decided prefix (else the search would have
+    // taken a larger one), so the remaining bits follow the shared ones
+    t |= hi & ((1u << low) - 1u);
     if (top < 0) t = hi;                                 // a single key value
     int gt = 0;
 #pragma unroll
