@@ -31,3 +31,30 @@ def random_selection(rng, n_cand: int, k: int) -> list:
     n = min(k, n_cand)
     sel = sorted(rng.choice(n_cand, size=n, replace=False).tolist()) if n else []
     return sel + [-1] * (k - n)
+
+
+def check_fp8(got, ref):
+    """FP8 attention output against the oracle's attend_fp8 (o, amean, rms):
+    every element within 2^-4 amean + 2^-8 |o| + 3e-3 (the kernel rounds each
+    probability times its value row's exponent to E4M3: relative error at most
+    2^-4 per weight; the rest covers bf16 outputs and split records), and the
+    mean of ((o_gpu - o) / rms)^2 below (0.6 * 2^-4)^2."""
+    o, am, rm = ref
+    g = f64(got)
+    assert g.shape == o.shape and np.isfinite(g).all()
+    err = np.abs(g - o)
+    tol = 2.0 ** -4 * am + 2.0 ** -8 * np.abs(o) + 3e-3
+    worst = float((err / tol).max())
+    ms = float(np.mean((err / np.maximum(rm, 1e-3)) ** 2))
+    say(f"  max err {err.max():.3g}, worst err/tol {worst:.3f}, mean (err/rms)^2 {ms:.3g}")
+    assert worst <= 1.0
+    assert ms <= (0.6 * 2.0 ** -4) ** 2
+
+
+def fp8_host_rows(codes, words):
+    """FP8 rows as the library stores them (codes, one scale word per row with
+    the exponent byte in bits 23..30) in the oracle's layout: codes and the
+    exponent byte repeated per 32 values."""
+    c = codes.cpu().numpy()
+    e = (words.cpu().numpy() >> 23).astype(np.uint8)
+    return c, np.repeat(e[..., None], c.shape[-1] // 32, axis=-1)

@@ -22,7 +22,8 @@ import torch
 import oracle
 from compressed_sparse_attention_04_amd import binding as csa
 from compressed_sparse_attention_04_amd import inputs as I
-from tests.gpu_helpers import DEV, f64, random_selection, say
+from tests.gpu_helpers import DEV, check_fp8 as check, f64, fp8_host_rows as host_rows, \
+    random_selection, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,31 +63,11 @@ def test_quantize_rows_bit_exact(dtype, rows, d, kind):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
-def check(got, ref):
-    o, am, rm = ref
-    g = f64(got)
-    assert g.shape == o.shape and np.isfinite(g).all()
-    err = np.abs(g - o)
-    tol = 2.0 ** -4 * am + 2.0 ** -8 * np.abs(o) + 3e-3
-    worst = float((err / tol).max())
-    ms = float(np.mean((err / np.maximum(rm, 1e-3)) ** 2))
-    say(f"  max err {err.max():.3g}, worst err/tol {worst:.3f}, mean (err/rms)^2 {ms:.3g}")
-    assert worst <= 1.0
-    assert ms <= (0.6 * 2.0 ** -4) ** 2
-
-
 def enc(t):
     """The oracle's FP8 rows of t; on the device as codes and one scale word
     per row (the row's exponent byte in bits 23..30)."""
     c, s = oracle.quant_fp8_rows(f64(t))
     return torch.from_numpy(c).to(DEV), torch.from_numpy(s[..., 0].astype(np.int32) << 23).to(DEV)
-
-
-def host_rows(codes, words):
-    """Back to the oracle's layout: codes and the exponent byte per 32 values."""
-    c = codes.cpu().numpy()
-    e = (words.cpu().numpy() >> 23).astype(np.uint8)
-    return c, np.repeat(e[..., None], c.shape[-1] // 32, axis=-1)
 
 
 def fp8_case(H, T, m, W, k, q_rows, B=1, seed=51, decode_tail=False, corrupt=False,

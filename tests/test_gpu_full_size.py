@@ -9,7 +9,13 @@ decoded entries.
 The inputs are drawn on the GPU by the shared input module and copied to the
 host for the oracle, so both sides see the same numbers.  The oracle runs its
 own chain from the raw inputs (its own compression, MXFP4 encoding, scores
-and top-k) and never takes an intermediate result of the GPU path.
+and top-k) and never takes an intermediate result of the GPU path, with one
+exception: the FP8 decode cases (bench.py --kv-format fp8) check the GPU's
+pooled caches against the oracle's pooling, then hand those bf16 caches to
+the oracle's FP8 row encoder, whose codes must equal the library's bit for
+bit, so that the FP8 attention on both sides reads the same codes (an E4M3
+code can flip where the two poolings round differently, which the FP8
+attention bound does not cover).
 """
 import numpy as np
 import pytest
@@ -18,7 +24,7 @@ import torch
 import oracle
 from compressed_sparse_attention_04_amd import binding as csa
 from compressed_sparse_attention_04_amd import inputs as I
-from tests.gpu_helpers import DEV, TOL, f64, maxerr, say
+from tests.gpu_helpers import DEV, TOL, check_fp8, f64, fp8_host_rows, maxerr, say
 
 pytestmark = pytest.mark.gpu
 
@@ -209,3 +215,58 @@ def test_decode_1m_full_size(name, seqs, kv_fmt):
         err = maxerr(go[b:b + 1].cpu(), ref)
         say("  sequence", b, "output max err", err)
         assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name,seqs", [("hca_decode_1m", [3]), ("csa_decode_1m", [11])])
+def test_decode_1m_full_size_fp8(name, seqs):
+    """bench.py --kv-format fp8's decode step at full size: every entry and
+    window row encoded to an FP8 row by the library, FP8 attention."""
+    w = I.HCA_DECODE_1M if name == "hca_decode_1m" else I.CSA_DECODE_1M
+    t = w.q_pos0
+    say("full size", w.name, "fp8", "sequences", seqs)
+    ck, cv, rk, rv = decode_caches_gpu(w, w.kind == "csa")
+    f8 = {n: csa.csa_quantize_fp8_rows(x) for n, x in (("ck", ck), ("cv", cv), ("rk", rk),
+                                                         ("rv", rv))}
+    q = I.draw_queries(w, device=DEV)
+    if w.kind == "csa":
+        k_idx = I.draw_indexer_keys(w, device=DEV)
+        gkc, gks = csa.csa_quantize_mxfp4(k_idx)
+        q_idx = I.draw_indexer_queries(w, device=DEV)
+        iws = torch.empty(max(1, csa.csa_index_topk_workspace(w.B, 1, w.HI, w.dI, w.Nc, w.m, w.W,
+                                                                w.k, t)),
+                          dtype=torch.uint8, device=DEV)
+        aws = torch.empty(max(1, csa.csa_attend_workspace(1, w.B, 1, w.H, w.D, w.k, w.W)),
+                          dtype=torch.uint8, device=DEV)
+        gtk = csa.csa_index_topk(q_idx, gkc, gks, m=w.m, W=w.W, k=w.k, q_pos0=t, ws=iws)
+        go = csa.csa_attend_fp8(q, f8["ck"][0], f8["cv"][0], f8["ck"][1], f8["cv"][1], gtk,
+                                f8["rk"][0], f8["rv"][0], f8["rk"][1], f8["rv"][1], m=w.m, W=w.W,
+                                q_pos0=t, raw_pos0=t - w.W + 1, ws=aws)
+    else:
+        aws = torch.empty(max(1, csa.hca_attend_workspace(1, w.B, 1, w.H, w.D, w.Nc, w.m, w.W,
+                                                          t)), dtype=torch.uint8, device=DEV)
+        go = csa.hca_attend_fp8(q, f8["ck"][0], f8["cv"][0], f8["ck"][1], f8["cv"][1],
+                                f8["rk"][0], f8["rv"][0], f8["rk"][1], f8["rv"][1], m=w.m, W=w.W,
+                                q_pos0=t, raw_pos0=t - w.W + 1, ws=aws)
+    torch.cuda.synchronize()
+    for b in seqs:
+        ock, ocv, _, _ = decode_caches_oracle(w, b)
+        err_c = max(maxerr(ck[b:b + 1].cpu(), ock), maxerr(cv[b:b + 1].cpu(), ocv))
+        say("  sequence", b, "compressed caches max err", err_c)
+        assert err_c <= TOL[w.dtype]
+        host = {}
+        for n, x in (("ck", ck), ("cv", cv), ("rk", rk), ("rv", rv)):
+            oc, os_ = oracle.quant_fp8_rows(f64(x[b:b + 1].cpu()))
+            gc, gs = fp8_host_rows(f8[n][0][b:b + 1], f8[n][1][b:b + 1])
+            assert np.array_equal(gc, oc) and np.array_equal(gs, os_), n
+            host[n] = (oc, os_)
+        if w.kind == "csa":
+            kc, ks = oracle.quant_mxfp4(f64(k_idx[b:b + 1].cpu()))
+            tk, exact = oracle.index_topk(f64(q_idx[b:b + 1].cpu()), kc, ks, [t], w.m, w.W, w.k)
+            assert exact
+            assert np.array_equal(gtk[b:b + 1].cpu().numpy(), tk)
+        else:
+            tk = None
+        ref = oracle.attend_fp8(f64(q[b:b + 1].cpu()), *host["ck"], *host["cv"], tk,
+                                *host["rk"], *host["rv"], t - w.W + 1, [t], w.m, w.W)
+        say("  sequence", b)
+        check_fp8(go[b:b + 1].cpu(), ref)
