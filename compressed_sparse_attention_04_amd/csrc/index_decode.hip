@@ -35,7 +35,7 @@ constexpr int DS_NT = 256;             // threads of a scanning block
 constexpr int DS_UNR = 4;              // key tiles per load batch of a scanning wave
 constexpr int DS_QT = 8;               // rows (queries x sequence) per sequence at most
 constexpr int DS_KEYS = 8192;          // LDS key words of a scanning block (all its rows)
-constexpr int DM_NT = 256;             // threads of a merging block
+constexpr int DM_NT = 512;             // threads of a merging block
 constexpr int DM_UCAP = 8192;          // union capacity (chunks x cap)
 constexpr int DM_MAXW = 8192;          // bitmap words of the exact path -> 262144 candidates
 constexpr int DM_CAP = 1024;           // collected keys of the exact path
@@ -61,7 +61,7 @@ __host__ __device__ __forceinline__ DecodeGeom decode_geom(int64_t Tq, int64_t n
     cap = cap < lim ? cap : lim;
     g.cap = cap < g.ch ? cap : g.ch;
     const int u = g.nchunks * g.cap;
-    g.ept = u <= 8 * DM_NT ? 8 : u <= 16 * DM_NT ? 16 : 32;
+    g.ept = u <= 4 * DM_NT ? 4 : u <= 8 * DM_NT ? 8 : u <= 16 * DM_NT ? 16 : 32;
     return g;
 }
 
@@ -623,7 +623,8 @@ static void launch_decode_t(int64_t B, int64_t Tq, int dI, int64_t Nc, int64_t m
                            (const T*)q_idx, qs, kc, ks, ws, topk, Tq, dI, Nc, m, W, k, q_pos0, \
                            g);                                                               \
     } while (0)
-    if (g.ept == 8) CSA_DM_CASE(8);
+    if (g.ept == 4) CSA_DM_CASE(4);
+    else if (g.ept == 8) CSA_DM_CASE(8);
     else if (g.ept == 16) CSA_DM_CASE(16);
     else CSA_DM_CASE(32);
 #undef CSA_DM_CASE
